@@ -1,0 +1,159 @@
+/*
+ * gemm_oracle.c -- the CPU oracle for dense row-major fp32 C = A x B.
+ *
+ * TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg may load this
+ * library.  It shares no source, header or helper with the HIP library.
+ *
+ * What it computes.  Every page agrees on the definition: element (i, j) of
+ * the product is the dot product of row i of A with column j of B
+ * ("Optimizing a WebGPU Matmul Kernel using Subgroups", section 1 Naive;
+ * "WebGPU 行列積の限界を測る", the N x N definition and the CPU triple loop).
+ * The CPU loop on that last page keeps its running sum in a JavaScript
+ * number, i.e. an IEEE binary64 value, and rounds once when it stores into a
+ * Float32Array.  This oracle does the same:
+ *
+ *   Cd[i][j] = sum over k = 0 .. K-1, in ascending k, of (double)A[i][k] * (double)B[k][j]
+ *   C[i][j]  = (float)Cd[i][j]                       (round to nearest even)
+ *   ABS[i][j]= sum over k of |(double)A[i][k] * (double)B[k][j]|
+ *
+ * ABS is the scale of the element-wise tolerance used by the parity tests.
+ *
+ * Exactness facts a reader can check:
+ *   - the product of two binary32 values has at most 48 significant bits, so
+ *     it is exact in binary64; fused or unfused multiply-add cannot differ;
+ *   - each element is summed in ascending k whatever the loop nest, so the
+ *     result does not depend on the number of threads.
+ *
+ * Layout (readings where the pages are silent): row-major with leading
+ * dimensions, A[i*lda + k], B[k*ldb + j], C[i*ldc + j], lda >= K, ldb >= N,
+ * ldc >= N.  Only the M x N window of C is written.  K = 0 gives +0.0.
+ *
+ * Loop order is i (parallel over threads), then k, then j: row i of the
+ * result is built in two binary64 row buffers while B is read row by row.
+ * No blocking, no reassociation.  Build without -ffast-math.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Status codes of this library (independent of the HIP library's). */
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+#define ORACLE_NO_MEMORY 2
+
+int oracle_version(void) { return 1; }
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/*
+ * oracle_gemm_f64acc
+ *   M, N, K        sizes (>= 0)
+ *   A, lda         M x K row-major, lda >= K
+ *   B, ldb         K x N row-major, ldb >= N
+ *   C, ldc         output, rounded to binary32; may be NULL
+ *   Cd, ldcd       output, the binary64 sum before rounding; may be NULL
+ *   ABS, ldabs     output, sum of |products| in binary64; may be NULL
+ * Returns ORACLE_OK, ORACLE_BAD_ARG or ORACLE_NO_MEMORY.
+ */
+int oracle_gemm_f64acc(int64_t M, int64_t N, int64_t K,
+                       const float *A, int64_t lda,
+                       const float *B, int64_t ldb,
+                       float *C, int64_t ldc,
+                       double *Cd, int64_t ldcd,
+                       double *ABS, int64_t ldabs) {
+  if (M < 0 || N < 0 || K < 0) return ORACLE_BAD_ARG;
+  if (M == 0 || N == 0) return ORACLE_OK;
+  if (lda < K || ldb < N) return ORACLE_BAD_ARG;
+  if (C && ldc < N) return ORACLE_BAD_ARG;
+  if (Cd && ldcd < N) return ORACLE_BAD_ARG;
+  if (ABS && ldabs < N) return ORACLE_BAD_ARG;
+  if (K > 0 && (!A || !B)) return ORACLE_BAD_ARG;
+
+  int failed = 0;
+#pragma omp parallel
+  {
+    double *acc = (double *)malloc((size_t)N * sizeof(double));
+    double *mag = (double *)malloc((size_t)N * sizeof(double));
+    if (!acc || !mag) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+      if (!acc || !mag) continue;
+      for (int64_t j = 0; j < N; ++j) {
+        acc[j] = 0.0;
+        mag[j] = 0.0;
+      }
+      for (int64_t k = 0; k < K; ++k) {
+        const double a = (double)A[i * lda + k];
+        const float *brow = B + k * ldb;
+        for (int64_t j = 0; j < N; ++j) {
+          const double p = a * (double)brow[j];
+          acc[j] += p;
+          mag[j] += fabs(p);
+        }
+      }
+      for (int64_t j = 0; j < N; ++j) {
+        if (C) C[i * ldc + j] = (float)acc[j];
+        if (Cd) Cd[i * ldcd + j] = acc[j];
+        if (ABS) ABS[i * ldabs + j] = mag[j];
+      }
+    }
+    free(acc);
+    free(mag);
+  }
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/*
+ * oracle_gemm_elems -- the same definition evaluated at a list of (i, j)
+ * positions only, for spot checks of products too large to compute whole.
+ *   rows[t], cols[t]  the positions, 0 <= rows[t] < M, 0 <= cols[t] < N
+ *   C, Cd, ABS        one value per position (any may be NULL)
+ */
+int oracle_gemm_elems(int64_t M, int64_t N, int64_t K,
+                      const float *A, int64_t lda,
+                      const float *B, int64_t ldb,
+                      int64_t count, const int64_t *rows, const int64_t *cols,
+                      float *C, double *Cd, double *ABS) {
+  if (M < 0 || N < 0 || K < 0 || count < 0) return ORACLE_BAD_ARG;
+  if (lda < K || ldb < N) return ORACLE_BAD_ARG;
+  if (count > 0 && (!rows || !cols)) return ORACLE_BAD_ARG;
+  for (int64_t t = 0; t < count; ++t)
+    if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N)
+      return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < count; ++t) {
+    const int64_t i = rows[t], j = cols[t];
+    double acc = 0.0, mag = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double p = (double)A[i * lda + k] * (double)B[k * ldb + j];
+      acc += p;
+      mag += fabs(p);
+    }
+    if (C) C[t] = (float)acc;
+    if (Cd) Cd[t] = acc;
+    if (ABS) ABS[t] = mag;
+  }
+  return ORACLE_OK;
+}

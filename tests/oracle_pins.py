@@ -1,0 +1,253 @@
+"""Pins for the CPU oracle: checks against facts the definition and the
+mathematics fix, independent of the oracle's own code.
+
+Each ``pin_*`` takes a GEMM function ``fn(A, B) -> (C, Cd, ABS)`` with the
+oracle's contract (float32 inputs with contiguous rows and any row pitch;
+float32 C, float64 Cd and ABS) and returns a list of failure messages (empty
+when the pin holds).  The same pins are run against deliberately wrong
+variants in ``test_oracle_pins.py`` to show that each plausible mistake is
+caught by at least one of them.
+"""
+from __future__ import annotations
+
+import json
+from fractions import Fraction
+from pathlib import Path
+
+import numpy as np
+import torch
+
+from dense_fp32_gemm_f32_amd import inputs
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+def _np(t: torch.Tensor) -> np.ndarray:
+    return t.numpy()
+
+
+def _ints(rows, cols, seed, lo=-2, hi=2):
+    return _np(inputs.int_matrix(rows, cols, seed, lo, hi))
+
+
+def _exact_int(A, B):
+    """Integer product in int64: exact, no floating point involved."""
+    return A.astype(np.int64) @ B.astype(np.int64)
+
+
+def _fail(name, msg):
+    return [f"{name}: {msg}"]
+
+
+# --- closed forms -----------------------------------------------------------
+
+def pin_identity(fn):
+    """I x B = B and A x I = A, bit for bit (one nonzero product per term)."""
+    errs = []
+    for (m, n, seed) in [(17, 23, 11), (64, 40, 12), (5, 1, 13)]:
+        B = _np(inputs.uniform_matrix(m, n, seed))
+        C, _, _ = fn(np.eye(m, dtype=np.float32), B)
+        if not np.array_equal(C, B):
+            errs += _fail("identity-left", f"I({m}) x B({m}x{n}) != B")
+        A = _np(inputs.uniform_matrix(n, m, seed + 100))
+        C, _, _ = fn(A, np.eye(m, dtype=np.float32))
+        if not np.array_equal(C, A):
+            errs += _fail("identity-right", f"A({n}x{m}) x I({m}) != A")
+    return errs
+
+
+def pin_permutation(fn):
+    """P x B permutes the rows of B, A x P permutes the columns of A."""
+    errs = []
+    rng = np.random.default_rng(7)
+    for (m, n) in [(19, 13), (32, 48), (24, 24)]:
+        p = rng.permutation(m)
+        P = np.zeros((m, m), dtype=np.float32)
+        P[np.arange(m), p] = 1.0           # (P x B)[i] = B[p[i]]
+        B = _np(inputs.uniform_matrix(m, n, 21))
+        C, _, _ = fn(P, B)
+        if not np.array_equal(C, B[p]):
+            errs += _fail("permutation-left", f"rows not permuted at {m}x{n}")
+        A = _np(inputs.uniform_matrix(n, m, 22))
+        C, _, _ = fn(A, P)                 # (A x P)[:, j] = A[:, q] with p[q] = j
+        q = np.argsort(p)
+        if not np.array_equal(C, A[:, q]):
+            errs += _fail("permutation-right", f"columns not permuted at {n}x{m}")
+    return errs
+
+
+def pin_all_ones(fn):
+    """Ones(M x K) x Ones(K x N) = K everywhere."""
+    errs = []
+    for (m, n, k) in [(3, 5, 7), (16, 9, 300)]:
+        C, Cd, ABS = fn(np.ones((m, k), np.float32), np.ones((k, n), np.float32))
+        if not np.all(C == np.float32(k)):
+            errs += _fail("all-ones", f"C != {k} at {m}x{n}x{k}")
+        if ABS is not None and not np.all(ABS == float(k)):
+            errs += _fail("all-ones", "ABS != K")
+    return errs
+
+
+def pin_rank1(fn):
+    """Both readings of the rank-1 closed form, small integers, exact:
+    (u v^T)(w z^T) = (v.w) u z^T  and  (u v^T) W = u (v^T W)."""
+    errs = []
+    m, k, n = 11, 9, 14
+    u, v = _ints(m, 1, 31, -3, 3), _ints(k, 1, 32, -3, 3)
+    w, z = _ints(k, 1, 33, -3, 3), _ints(n, 1, 34, -3, 3)
+    A = (u @ v.T).astype(np.float32)
+    B = (w @ z.T).astype(np.float32)
+    dot = sum(int(v[t, 0]) * int(w[t, 0]) for t in range(k))
+    want = np.array([[dot * int(u[i, 0]) * int(z[j, 0]) for j in range(n)]
+                     for i in range(m)], dtype=np.float32)
+    C, _, _ = fn(A, B)
+    if not np.array_equal(C, want):
+        errs += _fail("rank1-outer", "(u v^T)(w z^T) != (v.w) u z^T")
+    W = _ints(k, n, 35, -4, 4)
+    vW = [sum(int(v[t, 0]) * int(W[t, j]) for t in range(k)) for j in range(n)]
+    want = np.array([[int(u[i, 0]) * vW[j] for j in range(n)] for i in range(m)],
+                    dtype=np.float32)
+    C, _, _ = fn(A, W)
+    if not np.array_equal(C, want):
+        errs += _fail("rank1-left", "(u v^T) W != u (v^T W)")
+    return errs
+
+
+# --- brute force --------------------------------------------------------------
+
+def pin_integer_bruteforce(fn):
+    """Random small integers against an int64 product (exact in any order),
+    including padded row pitches and a 1-row / 1-column / 1-deep case."""
+    errs = []
+    cases = [(32, 24, 16, 0, 0), (37, 29, 53, 3, 5), (1, 50, 40, 0, 0),
+             (50, 1, 40, 0, 0), (20, 30, 1, 2, 0), (64, 64, 257, 0, 7)]
+    for t, (m, n, k, pa, pb) in enumerate(cases):
+        A, B = inputs.make_ab(m, n, k, "int2", "int2", 500 + t, lda=k + pa, ldb=n + pb)
+        A, B = _np(A), _np(B)
+        C, Cd, ABS = fn(A, B)
+        want = _exact_int(A, B)
+        if not np.array_equal(C, want.astype(np.float32)):
+            errs += _fail("int-bruteforce", f"C wrong at {m}x{n}x{k} (pads {pa},{pb})")
+        if Cd is not None and not np.array_equal(Cd, want.astype(np.float64)):
+            errs += _fail("int-bruteforce", f"Cd wrong at {m}x{n}x{k}")
+        if ABS is not None:
+            want_abs = np.abs(A.astype(np.int64)) @ np.abs(B.astype(np.int64))
+            if not np.array_equal(ABS, want_abs.astype(np.float64)):
+                errs += _fail("int-bruteforce", f"ABS != |A| |B| at {m}x{n}x{k}")
+    return errs
+
+
+def pin_exact_rational(fn):
+    """Tiny inputs on a 2^-12 grid: every partial sum is exact in binary64,
+    so the true sum is known exactly (Fraction) and C must be its single
+    round-to-nearest-even rounding to binary32."""
+    errs = []
+    rng = np.random.default_rng(99)
+    for (m, n, k) in [(3, 4, 5), (6, 2, 8), (1, 7, 3)]:
+        A = (rng.integers(-4095, 4096, (m, k)) / 4096.0).astype(np.float32)
+        B = (rng.integers(-4095, 4096, (k, n)) / 4096.0).astype(np.float32)
+        C, Cd, _ = fn(A, B)
+        for i in range(m):
+            for j in range(n):
+                s = sum((Fraction(float(A[i, p])) * Fraction(float(B[p, j])) for p in range(k)),
+                        Fraction(0))
+                exact64 = float(s)       # exact: s is a multiple of 2^-24 below 2^4
+                if Fraction(exact64) != s:
+                    raise AssertionError("grid assumption broken")
+                if np.float32(exact64) != C[i, j]:
+                    errs += _fail("exact-rational", f"C[{i},{j}] not RN-even of exact sum")
+                if Cd is not None and Cd[i, j] != exact64:
+                    errs += _fail("exact-rational", f"Cd[{i},{j}] != exact sum")
+    return errs
+
+
+def pin_golden_page_pattern(fn):
+    """The integer pattern checked on the 'GPU compute shaders' page."""
+    g = json.loads((GOLDEN / "gpu_compute_shaders_tiled_matmul_pattern.json").read_text())
+    m, n, k = g["m"], g["n"], g["k"]
+    a = np.array([(i % g["a_mod"]) + g["a_offset"] for i in range(m * k)], np.float32).reshape(m, k)
+    b = np.array([(i % g["b_mod"]) + g["b_offset"] for i in range(k * n)], np.float32).reshape(k, n)
+    C, _, _ = fn(a, b)
+    errs = []
+    for e in g["hand_derived"]:
+        if C[e["row"], e["col"]] != e["value"]:
+            errs += _fail("page-pattern", f"C[{e['row']},{e['col']}] = {C[e['row'], e['col']]} != {e['value']}")
+    # the page's own check: each element equals the ascending-k sum (exact for integers)
+    for r in range(m):
+        for q in range(n):
+            want = 0
+            for p in range(k):
+                want += int(a[r, p]) * int(b[p, q])
+            if C[r, q] != want:
+                return errs + _fail("page-pattern", f"C[{r},{q}] != {want}")
+    return errs
+
+
+# --- metamorphic relations ----------------------------------------------------
+
+def pin_transpose(fn):
+    """(B^T A^T) = (A B)^T bit for bit: same products, same ascending k."""
+    A = _np(inputs.uniform_matrix(21, 34, 41))
+    B = _np(inputs.uniform_matrix(34, 15, 42))
+    C1, _, _ = fn(A, B)
+    C2, _, _ = fn(np.ascontiguousarray(B.T), np.ascontiguousarray(A.T))
+    return [] if np.array_equal(C1, C2.T) else _fail("transpose", "(B^T A^T)^T != A B")
+
+
+def pin_linearity(fn):
+    """(A1 + A2) B = A1 B + A2 B on integers (exact)."""
+    A1, A2 = _ints(18, 27, 51, -3, 3), _ints(18, 27, 52, -3, 3)
+    B = _ints(27, 22, 53, -3, 3)
+    C, _, _ = fn((A1 + A2).astype(np.float32), B)
+    C1, _, _ = fn(A1, B)
+    C2, _, _ = fn(A2, B)
+    return [] if np.array_equal(C, C1 + C2) else _fail("linearity", "(A1+A2)B != A1 B + A2 B")
+
+
+def pin_pitch_invariance(fn):
+    """Same values with padded pitches (padding = NaN) give the same C."""
+    A, B = inputs.make_ab(23, 31, 45, "u11", "u11", 61)
+    Ap, Bp = inputs.make_ab(23, 31, 45, "u11", "u11", 61, lda=48, ldb=36)
+    C1, _, _ = fn(_np(A), _np(B))
+    C2, _, _ = fn(_np(Ap), _np(Bp))
+    if not np.all(np.isfinite(C2)):
+        return _fail("pitch", "padding leaked into C")
+    return [] if np.array_equal(C1, C2) else _fail("pitch", "C depends on the row pitch")
+
+
+# --- agreement with a library routine and the error bound ----------------------
+
+def pin_float64_library(fn):
+    """Random U[-1,1) and N(0,1) inputs: the binary64 sum agrees with torch's
+    float64 matmul within the summation bound 2 K u64 sum|a b|, and C is within
+    one binary32 rounding of the exact product."""
+    errs = []
+    for (m, n, k, dist, seed) in [(40, 50, 300, "u11", 71), (33, 17, 1000, "normal", 72)]:
+        A, B = inputs.make_ab(m, n, k, dist, dist, seed)
+        C, Cd, ABS = fn(_np(A), _np(B))
+        ref = (A.double() @ B.double()).numpy()
+        absref = (A.double().abs() @ B.double().abs()).numpy()
+        u64 = 2.0 ** -53
+        bound64 = 2 * k * u64 * absref
+        if Cd is not None and not np.all(np.abs(Cd - ref) <= bound64):
+            errs += _fail("float64-library", f"Cd differs from float64 matmul at {m}x{n}x{k}")
+        if ABS is not None and not np.all(np.abs(ABS - absref) <= bound64):
+            errs += _fail("float64-library", "ABS differs from |A| |B|")
+        # binary32 rounding of the (nearly) exact value: half an ulp plus bound64
+        err = np.abs(C.astype(np.float64) - ref)
+        allow = np.abs(ref) * 2.0 ** -24 + 2 * bound64 + 1e-45
+        if not np.all(err <= allow):
+            errs += _fail("float64-library", f"C not the rounded product at {m}x{n}x{k}")
+    return errs
+
+
+ALL_PINS = [pin_identity, pin_permutation, pin_all_ones, pin_rank1,
+            pin_integer_bruteforce, pin_exact_rational, pin_golden_page_pattern,
+            pin_transpose, pin_linearity, pin_pitch_invariance, pin_float64_library]
+
+
+def run_all(fn):
+    errs = []
+    for p in ALL_PINS:
+        errs += p(fn)
+    return errs

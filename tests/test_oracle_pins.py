@@ -1,0 +1,140 @@
+"""The CPU oracle against its pins, and the pins against planted mistakes.
+
+CPU only.  The oracle must pass every pin; each mutant below (a plausible
+mistake written as a small numpy variant of the oracle's contract) must fail
+at least one pin, which shows the pins can tell.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests import oracle_pins as pins
+
+
+def oracle_fn(A, B):
+    return oracle.gemm(A, B)
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_passes_pin(pin):
+    errs = pin(oracle_fn)
+    assert not errs, "\n".join(errs)
+
+
+# ---- planted mistakes (CPU, numpy) -----------------------------------------
+
+def _variant(mistake):
+    """Oracle-like GEMM with one planted mistake."""
+    def fn(A, B):
+        M, K = A.shape
+        N = B.shape[1]
+        acc_t = np.float32 if mistake == "fp32_accumulate" else np.float64
+        acc = np.zeros((M, N), acc_t)
+        mag = np.zeros((M, N), np.float64)
+        ks = range(K)
+        if mistake == "drop_last_k":
+            ks = range(max(K - 1, 0))
+        if mistake == "skip_first_k":
+            ks = range(1, K)
+        Aeff = A
+        if mistake == "ignore_lda" and M > 1 and A.strides[0] != 4 * K:
+            flat = np.lib.stride_tricks.as_strided(A, shape=(M * K,), strides=(4,))
+            Aeff = flat.reshape(M, K)
+        for k in ks:
+            a = Aeff[:, k:k + 1].astype(acc_t)
+            if mistake == "transpose_b" and B.shape[0] == B.shape[1]:
+                b = B[:, k:k + 1].T.astype(acc_t)
+            else:
+                b = B[k:k + 1, :].astype(acc_t)
+            p = a * b
+            if mistake == "negate_middle" and k == K // 2:
+                p = -p
+            if mistake == "row_shift":
+                p = np.roll(p, 1, axis=0)
+            acc += p
+            mag += np.abs(p.astype(np.float64))
+        if mistake == "abs_of_sum":
+            mag = np.abs(acc.astype(np.float64))
+        Cd = acc.astype(np.float64)
+        if mistake == "round_toward_zero":
+            C = Cd.astype(np.float32)
+            over = np.abs(C.astype(np.float64)) > np.abs(Cd)
+            C[over] = np.nextafter(C[over], np.float32(0))
+        else:
+            C = Cd.astype(np.float32)
+        if mistake == "swap_operands" and A.shape[0] == A.shape[1] == B.shape[0] == B.shape[1]:
+            C = (B.astype(np.float64) @ A.astype(np.float64)).astype(np.float32)
+        return C, Cd, mag
+    return fn
+
+
+MISTAKES = ["drop_last_k", "skip_first_k", "transpose_b", "negate_middle", "row_shift",
+            "fp32_accumulate", "round_toward_zero", "ignore_lda", "abs_of_sum",
+            "swap_operands"]
+
+
+def test_correct_variant_passes_all_pins():
+    """The mutant harness itself, with no mistake, satisfies every pin."""
+    errs = pins.run_all(_variant("none"))
+    assert not errs, "\n".join(errs)
+
+
+@pytest.mark.parametrize("mistake", MISTAKES)
+def test_pins_catch_planted_mistake(mistake):
+    errs = pins.run_all(_variant(mistake))
+    assert errs, f"no pin caught the planted mistake {mistake!r}"
+
+
+# ---- direct definitional checks of the oracle's interface -------------------
+
+def test_empty_sum_is_positive_zero():
+    A = np.zeros((3, 0), np.float32)
+    B = np.zeros((0, 4), np.float32)
+    C, Cd, ABS = oracle.gemm(A, B)
+    assert C.shape == (3, 4) and np.all(C == 0) and not np.any(np.signbit(C))
+
+
+def test_cancelling_sum_is_positive_zero():
+    A = np.array([[1.0, -1.0]], np.float32)
+    B = np.array([[0.75], [0.75]], np.float32)
+    C, _, _ = oracle.gemm(A, B)
+    assert C[0, 0] == 0 and not np.signbit(C[0, 0])
+
+
+def test_empty_output():
+    C, _, _ = oracle.gemm(np.zeros((0, 5), np.float32), np.ones((5, 3), np.float32))
+    assert C.shape == (0, 3)
+
+
+def test_nan_propagates_along_its_row():
+    A = np.ones((4, 6), np.float32)
+    A[2, 3] = np.nan
+    C, _, _ = oracle.gemm(A, np.ones((6, 5), np.float32))
+    assert np.all(np.isnan(C[2])) and np.all(np.isfinite(np.delete(C, 2, axis=0)))
+
+
+def test_elems_match_full_product():
+    from dense_fp32_gemm_f32_amd import inputs
+    A, B = inputs.make_ab(37, 45, 61, "normal", "normal", 81, lda=64, ldb=50)
+    A, B = A.numpy(), B.numpy()
+    C, Cd, ABS = oracle.gemm(A, B)
+    rng = np.random.default_rng(3)
+    r, c = rng.integers(0, 37, 200), rng.integers(0, 45, 200)
+    Ce, Cde, ABSe = oracle.gemm_elems(A, B, r, c)
+    assert np.array_equal(Ce, C[r, c]) and np.array_equal(Cde, Cd[r, c])
+    assert np.array_equal(ABSe, ABS[r, c])
+
+
+def test_thread_count_does_not_change_result():
+    from dense_fp32_gemm_f32_amd import inputs
+    A, B = inputs.make_ab(64, 70, 300, "u11", "u11", 91)
+    A, B = A.numpy(), B.numpy()
+    n0 = oracle.max_threads()
+    try:
+        oracle.set_threads(1)
+        C1, Cd1, _ = oracle.gemm(A, B)
+        oracle.set_threads(max(2, n0))
+        C2, Cd2, _ = oracle.gemm(A, B)
+    finally:
+        oracle.set_threads(n0)
+    assert np.array_equal(C1, C2) and np.array_equal(Cd1, Cd2)
