@@ -1,0 +1,215 @@
+"""ctypes binding of ``libgemm_f32.so`` (the C ABI in ``include/gemm_f32.h``).
+
+Two layers, both argument marshalling only -- every step of the product runs
+in the HIP kernels:
+
+* functions named exactly as the C entry points (``gemm_f32``,
+  ``gemm_f32_ref_gpu``, ...) taking plain integers: sizes, device pointers,
+  pitches and a ``hipStream_t`` as an integer (0 = default stream);
+* ``gemm`` / ``gemm_ref`` / ``run_kernel``: the same calls on torch tensors,
+  which read sizes, pitches and pointers from the tensors and enqueue on
+  torch's current stream of the tensors' device.
+
+There is no fallback: if the library is missing, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libgemm_f32.so"
+
+GEMM_F32_OK = 0
+STATUS_NAMES = {
+    0: "GEMM_F32_OK", 1: "GEMM_F32_ERR_INVALID_DIM", 2: "GEMM_F32_ERR_INVALID_LD",
+    3: "GEMM_F32_ERR_NULL_PTR", 4: "GEMM_F32_ERR_ALIAS", 5: "GEMM_F32_ERR_DEVICE",
+    6: "GEMM_F32_ERR_WORKSPACE", 7: "GEMM_F32_ERR_LAUNCH", 8: "GEMM_F32_ERR_BAD_KERNEL",
+    9: "GEMM_F32_ERR_POINTER",
+}
+EXPORTS = ["gemm_f32", "gemm_f32_ref_gpu", "gemm_f32_status_string",
+           "gemm_f32_selected_kernel", "gemm_f32_version", "gemm_f32_kernel_count",
+           "gemm_f32_kernel_name", "gemm_f32_run_kernel", "gemm_f32_release_workspaces"]
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} "
+                         f"({gemm_f32_status_string(status)})")
+
+
+_lib = None
+
+
+def load():
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise FileNotFoundError(
+            f"{LIB_PATH} is missing: build it with `python -m dense_fp32_gemm_f32_amd.build_lib` "
+            "(there is no CPU or PyTorch fallback)")
+    lib = ctypes.CDLL(str(LIB_PATH))
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    gemm_args = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
+    for name in ("gemm_f32", "gemm_f32_ref_gpu"):
+        getattr(lib, name).argtypes = gemm_args
+        getattr(lib, name).restype = ctypes.c_int
+    lib.gemm_f32_run_kernel.argtypes = [ctypes.c_int, *gemm_args]
+    lib.gemm_f32_run_kernel.restype = ctypes.c_int
+    lib.gemm_f32_status_string.argtypes = [ctypes.c_int]
+    lib.gemm_f32_status_string.restype = ctypes.c_char_p
+    lib.gemm_f32_selected_kernel.argtypes = [i64, i64, i64, i64, i64, i64, vp, vp, vp]
+    lib.gemm_f32_selected_kernel.restype = ctypes.c_char_p
+    lib.gemm_f32_version.argtypes = []
+    lib.gemm_f32_version.restype = ctypes.c_int
+    lib.gemm_f32_kernel_count.argtypes = []
+    lib.gemm_f32_kernel_count.restype = ctypes.c_int
+    lib.gemm_f32_kernel_name.argtypes = [ctypes.c_int]
+    lib.gemm_f32_kernel_name.restype = ctypes.c_char_p
+    lib.gemm_f32_release_workspaces.argtypes = []
+    lib.gemm_f32_release_workspaces.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ---- the C entry points, same names, plain integers ------------------------
+
+def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    return load().gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_ref_gpu(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    return load().gemm_f32_ref_gpu(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_run_kernel(index, M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    return load().gemm_f32_run_kernel(index, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_status_string(status: int) -> str:
+    return load().gemm_f32_status_string(int(status)).decode()
+
+
+def gemm_f32_selected_kernel(M, N, K, lda, ldb, ldc, A=0, B=0, C=0) -> str:
+    return load().gemm_f32_selected_kernel(M, N, K, lda, ldb, ldc, A, B, C).decode()
+
+
+def gemm_f32_version() -> int:
+    return load().gemm_f32_version()
+
+
+def gemm_f32_kernel_count() -> int:
+    return load().gemm_f32_kernel_count()
+
+
+def gemm_f32_kernel_name(index: int) -> str | None:
+    r = load().gemm_f32_kernel_name(index)
+    return None if r is None else r.decode()
+
+
+def gemm_f32_release_workspaces() -> int:
+    return load().gemm_f32_release_workspaces()
+
+
+def kernel_names() -> list[str]:
+    return [gemm_f32_kernel_name(i) for i in range(gemm_f32_kernel_count())]
+
+
+def kernel_index(name: str) -> int:
+    names = kernel_names()
+    if name not in names:
+        raise KeyError(f"no kernel named {name!r}")
+    return names.index(name)
+
+
+# ---- torch tensors -----------------------------------------------------------
+
+def _pitch(t, name):
+    import torch
+    if t.dtype != torch.float32 or t.dim() != 2:
+        raise TypeError(f"{name} must be a 2-D float32 tensor")
+    if t.device.type != "cuda":
+        raise TypeError(f"{name} must be on a GPU (got {t.device})")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} rows must be contiguous (stride(1) == 1)")
+    return max(t.stride(0), t.shape[1], 1) if t.shape[0] > 1 else max(t.shape[1], 1)
+
+
+def _args(A, B, C):
+    import torch
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner sizes differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if tuple(C.shape) != (M, N):
+        raise ValueError(f"C must be {M}x{N}, got {tuple(C.shape)}")
+    lda, ldb, ldc = _pitch(A, "A"), _pitch(B, "B"), _pitch(C, "C")
+    if not (A.device == B.device == C.device):
+        raise ValueError("A, B and C must be on one device")
+    stream = torch.cuda.current_stream(A.device).cuda_stream
+    return (M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, stream), C
+
+
+def gemm(A, B, C=None):
+    """C = A @ B on the GPU with the dispatcher's kernel; returns C."""
+    args, C = _args(A, B, C)
+    with _device(A):
+        rc = gemm_f32(*args)
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc, "gemm_f32")
+    return C
+
+
+def gemm_ref(A, B, C=None):
+    """C = A @ B with the naive reference kernel; returns C."""
+    args, C = _args(A, B, C)
+    with _device(A):
+        rc = gemm_f32_ref_gpu(*args)
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc, "gemm_f32_ref_gpu")
+    return C
+
+
+def run_kernel(index_or_name, A, B, C=None):
+    """C = A @ B with one named (or indexed) kernel of the table; returns C."""
+    index = kernel_index(index_or_name) if isinstance(index_or_name, str) else int(index_or_name)
+    args, C = _args(A, B, C)
+    with _device(A):
+        rc = gemm_f32_run_kernel(index, *args)
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc, f"gemm_f32_run_kernel({index_or_name})")
+    return C
+
+
+def selected_kernel(A, B, C=None) -> str:
+    M, K = A.shape
+    N = B.shape[1]
+    ldc = N if C is None else max(C.stride(0), N)
+    return gemm_f32_selected_kernel(M, N, K, max(A.stride(0), K, 1), max(B.stride(0), N, 1),
+                                    max(ldc, 1), A.data_ptr(), B.data_ptr(),
+                                    0 if C is None else C.data_ptr())
+
+
+class _device:
+    """Make the tensor's device current for the call (the library uses the
+    current HIP device)."""
+
+    def __init__(self, t):
+        self.idx = t.device.index
+
+    def __enter__(self):
+        import torch
+        self.prev = torch.cuda.current_device()
+        if self.idx is not None and self.idx != self.prev:
+            torch.cuda.set_device(self.idx)
+
+    def __exit__(self, *exc):
+        import torch
+        if self.idx is not None and self.idx != self.prev:
+            torch.cuda.set_device(self.prev)
+        return False

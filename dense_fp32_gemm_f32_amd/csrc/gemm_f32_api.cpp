@@ -1,0 +1,399 @@
+// C ABI of the gfx950 fp32 GEMM library: argument checks, the tuning-table
+// dispatcher, the skinny kernel's workspace, and the kernel table.
+//
+// The pages pass caller-created buffers and M, N, K to one GEMM entry point
+// ("WebGPU WGSL Compute Shaders: Custom Matrix Multiplication (GEMM)
+// Optimization Guide", section 5, and the dimensions uniform of the ybb.press
+// page); this library takes device pointers, sizes, row pitches and a HIP
+// stream instead, and reports errors with status codes.
+#include "../../include/gemm_f32.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "gemm_f32_internal.h"
+#include "tuning_gfx950.h"
+
+using gemmf32::Problem;
+
+namespace {
+
+// ---- kernel table: MFMA variants, skinny variants, the naive kernel -------
+enum class Kind { Mfma, Skinny, Ref };
+struct Entry {
+  Kind kind;
+  int sub;  // index within its family
+  const char* name;
+};
+
+const std::vector<Entry>& entries() {
+  static const std::vector<Entry> table = [] {
+    std::vector<Entry> t;
+    for (int i = 0; i < gemmf32::mfma_variant_count(); ++i)
+      t.push_back({Kind::Mfma, i, gemmf32::mfma_variant(i).name});
+    for (int i = 0; i < gemmf32::skinny_variant_count(); ++i)
+      t.push_back({Kind::Skinny, i, gemmf32::skinny_variant(i).name});
+    t.push_back({Kind::Ref, 0, "ref_naive"});
+    return t;
+  }();
+  return table;
+}
+
+int find_entry(const std::string& name) {
+  const auto& t = entries();
+  for (size_t i = 0; i < t.size(); ++i)
+    if (name == t[i].name) return (int)i;
+  return -1;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---- argument checks (host only, nothing enqueued) -------------------------
+int check_args(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+               int64_t ldb, const float* C, int64_t ldc) {
+  const int64_t kMax = GEMM_F32_MAX_DIM;
+  if (M < 0 || N < 0 || K < 0 || M > kMax || N > kMax || K > kMax)
+    return GEMM_F32_ERR_INVALID_DIM;
+  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    return GEMM_F32_ERR_INVALID_LD;
+  // byte extents must stay far from overflow
+  const int64_t kMaxElems = INT64_C(1) << 60;
+  if ((M > 0 && lda > kMaxElems / M) || (K > 0 && ldb > kMaxElems / K) ||
+      (M > 0 && ldc > kMaxElems / M))
+    return GEMM_F32_ERR_INVALID_LD;
+  const bool has_a = M > 0 && K > 0, has_b = K > 0 && N > 0, has_c = M > 0 && N > 0;
+  if ((has_a && !A) || (has_b && !B) || (has_c && !C)) return GEMM_F32_ERR_NULL_PTR;
+  if (has_c) {
+    const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(((M - 1) * ldc + N) * 4);
+    if (has_a) {
+      const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)(((M - 1) * lda + K) * 4);
+      if (c0 < a1 && a0 < c1) return GEMM_F32_ERR_ALIAS;
+    }
+    if (has_b) {
+      const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(((K - 1) * ldb + N) * 4);
+      if (c0 < b1 && b0 < c1) return GEMM_F32_ERR_ALIAS;
+    }
+  }
+  return GEMM_F32_OK;
+}
+
+// ---- device check: gfx950 only, cached per device ---------------------------
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+int g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device(int* dev_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return GEMM_F32_ERR_DEVICE;
+  }
+  *dev_out = dev;
+  {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_state[dev] == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_F32_ERR_DEVICE;
+      }
+      g_dev_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    if (g_dev_state[dev] != 1) return GEMM_F32_ERR_DEVICE;
+  }
+  return GEMM_F32_OK;
+}
+
+// A, B and C must be memory the current device can reach.
+int check_pointer(const void* p, int dev) {
+  if (!p) return GEMM_F32_OK;  // only reached for empty matrices
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof(attr));
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return GEMM_F32_ERR_POINTER;
+  }
+  switch (attr.type) {
+    case hipMemoryTypeDevice:
+      return attr.device == dev ? GEMM_F32_OK : GEMM_F32_ERR_POINTER;
+    case hipMemoryTypeManaged:
+    case hipMemoryTypeUnified:
+      return GEMM_F32_OK;
+    case hipMemoryTypeHost:
+      return attr.devicePointer ? GEMM_F32_OK : GEMM_F32_ERR_POINTER;
+    default:
+      return GEMM_F32_ERR_POINTER;
+  }
+}
+
+// ---- skinny-kernel workspace, one per (device, stream) ----------------------
+// Layout: [arrival counters, 256-byte aligned][partial sums].  The counters
+// are zeroed once when the buffer is created; every call leaves them at zero.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  size_t counter_bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, uintptr_t>, Workspace>* g_ws = nullptr;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int get_workspace(int dev, hipStream_t s, size_t counter_words, size_t partial_floats,
+                  unsigned** counters, float** partials) {
+  const size_t cbytes = round_up(counter_words * 4, 256);
+  const size_t need = cbytes + partial_floats * 4;
+  if (std::getenv("GEMM_F32_TEST_FAIL_WORKSPACE")) return GEMM_F32_ERR_WORKSPACE;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  if (!g_ws) g_ws = new std::map<std::pair<int, uintptr_t>, Workspace>();
+  Workspace& w = (*g_ws)[{dev, (uintptr_t)s}];
+  if (w.bytes < need || w.counter_bytes < cbytes) {
+    if (w.ptr) {
+      // the stream may still be using the old buffer
+      if (hipStreamSynchronize(s) != hipSuccess || hipFree(w.ptr) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_F32_ERR_WORKSPACE;
+      }
+      w = Workspace{};
+    }
+    // grow with headroom so alternating shapes do not reallocate
+    const size_t cb = cbytes > 4096 ? cbytes : 4096;
+    const size_t bytes = cb + round_up(partial_floats * 4 + partial_floats * 2, 1 << 20);
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return GEMM_F32_ERR_WORKSPACE;
+    }
+    if (hipMemsetAsync(p, 0, cb, s) != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipFree(p);
+      return GEMM_F32_ERR_WORKSPACE;
+    }
+    w.ptr = p;
+    w.bytes = bytes;
+    w.counter_bytes = cb;
+  }
+  *counters = static_cast<unsigned*>(w.ptr);
+  *partials = reinterpret_cast<float*>(static_cast<char*>(w.ptr) + w.counter_bytes);
+  return GEMM_F32_OK;
+}
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("GEMM_F32_LOG");
+    return v && *v && *v != '0';
+  }();
+  return on;
+}
+
+// Can entry e run these arguments?
+bool entry_accepts(const Entry& e, const Problem& p) {
+  if (e.kind == Kind::Mfma) {
+    const auto& v = gemmf32::mfma_variant(e.sub);
+    if (v.vec_a && !(p.lda % 4 == 0 && aligned16(p.A))) return false;
+    if (v.vec_b && !(p.ldb % 4 == 0 && aligned16(p.B))) return false;
+    return true;
+  }
+  if (e.kind == Kind::Skinny) {
+    const auto& v = gemmf32::skinny_variant(e.sub);
+    if (p.M > v.mr) return false;
+    if (v.vec_b && !(p.ldb % 4 == 0 && aligned16(p.B))) return false;
+    return true;
+  }
+  return true;
+}
+
+int run_entry(const Entry& e, const Problem& p, int dev, hipStream_t s) {
+  if (log_enabled())
+    std::fprintf(stderr, "[gemm_f32] M=%d N=%d K=%d lda=%lld ldb=%lld ldc=%lld -> %s\n", p.M,
+                 p.N, p.K, (long long)p.lda, (long long)p.ldb, (long long)p.ldc, e.name);
+  hipError_t err = hipSuccess;
+  switch (e.kind) {
+    case Kind::Mfma:
+      err = gemmf32::mfma_variant(e.sub).launch(p, s);
+      break;
+    case Kind::Skinny: {
+      const auto& v = gemmf32::skinny_variant(e.sub);
+      const gemmf32::SkinnyPlan pl = v.plan(p, v.target_splits);
+      unsigned* counters = nullptr;
+      float* partials = nullptr;
+      if (pl.splits > 1) {
+        const int rc =
+            get_workspace(dev, s, pl.counter_words, pl.partial_floats, &counters, &partials);
+        if (rc != GEMM_F32_OK) return rc;
+      }
+      err = v.launch(p, pl, partials, counters, s);
+      break;
+    }
+    case Kind::Ref:
+      err = gemmf32::launch_ref(p, s);
+      break;
+  }
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    return GEMM_F32_ERR_LAUNCH;
+  }
+  return GEMM_F32_OK;
+}
+
+// ---- the dispatcher ---------------------------------------------------------
+std::string select_name(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                        const void* A, const void* B) {
+  if (M == 0 || N == 0) return "empty";
+  if (K == 0) return "fill_zero_k0";
+  const bool va = lda % 4 == 0 && aligned16(A);
+  const bool vb = ldb % 4 == 0 && aligned16(B);
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  for (const auto& row : gemmf32::kTuningGfx950) {
+    if (M > row.max_m || tiles < row.min_tiles) continue;
+    std::string base = row.kernel;
+    if (base.rfind("skinny", 0) == 0) return base + (vb ? "_vec" : "_scalar");
+    return base + (va && vb ? "_vec" : va ? "_veca" : vb ? "_vecb" : "_scalar");
+  }
+  return "ref_naive";
+}
+
+struct Prepared {
+  int status;
+  int dev;
+  Problem p;
+};
+
+Prepared prepare(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+                 int64_t ldb, float* C, int64_t ldc) {
+  Prepared r{};
+  r.status = check_args(M, N, K, A, lda, B, ldb, C, ldc);
+  if (r.status != GEMM_F32_OK) return r;
+  r.p = Problem{A, B, C, lda, ldb, ldc, (int)M, (int)N, (int)K};
+  if (M == 0 || N == 0) return r;
+  r.status = check_device(&r.dev);
+  if (r.status != GEMM_F32_OK) return r;
+  if (K > 0) {
+    if ((r.status = check_pointer(A, r.dev)) != GEMM_F32_OK) return r;
+    if ((r.status = check_pointer(B, r.dev)) != GEMM_F32_OK) return r;
+  }
+  r.status = check_pointer(C, r.dev);
+  return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+             int64_t ldb, float* C, int64_t ldc, void* stream) {
+  Prepared r = prepare(M, N, K, A, lda, B, ldb, C, ldc);
+  if (r.status != GEMM_F32_OK || M == 0 || N == 0) return r.status;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) {
+    if (gemmf32::launch_fill_zero(r.p, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return GEMM_F32_ERR_LAUNCH;
+    }
+    return GEMM_F32_OK;
+  }
+  const int idx = find_entry(select_name(M, N, K, lda, ldb, A, B));
+  if (idx < 0) return GEMM_F32_ERR_BAD_KERNEL;
+  return run_entry(entries()[idx], r.p, r.dev, s);
+}
+
+int gemm_f32_ref_gpu(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                     const float* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+  Prepared r = prepare(M, N, K, A, lda, B, ldb, C, ldc);
+  if (r.status != GEMM_F32_OK || M == 0 || N == 0) return r.status;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t err =
+      K == 0 ? gemmf32::launch_fill_zero(r.p, s) : gemmf32::launch_ref(r.p, s);
+  if (err != hipSuccess) {
+    (void)hipGetLastError();
+    return GEMM_F32_ERR_LAUNCH;
+  }
+  return GEMM_F32_OK;
+}
+
+int gemm_f32_run_kernel(int index, int64_t M, int64_t N, int64_t K, const float* A,
+                        int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                        void* stream) {
+  const auto& t = entries();
+  if (index < 0 || index >= (int)t.size()) return GEMM_F32_ERR_BAD_KERNEL;
+  Prepared r = prepare(M, N, K, A, lda, B, ldb, C, ldc);
+  if (r.status != GEMM_F32_OK || M == 0 || N == 0) return r.status;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) {
+    if (gemmf32::launch_fill_zero(r.p, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return GEMM_F32_ERR_LAUNCH;
+    }
+    return GEMM_F32_OK;
+  }
+  if (!entry_accepts(t[index], r.p)) return GEMM_F32_ERR_BAD_KERNEL;
+  return run_entry(t[index], r.p, r.dev, s);
+}
+
+const char* gemm_f32_status_string(int status) {
+  switch (status) {
+    case GEMM_F32_OK: return "ok";
+    case GEMM_F32_ERR_INVALID_DIM: return "invalid dimension (M, N or K negative or above GEMM_F32_MAX_DIM)";
+    case GEMM_F32_ERR_INVALID_LD: return "invalid leading dimension (pitch below row length)";
+    case GEMM_F32_ERR_NULL_PTR: return "null pointer for a non-empty matrix";
+    case GEMM_F32_ERR_ALIAS: return "C overlaps A or B";
+    case GEMM_F32_ERR_DEVICE: return "no usable HIP device, or the current device is not gfx950";
+    case GEMM_F32_ERR_WORKSPACE: return "workspace allocation failed";
+    case GEMM_F32_ERR_LAUNCH: return "kernel launch failed";
+    case GEMM_F32_ERR_BAD_KERNEL: return "kernel index unknown or unable to run these arguments";
+    case GEMM_F32_ERR_POINTER: return "pointer is not device memory the current device can access";
+    default: return "unknown status";
+  }
+}
+
+const char* gemm_f32_selected_kernel(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                                     int64_t ldc, const void* A, const void* B, const void* C) {
+  (void)C;
+  const int64_t kMax = GEMM_F32_MAX_DIM;
+  if (M < 0 || N < 0 || K < 0 || M > kMax || N > kMax || K > kMax) return "invalid";
+  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1)) return "invalid";
+  const std::string name = select_name(M, N, K, lda, ldb, A, B);
+  if (name == "empty") return "empty";
+  if (name == "fill_zero_k0") return "fill_zero_k0";
+  const int idx = find_entry(name);
+  return idx < 0 ? "invalid" : entries()[idx].name;
+}
+
+int gemm_f32_version(void) { return GEMM_F32_VERSION; }
+
+int gemm_f32_kernel_count(void) { return (int)entries().size(); }
+
+const char* gemm_f32_kernel_name(int index) {
+  const auto& t = entries();
+  if (index < 0 || index >= (int)t.size()) return nullptr;
+  return t[index].name;
+}
+
+int gemm_f32_release_workspaces(void) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  if (!g_ws) return GEMM_F32_OK;
+  int rc = GEMM_F32_OK;
+  int cur = -1;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : *g_ws) {
+    if (!kv.second.ptr) continue;
+    if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+        hipFree(kv.second.ptr) != hipSuccess) {
+      (void)hipGetLastError();
+      rc = GEMM_F32_ERR_WORKSPACE;
+    }
+  }
+  g_ws->clear();
+  if (have_cur) (void)hipSetDevice(cur);
+  return rc;
+}
+
+}  // extern "C"

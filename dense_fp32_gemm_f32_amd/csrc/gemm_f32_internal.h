@@ -1,0 +1,59 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace gemmf32 {
+
+// One GEMM call after validation: C[i*ldc+j] = sum_k A[i*lda+k] * B[k*ldb+j]
+// for 0 <= i < M, 0 <= j < N.  M, N, K fit in int32; pitches are 64-bit.
+struct Problem {
+  const float* A;
+  const float* B;
+  float* C;
+  int64_t lda, ldb, ldc;
+  int M, N, K;
+};
+
+// ---- macro-tiled fp32 MFMA kernel --------------------------------------
+struct MfmaVariant {
+  const char* name;
+  int bm, bn, bk;      // workgroup tile
+  int wm, wn;          // wave tile
+  bool vec_a, vec_b;   // 128-bit global loads of A / B (needs 16-byte rows)
+  hipError_t (*launch)(const Problem&, hipStream_t);
+};
+int mfma_variant_count();
+const MfmaVariant& mfma_variant(int i);
+
+// ---- skinny-M split-K kernel --------------------------------------------
+struct SkinnyPlan {
+  int splits;          // workgroups along K for one column strip
+  int kslice;          // K rows per workgroup (multiple of waves x unroll)
+  int strips;          // column strips of 256
+  size_t partial_floats;   // workspace floats for the partial sums (0 if splits == 1)
+  size_t counter_words;    // workspace uint32 arrival counters
+  size_t lds_bytes;        // dynamic LDS
+};
+struct SkinnyVariant {
+  const char* name;
+  int mr;              // rows of A handled (M <= mr)
+  int waves;           // waves per workgroup
+  int unroll;          // B rows in flight per wave
+  bool vec_b;          // 128-bit loads of B
+  int target_splits;   // preferred number of K splits (0 = choose from the shape)
+  SkinnyPlan (*plan)(const Problem&, int target_splits);
+  hipError_t (*launch)(const Problem&, const SkinnyPlan&, float* partials,
+                       unsigned* counters, hipStream_t);
+};
+int skinny_variant_count();
+const SkinnyVariant& skinny_variant(int i);
+
+// ---- naive reference and the K == 0 fill ----------------------------------
+hipError_t launch_ref(const Problem& p, hipStream_t s);
+hipError_t launch_fill_zero(const Problem& p, hipStream_t s);
+
+}  // namespace gemmf32

@@ -1,0 +1,143 @@
+/*
+ * gemm_f32.h -- C ABI of the MI355X (gfx950) dense fp32 GEMM library.
+ *
+ * Operation.  C = A x B for row-major fp32 matrices: A is M x K, B is K x N,
+ * C is M x N, and element (i, j) of C is row i of A dotted with column j of B.
+ * This is the operation every kernel of "Optimizing a WebGPU Matmul Kernel
+ * using Subgroups" computes (section 1 Naive defines it, sections 2-8 keep
+ * it), that "WebGPU 行列積の限界を測る" states as C = A x B for N x N
+ * matrices, and that the ybb.press page and "WebGPU WGSL Compute Shaders:
+ * Custom Matrix Multiplication (GEMM) Optimization Guide" (section 4) write
+ * with separate M, N, K sizes and guarded edges.
+ *
+ * Arithmetic.  Products and sums are fp32 (the pages accumulate in an f32
+ * variable).  The order of the K-term summation is not specified; results on
+ * small-integer inputs are exact, and on general inputs every element is
+ * within the usual fp32 summation error of the exact dot product.
+ * Bitwise-identical inputs on the same device give bitwise-identical outputs.
+ *
+ * Layout.  Row-major with leading dimensions (row pitches, in elements):
+ *   A[i*lda + k], B[k*ldb + j], C[i*ldc + j].
+ * Required: lda >= max(1, K), ldb >= max(1, N), ldc >= max(1, N).
+ * Only the M x N window of C is written; the rest of each C row (the pitch
+ * padding) and everything outside the window is never read or written.
+ * C's previous contents are never read (C is overwritten, no alpha/beta).
+ * K == 0 writes +0.0 to the window.  M == 0 or N == 0 is a successful no-op.
+ *
+ * Memory and ownership.  A, B and C are caller-owned device memory that the
+ * current HIP device can access (hipMalloc or a torch CUDA/HIP tensor).  The
+ * library keeps no reference to them after the call returns.  It owns only
+ * its code objects and, for the skinny-M kernel, a scratch workspace (per
+ * device and stream, allocated on first need, freed by
+ * gemm_f32_release_workspaces or at unload).  C must not overlap A or B.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ * stream).  Work is enqueued on it and the call returns without waiting; the
+ * caller synchronises.  Calls on one stream are ordered by the stream; calls
+ * on different streams may run concurrently (each stream has its own
+ * workspace).
+ *
+ * Errors.  Every function returns a status; no exceptions cross the ABI and
+ * there is no global error state.  Arguments are checked before anything is
+ * enqueued, in the order of the codes below (dimensions, pitches, pointers,
+ * aliasing, device), so a bad call changes nothing.  Sizes above
+ * GEMM_F32_MAX_DIM in M, N or K are rejected as GEMM_F32_ERR_INVALID_DIM.
+ */
+#ifndef GEMM_F32_H
+#define GEMM_F32_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GEMM_F32_VERSION 1
+
+/* Largest accepted M, N or K (2^31 - 2^16: tile arithmetic stays in int32). */
+#define GEMM_F32_MAX_DIM INT64_C(2147418112)
+
+enum gemm_f32_status {
+  GEMM_F32_OK = 0,
+  GEMM_F32_ERR_INVALID_DIM = 1,   /* M, N or K negative or above GEMM_F32_MAX_DIM */
+  GEMM_F32_ERR_INVALID_LD = 2,    /* a pitch below the row length (or below 1) */
+  GEMM_F32_ERR_NULL_PTR = 3,      /* NULL A, B or C where the matrix has elements */
+  GEMM_F32_ERR_ALIAS = 4,         /* C's extent overlaps A's or B's */
+  GEMM_F32_ERR_DEVICE = 5,        /* no HIP device, or the current one is not gfx950 */
+  GEMM_F32_ERR_WORKSPACE = 6,     /* scratch workspace could not be allocated */
+  GEMM_F32_ERR_LAUNCH = 7,        /* the kernel launch reported an error */
+  GEMM_F32_ERR_BAD_KERNEL = 8,    /* unknown kernel index, or one that cannot run these arguments */
+  GEMM_F32_ERR_POINTER = 9        /* A, B or C is not memory the current device can access */
+};
+
+/*
+ * gemm_f32 -- C = A x B with the kernel the dispatcher picks from the gfx950
+ * tuning table (macro-tiled MFMA kernel, skinny-M split-K kernel, or the
+ * K == 0 fill).  Arguments as described above.
+ */
+int gemm_f32(int64_t M, int64_t N, int64_t K,
+             const float *A, int64_t lda,
+             const float *B, int64_t ldb,
+             float *C, int64_t ldc,
+             void *stream);
+
+/*
+ * gemm_f32_ref_gpu -- the same operation with the naive one-thread-per-output
+ * kernel ("Optimizing a WebGPU Matmul Kernel using Subgroups", sections 1-3:
+ * one invocation per element of C, adjacent threads on adjacent columns, k
+ * ascending with fp32 fused multiply-add).  Slow; for debugging and as a
+ * second GPU witness.  Same arguments, checks and errors as gemm_f32.
+ */
+int gemm_f32_ref_gpu(int64_t M, int64_t N, int64_t K,
+                     const float *A, int64_t lda,
+                     const float *B, int64_t ldb,
+                     float *C, int64_t ldc,
+                     void *stream);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *gemm_f32_status_string(int status);
+
+/*
+ * gemm_f32_selected_kernel -- name of the tuning-table entry gemm_f32 would
+ * run for these arguments ("empty", "fill_zero_k0", or a kernel name).  Pure
+ * host logic: touches no device and enqueues nothing.  The pointers are only
+ * inspected for 16-byte alignment.  Returns "invalid" for arguments gemm_f32
+ * would reject on dimensions or pitches.
+ */
+const char *gemm_f32_selected_kernel(int64_t M, int64_t N, int64_t K,
+                                     int64_t lda, int64_t ldb, int64_t ldc,
+                                     const void *A, const void *B, const void *C);
+
+/* Library version (GEMM_F32_VERSION). */
+int gemm_f32_version(void);
+
+/*
+ * Kernel table access, for tuning sweeps and for tests that exercise every
+ * kernel variant.  Index range [0, gemm_f32_kernel_count()).
+ * gemm_f32_kernel_name returns NULL for an index out of range.
+ * gemm_f32_run_kernel runs entry `index` exactly as gemm_f32 would run it if
+ * the dispatcher had picked it; entries that cannot handle the arguments
+ * (e.g. a vector-load variant with an unaligned pitch, or a skinny variant
+ * with too many rows) return GEMM_F32_ERR_BAD_KERNEL and enqueue nothing.
+ */
+int gemm_f32_kernel_count(void);
+const char *gemm_f32_kernel_name(int index);
+int gemm_f32_run_kernel(int index,
+                        int64_t M, int64_t N, int64_t K,
+                        const float *A, int64_t lda,
+                        const float *B, int64_t ldb,
+                        float *C, int64_t ldc,
+                        void *stream);
+
+/*
+ * gemm_f32_release_workspaces -- free every scratch workspace the library
+ * holds (all devices, all streams) after synchronising the devices they live
+ * on.  Safe to call at any time no call is in flight from another thread.
+ */
+int gemm_f32_release_workspaces(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F32_H */

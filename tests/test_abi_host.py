@@ -1,0 +1,129 @@
+"""The C ABI on the host: the library loads, exports what the header
+declares, and rejects bad arguments before touching any device.  CPU only:
+no call here reaches a kernel launch."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from dense_fp32_gemm_f32_amd import binding
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "gemm_f32.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_f32\w*)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("gemm_f32", "gemm_f32_ref_gpu", "gemm_f32_status_string",
+                 "gemm_f32_selected_kernel", "gemm_f32_version"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in gemm_f32.h but not exported"
+    assert sorted(binding.EXPORTS) == declared_functions()
+
+
+def test_version():
+    assert binding.gemm_f32_version() == 1
+
+
+def test_status_strings():
+    for code in list(binding.STATUS_NAMES) + [1234]:
+        s = binding.gemm_f32_status_string(code)
+        assert isinstance(s, str) and s
+    assert binding.gemm_f32_status_string(0) == "ok"
+
+
+def test_kernel_table():
+    names = binding.kernel_names()
+    assert len(names) == len(set(names)) == binding.gemm_f32_kernel_count()
+    assert any(n.startswith("mfma_") for n in names)
+    assert any(n.startswith("skinny_") for n in names)
+    assert "ref_naive" in names
+    assert binding.gemm_f32_kernel_name(-1) is None
+    assert binding.gemm_f32_kernel_name(len(names)) is None
+
+
+# Pointers that are never dereferenced: these calls fail validation first.
+P16 = 0x10000
+Q16 = 0x90000000
+R16 = 0x190000000
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 4, 4, P16, 4, Q16, 4, R16, 4), 1),
+    ((4, -1, 4, P16, 4, Q16, 4, R16, 4), 1),
+    ((4, 4, -1, P16, 4, Q16, 4, R16, 4), 1),
+    ((2 ** 31 - 2 ** 16 + 1, 4, 4, P16, 4, Q16, 4, R16, 4), 1),
+    ((4, 4, 4, P16, 3, Q16, 4, R16, 4), 2),
+    ((4, 4, 4, P16, 4, Q16, 3, R16, 4), 2),
+    ((4, 4, 4, P16, 4, Q16, 4, R16, 3), 2),
+    ((4, 4, 0, P16, 0, Q16, 4, R16, 4), 2),
+    ((4, 4, 4, 0, 4, Q16, 4, R16, 4), 3),
+    ((4, 4, 4, P16, 4, 0, 4, R16, 4), 3),
+    ((4, 4, 4, P16, 4, Q16, 4, 0, 4), 3),
+    ((4, 4, 4, P16, 4, Q16, 4, P16 + 8, 4), 4),
+    ((4, 4, 4, P16, 4, Q16, 4, Q16 + 60, 4), 4),
+])
+def test_argument_errors_before_any_device_call(args, code):
+    assert binding.gemm_f32(*args, 0) == code
+    assert binding.gemm_f32_ref_gpu(*args, 0) == code
+    assert binding.gemm_f32_run_kernel(0, *args, 0) == code
+
+
+def test_empty_problems_succeed_without_a_device():
+    assert binding.gemm_f32(0, 4, 4, 0, 4, Q16, 4, 0, 4, 0) == 0
+    assert binding.gemm_f32(4, 0, 4, P16, 4, 0, 1, 0, 1, 0) == 0
+    # a NULL A is fine when A has no elements, even if M > 0 (K == 0), but the
+    # K == 0 fill needs a device, so only the M == 0 / N == 0 cases run here
+
+
+def test_adjacent_but_not_overlapping_is_not_alias():
+    # C starts right after A's last element: validation passes, then the
+    # device check (no GPU here, or a real one) decides; never ERR_ALIAS.
+    rc = binding.gemm_f32(4, 4, 4, P16, 4, Q16, 4, P16 + 64, 4, 0)
+    assert rc != 4
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,A,B,expect", [
+    (0, 5, 5, 5, 5, P16, Q16, "empty"),
+    (5, 0, 5, 5, 1, P16, Q16, "empty"),
+    (5, 5, 0, 1, 5, P16, Q16, "fill_zero_k0"),
+    (8, 8192, 8192, 8192, 8192, P16, Q16, "skinny_m8_"),
+    (3, 8192, 8192, 8192, 8192, P16, Q16, "skinny_m4_"),
+    (16, 4096, 4096, 4096, 4096, P16, Q16, "skinny_m16_"),
+    (8, 3001, 1531, 1531, 3001, P16, Q16, "skinny_m8_"),
+    (4096, 4096, 4096, 4096, 4096, P16, Q16, "mfma_128x128"),
+    (2047, 3001, 1531, 1531, 3001, P16, Q16, "mfma_128x128"),
+    (512, 512, 512, 512, 512, P16, Q16, "mfma_64x64"),
+])
+def test_dispatcher_families(M, N, K, lda, ldb, A, B, expect):
+    name = binding.gemm_f32_selected_kernel(M, N, K, lda, ldb, max(N, 1), A, B, R16)
+    assert name.startswith(expect), name
+
+
+def test_dispatcher_load_width_follows_alignment():
+    sel = binding.gemm_f32_selected_kernel
+    assert sel(4096, 4096, 4096, 4096, 4096, 4096, P16, Q16, R16).endswith("_vec")
+    assert sel(4096, 4096, 4096, 4097, 4096, 4096, P16, Q16, R16).endswith("_vecb")
+    assert sel(4096, 4096, 4096, 4096, 4098, 4096, P16, Q16, R16).endswith("_veca")
+    assert sel(4096, 4096, 4096, 4096, 4096, 4096, P16 + 4, Q16 + 8, R16).endswith("_scalar")
+    assert sel(2047, 3001, 1531, 1531, 3001, 3001, P16, Q16, R16).endswith("_scalar")
+    assert sel(8, 8192, 8192, 8192, 8192, 8192, P16, Q16 + 4, R16).endswith("_scalar")
+    assert sel(8, 8192, 8192, 8192, 8192, 8192, P16, Q16, R16).endswith("_vec")
+
+
+def test_dispatcher_rejects_bad_arguments():
+    sel = binding.gemm_f32_selected_kernel
+    assert sel(-1, 4, 4, 4, 4, 4, P16, Q16, R16) == "invalid"
+    assert sel(4, 4, 4, 3, 4, 4, P16, Q16, R16) == "invalid"
