@@ -205,6 +205,7 @@ bool entry_accepts(const Entry& e, const Problem& p) {
   if (e.kind == Kind::Skinny) {
     const auto& v = gemmf32::skinny_variant(e.sub);
     if (p.M > v.mr) return false;
+    if (v.vec_a && !(p.lda % 4 == 0 && aligned16(p.A))) return false;
     if (v.vec_b && !(p.ldb % 4 == 0 && aligned16(p.B))) return false;
     return true;
   }
@@ -254,9 +255,14 @@ std::string select_name(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ld
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   for (const auto& row : gemmf32::kTuningGfx950) {
     if (M > row.max_m || tiles < row.min_tiles) continue;
-    std::string base = row.kernel;
-    if (base.rfind("skinny", 0) == 0) return base + (vb ? "_vec" : "_scalar");
-    return base + (va && vb ? "_vec" : va ? "_veca" : vb ? "_vecb" : "_scalar");
+    std::string name = row.kernel;
+    const size_t cut = name.rfind('_');
+    const std::string base = name.substr(0, cut), width = name.substr(cut + 1);
+    // keep only the 128-bit loads the operands allow
+    const bool want_a = width == "vec" || width == "veca";
+    const bool want_b = width == "vec" || width == "vecb";
+    const bool a = want_a && va, b = want_b && vb;
+    return base + (a && b ? "_vec" : a ? "_veca" : b ? "_vecb" : "_scalar");
   }
   return "ref_naive";
 }

@@ -42,8 +42,9 @@ struct SkinnyVariant {
   const char* name;
   int mr;              // rows of A handled (M <= mr)
   int waves;           // waves per workgroup
-  int unroll;          // B rows in flight per wave
-  bool vec_b;          // 128-bit loads of B
+  int unroll;          // B rows per block (split-K variants)
+  bool vec_a;          // 128-bit loads of A (needs 16-byte A rows)
+  bool vec_b;          // 128-bit loads of B (needs 16-byte B rows)
   int target_splits;   // preferred number of K splits (0 = choose from the shape)
   SkinnyPlan (*plan)(const Problem&, int target_splits);
   hipError_t (*launch)(const Problem&, const SkinnyPlan&, float* partials,

@@ -59,7 +59,7 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n,
   tn = r / gm;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB>
+template <int BM, int BN, int BK, int WM, int WN>
 struct Cfg {
   static constexpr int kWavesM = BM / WM;
   static constexpr int kWavesN = BN / WN;
@@ -72,33 +72,38 @@ struct Cfg {
   static constexpr int kVecB = BK * BN / 4 / kThreads;
   static_assert(BM % WM == 0 && BN % WN == 0, "wave tiles must divide the tile");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "swizzles need 64-wide tile rows");
-  static_assert(BK % 4 == 0 && BK >= 8 && (BK & (BK - 1)) == 0, "BK power of two >= 8");
-  static_assert(64 % kChunksA == 0, "a wave covers whole A rows");
+  static_assert(BN % 64 == 0, "the B swizzle needs 64-wide tile rows");
+  static_assert(BK == 8 || BK == 16 || BK == 32, "BK in {8, 16, 32}");
   static_assert((BM * BK / 4) % kThreads == 0 && (BK * BN / 4) % kThreads == 0,
                 "tile loads divide evenly over the threads");
-  // LDS: A stored k-major (A^T tile, m contiguous), B stored k-major (n contiguous).
-  static constexpr int kLdsA = BK * BM;
-  static constexpr int kLdsB = BK * BN;
+  static constexpr int kLdsA = BM * BK;   // [m][k], k contiguous, 16-byte chunks swizzled
+  static constexpr int kLdsB = BK * BN;   // [k][n], n contiguous, swizzled
 };
 
-// XOR swizzle of the m index of the k-major A tile.  The 4-wide k chunk c of
-// a global load row lands in its own group of 64/kChunks banks, and rows k
-// and k+1 (read together by one MFMA A fragment: lanes 0-31 and 32-63) land
-// in opposite halves of the 64 banks.
+// A tile in LDS: row m holds BK floats as kChunks 16-byte chunks; logical
+// chunk c of row m sits at chunk c ^ swz_a(m).  Sixteen consecutive rows with
+// the same logical chunk then cover all 64 banks, so both the 128-bit
+// fragment reads (one row per lane) and the 128-bit tile writes are free of
+// bank conflicts.
 template <int kChunks>
-__device__ __forceinline__ int swz_a(int k) {
-  const int c = (k >> 2) & (kChunks - 1);
-  return (c ^ ((k & 1) * (kChunks / 2))) * (64 / kChunks);
+__device__ __forceinline__ int swz_a(int m) {
+  return (m / (16 / kChunks)) % kChunks;
 }
-// Rows k and k+1 of the B tile in opposite halves of the 64 banks.
-__device__ __forceinline__ int swz_b(int k) { return (k & 1) << 5; }
+// B tile in LDS: n of row k is XORed with 32 when bit 2 of k is set, so the
+// rows k and k + 4 read together by one fragment land in opposite bank halves.
+__device__ __forceinline__ int swz_b(int k) { return ((k >> 2) & 1) << 5; }
+
+// MFMA k-slot assignment.  One ds_read_b128 gives lane l four consecutive k
+// of its A row: k = 8q + 4*(l/32) + s for s = 0..3.  MFMA step s therefore
+// multiplies, in k-slot h = l/32, the term k = 8q + 4h + s; the B fragment of
+// step s supplies B[8q + 4h + s][n] in the same slot.  Each k of the 8-wide
+// group is used exactly once, so the sum is the same dot product.
 
 template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB, int kMinWaves>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     __attribute__((amdgpu_waves_per_eu(kMinWaves)))
     mfma_gemm_kernel(Problem p, int tiles_m, int tiles_n) {
-  using C_ = Cfg<BM, BN, BK, WM, WN, VA, VB>;
+  using C_ = Cfg<BM, BN, BK, WM, WN>;
   __shared__ __attribute__((aligned(16))) float lds_a[2][C_::kLdsA];
   __shared__ __attribute__((aligned(16))) float lds_b[2][C_::kLdsB];
 
@@ -108,10 +113,11 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
   int tm, tn;
   tile_coords(xcd_contiguous_id(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
+  const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
 
   // ---- global -> register staging ----------------------------------------
-  // A: thread loads float4 chunks along k; row = v / kChunksA.
-  // B: thread loads float4 chunks along n; row = v / kChunksB.
+  // A: float4 chunk c of tile row `row` (k = 4c..4c+3).
+  // B: float4 chunk of tile row `krow` (n = nc..nc+3).
   const float* a_ptr[C_::kVecA];
   bool a_row_ok[C_::kVecA];
 #pragma unroll
@@ -123,29 +129,49 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     a_ptr[v] = p.A + (int64_t)(a_row_ok[v] ? gr : 0) * p.lda + kc;
   }
   const float* b_ptr[C_::kVecB];
-  bool b_col_ok[C_::kVecB];  // whole float4 inside N
-  int b_ncol[C_::kVecB];     // global column of the chunk
+  int b_ncol[C_::kVecB];
 #pragma unroll
   for (int v = 0; v < C_::kVecB; ++v) {
     const int e = tid + v * C_::kThreads;
     const int krow = e / C_::kChunksB, nc = (e % C_::kChunksB) * 4;
     b_ncol[v] = n0 + nc;
-    b_col_ok[v] = n0 + nc + 3 < N;
     b_ptr[v] = p.B + (int64_t)krow * p.ldb + (b_ncol[v] < N ? b_ncol[v] : 0);
   }
 
   float4 ra[C_::kVecA], rb[C_::kVecB];
 
-  auto load_tiles = [&](int k0) {
+  // Interior K-tile of an interior output tile: no masks.
+  auto load_tiles_full = [&](int k0) {
+#pragma unroll
+    for (int v = 0; v < C_::kVecA; ++v) {
+      const float* src = a_ptr[v] + k0;
+      if (VA) {
+        ra[v] = *reinterpret_cast<const float4*>(src);
+      } else {
+        ra[v] = make_float4(src[0], src[1], src[2], src[3]);
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < C_::kVecB; ++v) {
+      const float* src = b_ptr[v] + (int64_t)k0 * p.ldb;
+      if (VB) {
+        rb[v] = *reinterpret_cast<const float4*>(src);
+      } else {
+        rb[v] = make_float4(src[0], src[1], src[2], src[3]);
+      }
+    }
+  };
+  // Any K-tile: elements outside M x K (A) or K x N (B) become 0.0.
+  auto load_tiles_masked = [&](int k0) {
 #pragma unroll
     for (int v = 0; v < C_::kVecA; ++v) {
       const int e = tid + v * C_::kThreads;
       const int gk = k0 + (e % C_::kChunksA) * 4;
       const float* src = a_ptr[v] + k0;
-      if (VA && a_row_ok[v] && gk + 3 < K) {
+      const bool ok = a_row_ok[v];
+      if (VA && ok && gk + 3 < K) {
         ra[v] = *reinterpret_cast<const float4*>(src);
       } else {
-        const bool ok = a_row_ok[v];
         ra[v].x = (ok && gk + 0 < K) ? src[0] : 0.f;
         ra[v].y = (ok && gk + 1 < K) ? src[1] : 0.f;
         ra[v].z = (ok && gk + 2 < K) ? src[2] : 0.f;
@@ -158,15 +184,22 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
       const int gk = k0 + e / C_::kChunksB;
       const float* src = b_ptr[v] + (int64_t)k0 * p.ldb;
       const bool kok = gk < K;
-      if (VB && kok && b_col_ok[v]) {
+      const int nn = b_ncol[v];
+      if (VB && kok && nn + 3 < N) {
         rb[v] = *reinterpret_cast<const float4*>(src);
       } else {
-        const int nn = b_ncol[v];
         rb[v].x = (kok && nn + 0 < N) ? src[0] : 0.f;
         rb[v].y = (kok && nn + 1 < N) ? src[1] : 0.f;
         rb[v].z = (kok && nn + 2 < N) ? src[2] : 0.f;
         rb[v].w = (kok && nn + 3 < N) ? src[3] : 0.f;
       }
+    }
+  };
+  auto load_tiles = [&](int k0) {
+    if (full_mn && k0 + BK <= K) {
+      load_tiles_full(k0);
+    } else {
+      load_tiles_masked(k0);
     }
   };
 
@@ -176,11 +209,8 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 #pragma unroll
     for (int v = 0; v < C_::kVecA; ++v) {
       const int e = tid + v * C_::kThreads;
-      const int row = e / C_::kChunksA, kc = (e % C_::kChunksA) * 4;
-      la[(kc + 0) * BM + (row ^ swz_a<C_::kChunksA>(kc + 0))] = ra[v].x;
-      la[(kc + 1) * BM + (row ^ swz_a<C_::kChunksA>(kc + 1))] = ra[v].y;
-      la[(kc + 2) * BM + (row ^ swz_a<C_::kChunksA>(kc + 2))] = ra[v].z;
-      la[(kc + 3) * BM + (row ^ swz_a<C_::kChunksA>(kc + 3))] = ra[v].w;
+      const int row = e / C_::kChunksA, c = e % C_::kChunksA;
+      *reinterpret_cast<float4*>(&la[row * BK + 4 * (c ^ swz_a<C_::kChunksA>(row))]) = ra[v];
     }
 #pragma unroll
     for (int v = 0; v < C_::kVecB; ++v) {
@@ -194,8 +224,19 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
   const int wave = tid >> 6, lane = tid & 63;
   const int wmi = wave % C_::kWavesM, wni = wave / C_::kWavesM;
   const int lr = lane & 31, lk = lane >> 5;
-  const int am = wmi * WM + lr;   // + 32 * fragment
-  const int bn = wni * WN + lr;
+  // per-lane LDS offsets of the fragments (in floats, within one buffer)
+  int a_off[C_::kFragM][BK / 8];
+#pragma unroll
+  for (int i = 0; i < C_::kFragM; ++i) {
+    const int row = wmi * WM + 32 * i + lr;
+#pragma unroll
+    for (int q = 0; q < BK / 8; ++q)
+      a_off[i][q] = row * BK + 4 * ((2 * q + lk) ^ swz_a<C_::kChunksA>(row));
+  }
+  // B column of fragment j, swizzled: the k rows a lane reads all have bit 2 == lk
+  int b_off[C_::kFragN];
+#pragma unroll
+  for (int j = 0; j < C_::kFragN; ++j) b_off[j] = (wni * WN + 32 * j + lr) ^ (lk << 5);
 
   floatx16 acc[C_::kFragM][C_::kFragN];
 #pragma unroll
@@ -209,20 +250,25 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     const float* la = lds_a[buf];
     const float* lb = lds_b[buf];
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 2) {
-      const int k = kk + lk;
-      float fa[C_::kFragM], fb[C_::kFragN];
+    for (int q = 0; q < BK / 8; ++q) {
+      float4 fa[C_::kFragM];
 #pragma unroll
       for (int i = 0; i < C_::kFragM; ++i)
-        fa[i] = la[k * BM + ((am + 32 * i) ^ swz_a<C_::kChunksA>(k))];
+        fa[i] = *reinterpret_cast<const float4*>(&la[a_off[i][q]]);
 #pragma unroll
-      for (int j = 0; j < C_::kFragN; ++j)
-        fb[j] = lb[k * BN + ((bn + 32 * j) ^ swz_b(k))];
+      for (int s = 0; s < 4; ++s) {
+        const int krow = 8 * q + 4 * lk + s;
+        float fb[C_::kFragN];
 #pragma unroll
-      for (int i = 0; i < C_::kFragM; ++i)
+        for (int j = 0; j < C_::kFragN; ++j) fb[j] = lb[krow * BN + b_off[j]];
 #pragma unroll
-        for (int j = 0; j < C_::kFragN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < C_::kFragM; ++i) {
+          const float a = s == 0 ? fa[i].x : s == 1 ? fa[i].y : s == 2 ? fa[i].z : fa[i].w;
+#pragma unroll
+          for (int j = 0; j < C_::kFragN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, fb[j], acc[i][j], 0, 0, 0);
+        }
+      }
     }
   };
 
@@ -260,7 +306,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 
 template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB, int kMinWaves>
 hipError_t launch(const Problem& p, hipStream_t s) {
-  using C_ = Cfg<BM, BN, BK, WM, WN, VA, VB>;
+  using C_ = Cfg<BM, BN, BK, WM, WN>;
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
@@ -284,8 +330,13 @@ hipError_t launch(const Problem& p, hipStream_t s) {
    false, &launch<BM, BN, BK, WM, WN, false, false, MW>}
 
 const MfmaVariant kVariants[] = {
+    GEMMF32_MFMA(256, 256, 16, 128, 128, 1),
+    GEMMF32_MFMA(256, 256, 32, 128, 128, 1),
+    GEMMF32_MFMA(256, 128, 16, 128, 64, 2),
+    GEMMF32_MFMA(128, 256, 16, 64, 128, 2),
     GEMMF32_MFMA(128, 128, 16, 64, 64, 4),
     GEMMF32_MFMA(128, 128, 32, 64, 64, 2),
+    GEMMF32_MFMA(128, 64, 16, 64, 32, 4),
     GEMMF32_MFMA(64, 64, 16, 32, 32, 4),
 };
 

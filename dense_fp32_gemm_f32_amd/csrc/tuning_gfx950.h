@@ -1,9 +1,9 @@
 // Tuning table for gfx950 (MI355X): which kernel gemm_f32 runs for a shape.
 //
-// The first row whose bounds hold wins.  A row names a kernel family; the
-// dispatcher appends the load-width suffix the operands allow ("_vec" when
-// the rows of A and B are 16-byte aligned, otherwise "_veca", "_vecb" or
-// "_scalar"; skinny rows: "_vec" or "_scalar" for B).
+// The first row whose bounds hold wins.  A row names the kernel measured
+// fastest for 16-byte aligned operands; when the operands do not allow its
+// 128-bit loads the dispatcher falls back to the variant that they do allow
+// ("_vec" -> "_veca" / "_vecb" -> "_scalar").
 //
 // Columns:
 //   max_m       the row applies when M <= max_m
@@ -24,11 +24,11 @@ struct TuningRow {
 constexpr int64_t kAnyM = INT64_C(0x7fffffff);
 
 constexpr TuningRow kTuningGfx950[] = {
-    {4, 0, "skinny_m4_w4_u8_s0"},
-    {8, 0, "skinny_m8_w4_u8_s0"},
-    {16, 0, "skinny_m16_w4_u4_s0"},
-    {kAnyM, 256, "mfma_128x128x16_w64x64"},
-    {kAnyM, 0, "mfma_64x64x16_w32x32"},
+    {4, 0, "skinnyfk_m4_c32_w16_p0_vec"},
+    {8, 0, "skinnyfk_m8_c32_w16_p0_vec"},
+    {16, 0, "skinnyfk_m16_c32_w8_p0_vec"},
+    {kAnyM, 256, "mfma_128x128x16_w64x64_veca"},
+    {kAnyM, 0, "mfma_64x64x16_w32x32_veca"},
 };
 
 }  // namespace gemmf32

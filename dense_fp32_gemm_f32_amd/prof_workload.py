@@ -1,0 +1,62 @@
+"""A short, profiler-friendly run of one GEMM workload plus a copy of known
+size, for rocprofv3 kernel traces and hardware counters.
+
+    rocprofv3 --kernel-trace --stats -d OUT -o run -f csv -- \
+        python3 -m dense_fp32_gemm_f32_amd.prof_workload --workload square_4096
+    rocprofv3 --pmc FETCH_SIZE -d OUT -o fetch -f csv -- \
+        python3 -m dense_fp32_gemm_f32_amd.prof_workload --workload square_4096
+
+The copy (``torch.Tensor.copy_`` of ``--copy-mib`` MiB, a plain streaming
+kernel that reads and writes exactly that many bytes) calibrates the
+FETCH_SIZE / WRITE_SIZE counters: HBM bytes of a GEMM launch are its counter
+value scaled by (known copy bytes / copy counter value).
+"""
+from __future__ import annotations
+
+import argparse
+import sys
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="square_4096")
+    ap.add_argument("--kernel", default="", help="run this kernel instead of the dispatcher's")
+    ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=0,
+                    help="rotate this many input copies (0: 4 when B exceeds 128 MiB)")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    args = ap.parse_args(argv)
+
+    import torch
+    from dense_fp32_gemm_f32_amd import binding, inputs
+
+    binding.load()
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS[args.workload]
+    copies = args.copies or (4 if 4 * w.K * w.N > 128 * 2 ** 20 else 1)
+    As, Bs, Cs = [], [], []
+    for c in range(copies):
+        a, b = inputs.make_ab(w.M, w.N, w.K, w.dist_a, w.dist_b, w.seed + 100 * c)
+        As.append(a.contiguous().to(dev))
+        Bs.append(b.contiguous().to(dev))
+        Cs.append(torch.empty((w.M, w.N), device=dev))
+    name = args.kernel or binding.selected_kernel(As[0], Bs[0], Cs[0])
+    print(f"workload {w.name}: kernel {name}, {args.reps} launches over {copies} input copies",
+          flush=True)
+    for i in range(args.reps):
+        binding.run_kernel(name, As[i % copies], Bs[i % copies], Cs[i % copies])
+    torch.cuda.synchronize()
+
+    n = args.copy_mib * 2 ** 20 // 4
+    src = torch.ones(n, device=dev)
+    dst = torch.empty(n, device=dev)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"calibration copy: 3 x {args.copy_mib} MiB read + {args.copy_mib} MiB written",
+          flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

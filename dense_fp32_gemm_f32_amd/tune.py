@@ -1,0 +1,107 @@
+"""Time every kernel of the table on given shapes (the sweep that the gfx950
+tuning table in ``csrc/tuning_gfx950.h`` is chosen from).
+
+    python -m dense_fp32_gemm_f32_amd.tune --shapes 4096x4096x4096,8x8192x8192 \
+        [--filter mfma_] [--reps 10] [--json out.json]
+
+A shape is MxNxK (row-major, packed pitches, 16-byte aligned bases).  Each
+kernel that accepts the shape runs ``--warmup`` times, then ``--reps`` times
+with a HIP event pair on the launch stream around each call.  Inputs rotate
+over enough copies to exceed the 256 MB last-level cache when B is large, so
+bandwidth-bound shapes stream from HBM.  Prints one line per (shape, kernel).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+
+
+def parse_shape(s: str):
+    m, n, k = (int(x) for x in s.lower().split("x"))
+    return m, n, k
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--shapes", default="4096x4096x4096")
+    ap.add_argument("--filter", default="", help="comma-separated kernel-name prefixes")
+    ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--json", default="")
+    ap.add_argument("--with-torch", action="store_true",
+                    help="also time torch.matmul in fp32 (vendor library, context only)")
+    args = ap.parse_args(argv)
+
+    import torch
+    from dense_fp32_gemm_f32_amd import binding, inputs
+
+    binding.load()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    names = binding.kernel_names()
+    prefixes = [p for p in args.filter.split(",") if p]
+    rows = []
+    for shape in args.shapes.split(","):
+        M, N, K = parse_shape(shape)
+        b_bytes = 4 * K * N
+        copies = max(1, min(4, -(-1024 * 2 ** 20 // max(b_bytes, 1)))) if b_bytes > 32 * 2 ** 20 else 1
+        As, Bs, Cs = [], [], []
+        for c in range(copies):
+            a, b = inputs.make_ab(M, N, K, "u11", "u11", 9000 + c)
+            As.append(a.to(dev))
+            Bs.append(b.to(dev))
+            Cs.append(torch.empty((M, N), device=dev))
+        flops = 2.0 * M * N * K
+        algo_bytes = 4.0 * (M * K + K * N + M * N)
+        default = binding.selected_kernel(As[0], Bs[0], Cs[0])
+        cands = [(i, n) for i, n in enumerate(names)
+                 if not prefixes or any(n.startswith(p) for p in prefixes)]
+        if args.with_torch:
+            cands.append((-1, "torch.matmul"))
+        for idx, name in cands:
+            if idx >= 0:
+                s = stream.cuda_stream
+
+                def call(i, idx=idx):
+                    a, b, c = As[i % copies], Bs[i % copies], Cs[i % copies]
+                    return binding.gemm_f32_run_kernel(idx, M, N, K, a.data_ptr(), K,
+                                                       b.data_ptr(), N, c.data_ptr(), N, s)
+                if call(0) != 0:
+                    continue   # kernel does not accept this shape
+            else:
+                torch.backends.cuda.matmul.allow_tf32 = False
+
+                def call(i):
+                    torch.matmul(As[i % copies], Bs[i % copies], out=Cs[i % copies])
+                    return 0
+            for i in range(args.warmup):
+                call(i)
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.reps)]
+            for i in range(args.reps):
+                evs[i][0].record(stream)
+                call(i)
+                evs[i][1].record(stream)
+            torch.cuda.synchronize()
+            ms = [a.elapsed_time(b) for a, b in evs]
+            mean = sum(ms) / len(ms)
+            row = {"shape": f"{M}x{N}x{K}", "kernel": name, "default": name == default,
+                   "mean_us": round(mean * 1e3, 2), "min_us": round(min(ms) * 1e3, 2),
+                   "tflops": round(flops / (mean * 1e-3) / 1e12, 2),
+                   "gbs": round(algo_bytes / (mean * 1e-3) / 1e9, 1)}
+            rows.append(row)
+            print(f"{row['shape']:>16} {name:<40} {'*' if row['default'] else ' '} "
+                  f"{row['mean_us']:>10.2f} us  min {row['min_us']:>10.2f}  "
+                  f"{row['tflops']:>8.2f} TFLOP/s  {row['gbs']:>9.1f} GB/s", flush=True)
+        del As, Bs, Cs
+        torch.cuda.empty_cache()
+    if args.json:
+        with open(args.json, "w") as f:
+            json.dump(rows, f, indent=1)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

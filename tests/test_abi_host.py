@@ -99,10 +99,10 @@ def test_adjacent_but_not_overlapping_is_not_alias():
     (0, 5, 5, 5, 5, P16, Q16, "empty"),
     (5, 0, 5, 5, 1, P16, Q16, "empty"),
     (5, 5, 0, 1, 5, P16, Q16, "fill_zero_k0"),
-    (8, 8192, 8192, 8192, 8192, P16, Q16, "skinny_m8_"),
-    (3, 8192, 8192, 8192, 8192, P16, Q16, "skinny_m4_"),
-    (16, 4096, 4096, 4096, 4096, P16, Q16, "skinny_m16_"),
-    (8, 3001, 1531, 1531, 3001, P16, Q16, "skinny_m8_"),
+    (8, 8192, 8192, 8192, 8192, P16, Q16, "skinnyfk_m8_"),
+    (3, 8192, 8192, 8192, 8192, P16, Q16, "skinnyfk_m4_"),
+    (16, 4096, 4096, 4096, 4096, P16, Q16, "skinnyfk_m16_"),
+    (8, 3001, 1531, 1531, 3001, P16, Q16, "skinnyfk_m8_"),
     (4096, 4096, 4096, 4096, 4096, P16, Q16, "mfma_128x128"),
     (2047, 3001, 1531, 1531, 3001, P16, Q16, "mfma_128x128"),
     (512, 512, 512, 512, 512, P16, Q16, "mfma_64x64"),
@@ -113,13 +113,27 @@ def test_dispatcher_families(M, N, K, lda, ldb, A, B, expect):
 
 
 def test_dispatcher_load_width_follows_alignment():
+    """Each table row names its preferred load widths; they are kept only
+    where the operands allow them."""
     sel = binding.gemm_f32_selected_kernel
-    assert sel(4096, 4096, 4096, 4096, 4096, 4096, P16, Q16, R16).endswith("_vec")
-    assert sel(4096, 4096, 4096, 4097, 4096, 4096, P16, Q16, R16).endswith("_vecb")
-    assert sel(4096, 4096, 4096, 4096, 4098, 4096, P16, Q16, R16).endswith("_veca")
+    names = binding.kernel_names()
+    for args in [(4096, 4096, 4096, 4096, 4096, 4096), (4096, 4096, 4096, 4097, 4096, 4096),
+                 (4096, 4096, 4096, 4096, 4098, 4096), (1000, 999, 777, 777, 999, 999)]:
+        M, N, K, lda, ldb, ldc = args
+        for pa, pb in [(P16, Q16), (P16 + 4, Q16), (P16, Q16 + 8), (P16 + 4, Q16 + 4)]:
+            name = sel(M, N, K, lda, ldb, ldc, pa, pb, R16)
+            assert name in names
+            width = name.rsplit("_", 1)[1]
+            a_ok = lda % 4 == 0 and pa % 16 == 0
+            b_ok = ldb % 4 == 0 and pb % 16 == 0
+            if width in ("vec", "veca"):
+                assert a_ok
+            if width in ("vec", "vecb"):
+                assert b_ok
     assert sel(4096, 4096, 4096, 4096, 4096, 4096, P16 + 4, Q16 + 8, R16).endswith("_scalar")
     assert sel(2047, 3001, 1531, 1531, 3001, 3001, P16, Q16, R16).endswith("_scalar")
-    assert sel(8, 8192, 8192, 8192, 8192, 8192, P16, Q16 + 4, R16).endswith("_scalar")
+    assert sel(8, 8192, 8192, 8192, 8192, 8192, P16, Q16 + 4, R16).endswith("_veca")
+    assert sel(8, 8192, 8192, 8192, 8192, 8192, P16 + 4, Q16 + 4, R16).endswith("_scalar")
     assert sel(8, 8192, 8192, 8192, 8192, 8192, P16, Q16, R16).endswith("_vec")
 
 

@@ -224,32 +224,36 @@ def test_errors_from_the_device_side(gpu_lib):
     torch.cuda.synchronize()
 
 
+SPLITK = "skinny_m8_w8_u4_s8_vecb"   # a kernel that combines K slices in a workspace
+
+
 def test_workspace_failure_is_reported(gpu_lib, monkeypatch):
     A = torch.ones((8, 4096), device="cuda")
     B = torch.ones((4096, 4096), device="cuda")
     C = torch.empty((8, 4096), device="cuda")
+    idx = gpu_lib.kernel_index(SPLITK)
     monkeypatch.setenv("GEMM_F32_TEST_FAIL_WORKSPACE", "1")
     s = torch.cuda.current_stream().cuda_stream
-    rc = gpu_lib.gemm_f32(8, 4096, 4096, A.data_ptr(), 4096, B.data_ptr(), 4096,
-                          C.data_ptr(), 4096, s)
+    rc = gpu_lib.gemm_f32_run_kernel(idx, 8, 4096, 4096, A.data_ptr(), 4096, B.data_ptr(),
+                                     4096, C.data_ptr(), 4096, s)
     assert rc == 6
     monkeypatch.delenv("GEMM_F32_TEST_FAIL_WORKSPACE")
-    gpu_lib.gemm(A, B, C)
+    gpu_lib.run_kernel(SPLITK, A, B, C)
     torch.cuda.synchronize()
     assert torch.all(C == 4096)
 
 
 def test_two_streams_concurrently(gpu_lib):
-    """Skinny calls on two streams use separate workspaces and both match."""
+    """Split-K calls on two streams use separate workspaces and both match."""
     A1, B1 = inputs.make_ab(8, 4096, 8192, "normal", "u11", 8001)
     A2, B2 = inputs.make_ab(6, 4096, 8192, "normal", "u11", 8002)
     dA1, dB1, dA2, dB2 = (t.cuda() for t in (A1, B1, A2, B2))
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     torch.cuda.synchronize()
     with torch.cuda.stream(s1):
-        C1 = gpu_lib.gemm(dA1, dB1)
+        C1 = gpu_lib.run_kernel(SPLITK, dA1, dB1)
     with torch.cuda.stream(s2):
-        C2 = gpu_lib.gemm(dA2, dB2)
+        C2 = gpu_lib.run_kernel(SPLITK, dA2, dB2)
     torch.cuda.synchronize()
     for (A, B, C) in ((A1, B1, C1), (A2, B2, C2)):
         C_ref, ABS = H.oracle_of(A, B)
