@@ -135,27 +135,24 @@ int check_pointer(const void* p, int dev) {
 }
 
 // ---- skinny-kernel workspace, one per (device, stream) ----------------------
-// Layout: [arrival counters, 256-byte aligned][partial sums].  The counters
-// are zeroed once when the buffer is created; every call leaves them at zero.
+// Holds the per-slice partial sums of the skinny kernel.  Kept for the life of
+// the process (or until gemm_f32_release_workspaces) and grown on demand.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
-  size_t counter_bytes = 0;
 };
 std::mutex g_ws_mu;
 std::map<std::pair<int, uintptr_t>, Workspace>* g_ws = nullptr;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int get_workspace(int dev, hipStream_t s, size_t counter_words, size_t partial_floats,
-                  unsigned** counters, float** partials) {
-  const size_t cbytes = round_up(counter_words * 4, 256);
-  const size_t need = cbytes + partial_floats * 4;
+int get_workspace(int dev, hipStream_t s, size_t partial_floats, float** partials) {
+  const size_t need = partial_floats * 4;
   if (std::getenv("GEMM_F32_TEST_FAIL_WORKSPACE")) return GEMM_F32_ERR_WORKSPACE;
   std::lock_guard<std::mutex> lk(g_ws_mu);
   if (!g_ws) g_ws = new std::map<std::pair<int, uintptr_t>, Workspace>();
   Workspace& w = (*g_ws)[{dev, (uintptr_t)s}];
-  if (w.bytes < need || w.counter_bytes < cbytes) {
+  if (w.bytes < need) {
     if (w.ptr) {
       // the stream may still be using the old buffer
       if (hipStreamSynchronize(s) != hipSuccess || hipFree(w.ptr) != hipSuccess) {
@@ -165,24 +162,16 @@ int get_workspace(int dev, hipStream_t s, size_t counter_words, size_t partial_f
       w = Workspace{};
     }
     // grow with headroom so alternating shapes do not reallocate
-    const size_t cb = cbytes > 4096 ? cbytes : 4096;
-    const size_t bytes = cb + round_up(partial_floats * 4 + partial_floats * 2, 1 << 20);
+    const size_t bytes = round_up(need + need / 2, 1 << 20);
     void* p = nullptr;
     if (hipMalloc(&p, bytes) != hipSuccess) {
       (void)hipGetLastError();
       return GEMM_F32_ERR_WORKSPACE;
     }
-    if (hipMemsetAsync(p, 0, cb, s) != hipSuccess) {
-      (void)hipGetLastError();
-      (void)hipFree(p);
-      return GEMM_F32_ERR_WORKSPACE;
-    }
     w.ptr = p;
     w.bytes = bytes;
-    w.counter_bytes = cb;
   }
-  *counters = static_cast<unsigned*>(w.ptr);
-  *partials = reinterpret_cast<float*>(static_cast<char*>(w.ptr) + w.counter_bytes);
+  *partials = static_cast<float*>(w.ptr);
   return GEMM_F32_OK;
 }
 
@@ -224,14 +213,12 @@ int run_entry(const Entry& e, const Problem& p, int dev, hipStream_t s) {
     case Kind::Skinny: {
       const auto& v = gemmf32::skinny_variant(e.sub);
       const gemmf32::SkinnyPlan pl = v.plan(p, v.target_splits);
-      unsigned* counters = nullptr;
       float* partials = nullptr;
       if (pl.splits > 1) {
-        const int rc =
-            get_workspace(dev, s, pl.counter_words, pl.partial_floats, &counters, &partials);
+        const int rc = get_workspace(dev, s, pl.partial_floats, &partials);
         if (rc != GEMM_F32_OK) return rc;
       }
-      err = v.launch(p, pl, partials, counters, s);
+      err = v.launch(p, pl, partials, s);
       break;
     }
     case Kind::Ref:

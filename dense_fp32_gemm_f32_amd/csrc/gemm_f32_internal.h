@@ -29,26 +29,24 @@ struct MfmaVariant {
 int mfma_variant_count();
 const MfmaVariant& mfma_variant(int i);
 
-// ---- skinny-M split-K kernel --------------------------------------------
+// ---- skinny-M kernel (column tiles x K slices, then a combine) ------------
 struct SkinnyPlan {
-  int splits;          // workgroups along K for one column strip
-  int kslice;          // K rows per workgroup (multiple of waves x unroll)
-  int strips;          // column strips of 256
+  int splits;              // K slices (workgroups along K for one column tile)
+  int kslice;              // 16-row super-blocks per slice
+  int strips;              // column tiles
   size_t partial_floats;   // workspace floats for the partial sums (0 if splits == 1)
-  size_t counter_words;    // workspace uint32 arrival counters
   size_t lds_bytes;        // dynamic LDS
 };
 struct SkinnyVariant {
   const char* name;
   int mr;              // rows of A handled (M <= mr)
   int waves;           // waves per workgroup
-  int unroll;          // B rows per block (split-K variants)
+  int unroll;          // super-blocks in flight per wave
   bool vec_a;          // 128-bit loads of A (needs 16-byte A rows)
-  bool vec_b;          // 128-bit loads of B (needs 16-byte B rows)
-  int target_splits;   // preferred number of K splits (0 = choose from the shape)
+  bool vec_b;          // wide loads of B (needs 16-byte B rows)
+  int target_splits;   // K slices (0 = choose from the shape)
   SkinnyPlan (*plan)(const Problem&, int target_splits);
-  hipError_t (*launch)(const Problem&, const SkinnyPlan&, float* partials,
-                       unsigned* counters, hipStream_t);
+  hipError_t (*launch)(const Problem&, const SkinnyPlan&, float* partials, hipStream_t);
 };
 int skinny_variant_count();
 const SkinnyVariant& skinny_variant(int i);

@@ -24,9 +24,7 @@ struct TuningRow {
 constexpr int64_t kAnyM = INT64_C(0x7fffffff);
 
 constexpr TuningRow kTuningGfx950[] = {
-    {4, 0, "skinnyfk_m4_c32_w16_p0_vec"},
-    {8, 0, "skinnyfk_m8_c32_w16_p0_vec"},
-    {16, 0, "skinnyfk_m16_c32_w8_p0_vec"},
+    {16, 0, "skinny_w8_c4_u4_s0_vec"},
     {kAnyM, 256, "mfma_128x128x16_w64x64_veca"},
     {kAnyM, 0, "mfma_64x64x16_w32x32_veca"},
 };

@@ -99,10 +99,10 @@ def test_adjacent_but_not_overlapping_is_not_alias():
     (0, 5, 5, 5, 5, P16, Q16, "empty"),
     (5, 0, 5, 5, 1, P16, Q16, "empty"),
     (5, 5, 0, 1, 5, P16, Q16, "fill_zero_k0"),
-    (8, 8192, 8192, 8192, 8192, P16, Q16, "skinnyfk_m8_"),
-    (3, 8192, 8192, 8192, 8192, P16, Q16, "skinnyfk_m4_"),
-    (16, 4096, 4096, 4096, 4096, P16, Q16, "skinnyfk_m16_"),
-    (8, 3001, 1531, 1531, 3001, P16, Q16, "skinnyfk_m8_"),
+    (8, 8192, 8192, 8192, 8192, P16, Q16, "skinny_w8_c4"),
+    (3, 8192, 8192, 8192, 8192, P16, Q16, "skinny_w8_c4"),
+    (16, 4096, 4096, 4096, 4096, P16, Q16, "skinny_w8_c4"),
+    (8, 3001, 1531, 1531, 3001, P16, Q16, "skinny_w8_c4"),
     (4096, 4096, 4096, 4096, 4096, P16, Q16, "mfma_128x128"),
     (2047, 3001, 1531, 1531, 3001, P16, Q16, "mfma_128x128"),
     (512, 512, 512, 512, 512, P16, Q16, "mfma_64x64"),
@@ -118,7 +118,9 @@ def test_dispatcher_load_width_follows_alignment():
     sel = binding.gemm_f32_selected_kernel
     names = binding.kernel_names()
     for args in [(4096, 4096, 4096, 4096, 4096, 4096), (4096, 4096, 4096, 4097, 4096, 4096),
-                 (4096, 4096, 4096, 4096, 4098, 4096), (1000, 999, 777, 777, 999, 999)]:
+                 (4096, 4096, 4096, 4096, 4098, 4096), (1000, 999, 777, 777, 999, 999),
+                 (8, 8192, 8192, 8192, 8192, 8192), (1, 100, 100, 101, 100, 100),
+                 (16, 64, 64, 64, 64, 64), (17, 64, 64, 64, 64, 64), (300, 40, 50, 50, 40, 40)]:
         M, N, K, lda, ldb, ldc = args
         for pa, pb in [(P16, Q16), (P16 + 4, Q16), (P16, Q16 + 8), (P16 + 4, Q16 + 4)]:
             name = sel(M, N, K, lda, ldb, ldc, pa, pb, R16)

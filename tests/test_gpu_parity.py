@@ -76,8 +76,7 @@ def _kernel_case(name):
     vec_a = suffix in ("vec", "veca")
     vec_b = suffix in ("vec", "vecb")
     if name.startswith("skinny"):
-        mr = int(name.split("_m")[1].split("_")[0])
-        M, N, K = mr - 1 if mr > 1 else 1, 1000 + 3, 2050
+        M, N, K = 13, 1000 + 3, 2050 + 7
     elif name.startswith("mfma"):
         M, N, K = 301, 263, 139
     else:
@@ -218,13 +217,13 @@ def test_errors_from_the_device_side(gpu_lib):
     # unknown kernel index, and a skinny kernel with too many rows
     assert b.gemm_f32_run_kernel(10 ** 6, 64, 64, 64, A.data_ptr(), 64, B.data_ptr(), 64,
                                  C.data_ptr(), 64, s) == 8
-    sk = [i for i, n in enumerate(b.kernel_names()) if n.startswith("skinny_m4")][0]
+    sk = [i for i, n in enumerate(b.kernel_names()) if n.startswith("skinny_")][0]
     assert b.gemm_f32_run_kernel(sk, 64, 64, 64, A.data_ptr(), 64, B.data_ptr(), 64,
                                  C.data_ptr(), 64, s) == 8
     torch.cuda.synchronize()
 
 
-SPLITK = "skinny_m8_w8_u4_s8_vecb"   # a kernel that combines K slices in a workspace
+SPLITK = "skinny_w16_c4_u4_s8_vec"   # a kernel that combines K slices in a workspace
 
 
 def test_workspace_failure_is_reported(gpu_lib, monkeypatch):
