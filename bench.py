@@ -19,7 +19,6 @@ of the same workload (the first R rows of A), scaled to GFLOP/s.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -75,17 +74,10 @@ def traffic_for(kernel_name: str):
         rec = json.loads(f.read_text()).get(kernel_name)
     except ValueError:
         return None
-    if not rec or rec.get("source_sha256") != kernel_source_hash():
+    from dense_fp32_gemm_f32_amd.prof_summary import source_hash
+    if not rec or rec.get("source_sha256") != source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in sorted((ROOT / "dense_fp32_gemm_f32_amd" / "csrc").glob("*")):
-        h.update(p.name.encode())
-        h.update(p.read_bytes())
-    return h.hexdigest()
 
 
 def cpu_baseline(w, target_s):

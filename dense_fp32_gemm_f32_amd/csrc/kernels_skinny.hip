@@ -214,23 +214,47 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4)
   }
 }
 
-// C[m][n] = sum over slices, in slice order, of part[slice][m][n].
+// C[m][n] = sum over slices, in slice order, of part[slice][m][n].  A thread
+// owns four consecutive elements of the flattened M x N partial array (loaded
+// as one 16-byte chunk when M*N is a multiple of 4).
 __global__ void __launch_bounds__(256) skinny_combine_kernel(Problem p, int slices,
                                                              const float* __restrict__ part) {
   const int64_t mn = (int64_t)p.M * p.N;
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= mn) return;
-  const int m = (int)(e / p.N), n = (int)(e % p.N);
-  float v[8];
-  float s = 0.f;
-  for (int s0 = 0; s0 < slices; s0 += 8) {
+  const int64_t e0 = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+  if (e0 >= mn) return;
+  const bool vec = (mn % 4) == 0;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < slices; s0 += 4) {
+    float4 v[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = s0 + j < slices ? part[(size_t)(s0 + j) * mn + e] : 0.f;
+    for (int j = 0; j < 4; ++j) {
+      const float* src = part + (size_t)(s0 + j) * mn + e0;
+      if (s0 + j >= slices) {
+        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      } else if (vec) {
+        v[j] = *reinterpret_cast<const float4*>(src);
+      } else {
+        v[j].x = src[0];
+        v[j].y = e0 + 1 < mn ? src[1] : 0.f;
+        v[j].z = e0 + 2 < mn ? src[2] : 0.f;
+        v[j].w = e0 + 3 < mn ? src[3] : 0.f;
+      }
+    }
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (s0 + j < slices) s += v[j];
+    for (int j = 0; j < 4; ++j) {
+      if (s0 + j < slices) {
+        s[0] += v[j].x;
+        s[1] += v[j].y;
+        s[2] += v[j].z;
+        s[3] += v[j].w;
+      }
+    }
   }
-  p.C[(int64_t)m * p.ldc + n] = s;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t e = e0 + q;
+    if (e < mn) p.C[(e / p.N) * p.ldc + e % p.N] = s[q];
+  }
 }
 
 // Slices: enough workgroups for every CU (or `target` slices if given), each
@@ -267,7 +291,7 @@ hipError_t launch_tile(const Problem& p, const SkinnyPlan& pl, float* partials, 
   const float* cpart = partials;
   void* cargs[] = {&pp, &slices, &cpart};
   return hipLaunchKernel(reinterpret_cast<const void*>(&skinny_combine_kernel),
-                         dim3((unsigned)((mn + 255) / 256)), dim3(256), cargs, 0, s);
+                         dim3((unsigned)((mn + 1023) / 1024)), dim3(256), cargs, 0, s);
 }
 
 #define GEMMF32_SKINNY_TILE(NW, CG, U, S)                                                   \
@@ -287,10 +311,12 @@ const SkinnyVariant kVariants[] = {
     GEMMF32_SKINNY_TILE(8, 1, 4, 1),
     GEMMF32_SKINNY_TILE(16, 4, 4, 0),    // 128 columns, K split to fill the GPU
     GEMMF32_SKINNY_TILE(8, 4, 4, 0),
-    GEMMF32_SKINNY_TILE(16, 4, 4, 8),
     GEMMF32_SKINNY_TILE(16, 2, 4, 0),    // 64 columns
     GEMMF32_SKINNY_TILE(8, 8, 4, 0),     // 256 columns
-    GEMMF32_SKINNY_TILE(16, 4, 6, 0),
+    GEMMF32_SKINNY_TILE(8, 4, 4, 2),
+    GEMMF32_SKINNY_TILE(8, 2, 4, 0),
+    GEMMF32_SKINNY_TILE(4, 4, 4, 0),
+    GEMMF32_SKINNY_TILE(16, 8, 4, 0),
 };
 
 }  // namespace

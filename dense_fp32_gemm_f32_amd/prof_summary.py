@@ -1,0 +1,156 @@
+"""Summarise rocprofv3 output (CSV) for ``profiles/``.
+
+    python -m dense_fp32_gemm_f32_amd.prof_summary \
+        --workload square_4096 --kernel mfma_128x128x16_w64x64_veca \
+        --match mfma_gemm_kernel --trace OUT/trace --fetch OUT/fetch --write OUT/write \
+        [--sq OUT/sq] --command "..." --out profiles/mfma_gemm_square_4096.md
+
+--trace: a ``--kernel-trace --stats`` run; --fetch / --write: ``--pmc FETCH_SIZE`` and
+``--pmc WRITE_SIZE`` runs of ``prof_workload`` (which ends with a copy of known
+size); --sq: an optional run with SQ/GRBM counters.  HBM bytes per launch are
+the kernel's FETCH_SIZE and WRITE_SIZE (KiB) scaled by the ratio of the copy's
+known bytes to its own counter values.  The result is written as a short
+markdown summary, and the per-launch bytes are recorded in
+``profiles/traffic.json`` under the kernel's table name together with a hash of
+the kernel sources (bench.py reports them only while the sources match).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+from collections import defaultdict
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent.parent
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted((ROOT / "dense_fp32_gemm_f32_amd" / "csrc").glob("*")):
+        h.update(p.name.encode())
+        h.update(p.read_bytes())
+    return h.hexdigest()
+
+
+def _find(d: Path, suffix: str) -> Path:
+    hits = sorted(Path(d).rglob(f"*{suffix}"))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def counters(d: Path):
+    """{kernel name: {counter: [values per dispatch]}} from a --pmc run."""
+    out = defaultdict(lambda: defaultdict(list))
+    with open(_find(d, "counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            out[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return out
+
+
+def durations(d: Path):
+    """{kernel name: (calls, avg ns, min ns, max ns)} from a --stats run."""
+    res = {}
+    with open(_find(d, "kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            res[r["Name"]] = (int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                              float(r["MaxNs"]))
+    return res
+
+
+def pick(names, match):
+    hits = [n for n in names if match in n]
+    if not hits:
+        raise KeyError(f"no kernel matching {match!r} in {list(names)}")
+    return hits
+
+
+def mean(v):
+    return sum(v) / len(v)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--kernel", required=True, help="table name of the kernel")
+    ap.add_argument("--match", required=True, help="substring of the rocprof kernel name(s)")
+    ap.add_argument("--trace", required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--sq")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--algo-bytes", type=float, required=True)
+    ap.add_argument("--flops", type=float, required=True)
+    ap.add_argument("--command", action="append", default=[])
+    ap.add_argument("--out", required=True)
+    args = ap.parse_args(argv)
+
+    lines = [f"# {args.kernel} on {args.workload}", ""]
+    lines += ["Commands (from the repository root on the MI355X box):", ""]
+    lines += [f"    {c}" for c in args.command] + [""]
+
+    dur = durations(Path(args.trace))
+    names = pick(dur, args.match)
+    lines += ["## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    tot_avg = 0.0
+    for n in names:
+        calls, avg, mn, mx = dur[n]
+        tot_avg += avg
+        lines.append(f"| `{n[:110]}` | {calls} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} |")
+    lines += ["", f"Sum of average durations of the matched kernels: {tot_avg / 1e3:.2f} us "
+              f"-> {args.flops / (tot_avg * 1e-9) / 1e12:.2f} TFLOP/s, "
+              f"{args.algo_bytes / (tot_avg * 1e-9) / 1e9:.1f} GB/s of algorithmic traffic", ""]
+
+    traffic = None
+    if args.fetch and args.write:
+        fc, wc = counters(Path(args.fetch)), counters(Path(args.write))
+        cf = mean(fc[COPY_KERNEL]["FETCH_SIZE"]) * 1024.0
+        cw = mean(wc[COPY_KERNEL]["WRITE_SIZE"]) * 1024.0
+        f_scale, w_scale = args.copy_bytes / cf, args.copy_bytes / cw
+        fetch = sum(mean(fc[n]["FETCH_SIZE"]) for n in pick(fc, args.match)) * 1024.0 * f_scale
+        write = sum(mean(wc[n]["WRITE_SIZE"]) for n in pick(wc, args.match)) * 1024.0 * w_scale
+        traffic = fetch + write
+        lines += ["## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
+                  f"Calibration copy of {args.copy_bytes} bytes: FETCH_SIZE reads "
+                  f"{cf:.0f} B (scale {f_scale:.3f}), WRITE_SIZE reads {cw:.0f} B "
+                  f"(scale {w_scale:.3f}).", "",
+                  "| per launch | bytes | x algorithmic |", "|---|---|---|",
+                  f"| fetched (scaled) | {fetch:.4g} | {fetch / args.algo_bytes:.3f} |",
+                  f"| written (scaled) | {write:.4g} | {write / args.algo_bytes:.3f} |",
+                  f"| total | {traffic:.4g} | {traffic / args.algo_bytes:.3f} |",
+                  f"| algorithmic 4(MK+KN+MN) | {args.algo_bytes:.4g} | 1 |", ""]
+
+    if args.sq:
+        sc = counters(Path(args.sq))
+        n = pick(sc, args.match)[0]
+        c = {k: mean(v) for k, v in sc[n].items()}
+        lines += ["## Core counters (first matched kernel, mean per dispatch)", "",
+                  "| counter | value |", "|---|---|"]
+        lines += [f"| {k} | {v:.6g} |" for k, v in sorted(c.items())]
+        if "GRBM_GUI_ACTIVE" in c and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            xcd_cycles = c["GRBM_GUI_ACTIVE"] / 8.0     # summed over the 8 XCDs
+            util = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * 1024.0)
+            lines += ["", f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/8 x 1024 SIMDs) "
+                          f"= {100 * util:.1f}%"]
+        if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_LDS_IDX_ACTIVE"):
+            lines += [f"LDS bank-conflict cycles / LDS active cycles = "
+                      f"{c['SQ_LDS_BANK_CONFLICT'] / c['SQ_LDS_IDX_ACTIVE']:.3f}"]
+        lines.append("")
+
+    Path(args.out).write_text("\n".join(lines) + "\n")
+    if traffic is not None:
+        tf = ROOT / "profiles" / "traffic.json"
+        rec = json.loads(tf.read_text()) if tf.exists() else {}
+        rec[args.kernel] = {"workload": args.workload, "hbm_bytes_per_launch": round(traffic),
+                            "algo_bytes": args.algo_bytes, "source_sha256": source_hash(),
+                            "summary": str(Path(args.out).name)}
+        tf.write_text(json.dumps(rec, indent=1, sort_keys=True) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()

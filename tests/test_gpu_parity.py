@@ -223,7 +223,7 @@ def test_errors_from_the_device_side(gpu_lib):
     torch.cuda.synchronize()
 
 
-SPLITK = "skinny_w16_c4_u4_s8_vec"   # a kernel that combines K slices in a workspace
+SPLITK = "skinny_w8_c4_u4_s0_vec"   # a kernel that combines K slices in a workspace
 
 
 def test_workspace_failure_is_reported(gpu_lib, monkeypatch):
