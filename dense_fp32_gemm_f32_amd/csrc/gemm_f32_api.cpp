@@ -54,7 +54,7 @@ int find_entry(const std::string& name) {
   return -1;
 }
 
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 // ---- argument checks (host only, nothing enqueued) -------------------------
 int check_args(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
@@ -71,6 +71,8 @@ int check_args(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, con
     return GEMM_F32_ERR_INVALID_LD;
   const bool has_a = M > 0 && K > 0, has_b = K > 0 && N > 0, has_c = M > 0 && N > 0;
   if ((has_a && !A) || (has_b && !B) || (has_c && !C)) return GEMM_F32_ERR_NULL_PTR;
+  if ((has_a && !aligned4(A)) || (has_b && !aligned4(B)) || (has_c && !aligned4(C)))
+    return GEMM_F32_ERR_POINTER;
   if (has_c) {
     const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(((M - 1) * ldc + N) * 4);
     if (has_a) {
@@ -187,16 +189,12 @@ bool log_enabled() {
 bool entry_accepts(const Entry& e, const Problem& p) {
   if (e.kind == Kind::Mfma) {
     const auto& v = gemmf32::mfma_variant(e.sub);
-    if (v.vec_a && !(p.lda % 4 == 0 && aligned16(p.A))) return false;
-    if (v.vec_b && !(p.ldb % 4 == 0 && aligned16(p.B))) return false;
+    (void)v;   // 128-bit loads need only the 4-byte alignment checked up front
     return true;
   }
   if (e.kind == Kind::Skinny) {
     const auto& v = gemmf32::skinny_variant(e.sub);
-    if (p.M > v.mr) return false;
-    if (v.vec_a && !(p.lda % 4 == 0 && aligned16(p.A))) return false;
-    if (v.vec_b && !(p.ldb % 4 == 0 && aligned16(p.B))) return false;
-    return true;
+    return p.M <= v.mr;
   }
   return true;
 }
@@ -237,8 +235,10 @@ std::string select_name(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ld
                         const void* A, const void* B) {
   if (M == 0 || N == 0) return "empty";
   if (K == 0) return "fill_zero_k0";
-  const bool va = lda % 4 == 0 && aligned16(A);
-  const bool vb = ldb % 4 == 0 && aligned16(B);
+  // 128-bit loads need only 4-byte aligned rows, which every accepted call has
+  const bool va = aligned4(A), vb = aligned4(B);
+  (void)lda;
+  (void)ldb;
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   for (const auto& row : gemmf32::kTuningGfx950) {
     if (M > row.max_m || tiles < row.min_tiles) continue;

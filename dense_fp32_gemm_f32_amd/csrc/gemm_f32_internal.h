@@ -23,7 +23,7 @@ struct MfmaVariant {
   const char* name;
   int bm, bn, bk;      // workgroup tile
   int wm, wn;          // wave tile
-  bool vec_a, vec_b;   // 128-bit global loads of A / B (needs 16-byte rows)
+  bool vec_a, vec_b;   // 128-bit global loads of A / B (any pitch, 4-byte aligned)
   hipError_t (*launch)(const Problem&, hipStream_t);
 };
 int mfma_variant_count();

@@ -35,6 +35,15 @@ namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
+// 16 bytes from a float address that is only 4-byte aligned.  Multi-dword
+// global loads on gfx950 need dword alignment only, and the compiler emits one
+// global_load_dwordx4 for this copy, so rows with any pitch load at 128 bits.
+__device__ __forceinline__ float4 load4(const float* p) {
+  float4 v;
+  __builtin_memcpy(&v, p, sizeof(v));
+  return v;
+}
+
 constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kGroupM = 8;   // tile rows per raster group
 
@@ -99,7 +108,13 @@ __device__ __forceinline__ int swz_b(int k) { return ((k >> 2) & 1) << 5; }
 // step s supplies B[8q + 4h + s][n] in the same slot.  Each k of the 8-wide
 // group is used exactly once, so the sum is the same dot product.
 
-template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB, int kMinWaves>
+// SCHED 0: the next K-tile is written to LDS after all MFMAs of this one.
+// SCHED 1: it is written after the first half of them, so the write, the
+//          barrier and the first fragment reads of the next tile overlap the
+//          second half.
+// SCHED 2: as 1, and the wave runs at raised priority while it issues memory
+//          instructions, lowered again for the MFMAs.
+template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB, int kMinWaves, int SCHED>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     __attribute__((amdgpu_waves_per_eu(kMinWaves)))
     mfma_gemm_kernel(Problem p, int tiles_m, int tiles_n) {
@@ -146,7 +161,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     for (int v = 0; v < C_::kVecA; ++v) {
       const float* src = a_ptr[v] + k0;
       if (VA) {
-        ra[v] = *reinterpret_cast<const float4*>(src);
+        ra[v] = load4(src);
       } else {
         ra[v] = make_float4(src[0], src[1], src[2], src[3]);
       }
@@ -155,7 +170,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     for (int v = 0; v < C_::kVecB; ++v) {
       const float* src = b_ptr[v] + (int64_t)k0 * p.ldb;
       if (VB) {
-        rb[v] = *reinterpret_cast<const float4*>(src);
+        rb[v] = load4(src);
       } else {
         rb[v] = make_float4(src[0], src[1], src[2], src[3]);
       }
@@ -170,7 +185,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
       const float* src = a_ptr[v] + k0;
       const bool ok = a_row_ok[v];
       if (VA && ok && gk + 3 < K) {
-        ra[v] = *reinterpret_cast<const float4*>(src);
+        ra[v] = load4(src);
       } else {
         ra[v].x = (ok && gk + 0 < K) ? src[0] : 0.f;
         ra[v].y = (ok && gk + 1 < K) ? src[1] : 0.f;
@@ -186,7 +201,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
       const bool kok = gk < K;
       const int nn = b_ncol[v];
       if (VB && kok && nn + 3 < N) {
-        rb[v] = *reinterpret_cast<const float4*>(src);
+        rb[v] = load4(src);
       } else {
         rb[v].x = (kok && nn + 0 < N) ? src[0] : 0.f;
         rb[v].y = (kok && nn + 1 < N) ? src[1] : 0.f;
@@ -246,11 +261,12 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](int buf) {
+  // MFMAs of the 8-wide k groups [q0, q1) of LDS buffer `buf`
+  auto compute = [&](int buf, int q0, int q1) {
     const float* la = lds_a[buf];
     const float* lb = lds_b[buf];
 #pragma unroll
-    for (int q = 0; q < BK / 8; ++q) {
+    for (int q = q0; q < q1; ++q) {
       float4 fa[C_::kFragM];
 #pragma unroll
       for (int i = 0; i < C_::kFragM; ++i)
@@ -274,15 +290,22 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 
   // ---- K loop: double-buffered LDS, one barrier per K-tile ---------------
   const int ktiles = (K + BK - 1) / BK;
+  constexpr int kGroups = BK / 8;
+  constexpr int kHalf = SCHED == 0 ? kGroups : (kGroups + 1) / 2;
   load_tiles(0);
   store_tiles(0);
   __syncthreads();
   for (int t = 0; t < ktiles; ++t) {
     const int cur = t & 1;
     const bool more = t + 1 < ktiles;
+    if (SCHED == 2) __builtin_amdgcn_s_setprio(1);
     if (more) load_tiles((t + 1) * BK);
-    compute(cur);
+    if (SCHED == 2) __builtin_amdgcn_s_setprio(0);
+    compute(cur, 0, kHalf);
+    if (SCHED == 2) __builtin_amdgcn_s_setprio(1);
     if (more) store_tiles(cur ^ 1);
+    if (SCHED == 2) __builtin_amdgcn_s_setprio(0);
+    compute(cur, kHalf, kGroups);
     __syncthreads();
   }
 
@@ -304,7 +327,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB, int kMinWaves>
+template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB, int kMinWaves, int SCHED>
 hipError_t launch(const Problem& p, hipStream_t s) {
   using C_ = Cfg<BM, BN, BK, WM, WN>;
   const int tiles_m = (p.M + BM - 1) / BM;
@@ -315,19 +338,21 @@ hipError_t launch(const Problem& p, hipStream_t s) {
   int tm = tiles_m, tn = tiles_n;
   void* args[] = {&pp, &tm, &tn};
   return hipLaunchKernel(
-      reinterpret_cast<const void*>(&mfma_gemm_kernel<BM, BN, BK, WM, WN, VA, VB, kMinWaves>),
+      reinterpret_cast<const void*>(
+          &mfma_gemm_kernel<BM, BN, BK, WM, WN, VA, VB, kMinWaves, SCHED>),
       dim3((unsigned)tiles), dim3(C_::kThreads), args, 0, s);
 }
 
-#define GEMMF32_MFMA(BM, BN, BK, WM, WN, MW)                                           \
-  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_vec", BM, BN, BK, WM, WN, true, true, \
-   &launch<BM, BN, BK, WM, WN, true, true, MW>},                                       \
-  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_veca", BM, BN, BK, WM, WN, true, false,\
-   &launch<BM, BN, BK, WM, WN, true, false, MW>},                                      \
-  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_vecb", BM, BN, BK, WM, WN, false, true,\
-   &launch<BM, BN, BK, WM, WN, false, true, MW>},                                      \
-  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_scalar", BM, BN, BK, WM, WN, false,  \
-   false, &launch<BM, BN, BK, WM, WN, false, false, MW>}
+#define GEMMF32_MFMA_S(BM, BN, BK, WM, WN, MW, SC, TAG)                                     \
+  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_vec", BM, BN, BK, WM, WN, true, true,   \
+   &launch<BM, BN, BK, WM, WN, true, true, MW, SC>},                                         \
+  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_veca", BM, BN, BK, WM, WN, true, false, \
+   &launch<BM, BN, BK, WM, WN, true, false, MW, SC>},                                        \
+  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_vecb", BM, BN, BK, WM, WN, false, true, \
+   &launch<BM, BN, BK, WM, WN, false, true, MW, SC>},                                        \
+  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_scalar", BM, BN, BK, WM, WN, false,    \
+   false, &launch<BM, BN, BK, WM, WN, false, false, MW, SC>}
+#define GEMMF32_MFMA(BM, BN, BK, WM, WN, MW) GEMMF32_MFMA_S(BM, BN, BK, WM, WN, MW, 0, "")
 
 const MfmaVariant kVariants[] = {
     GEMMF32_MFMA(256, 256, 16, 128, 128, 1),
@@ -338,6 +363,12 @@ const MfmaVariant kVariants[] = {
     GEMMF32_MFMA(128, 128, 32, 64, 64, 2),
     GEMMF32_MFMA(128, 64, 16, 64, 32, 4),
     GEMMF32_MFMA(64, 64, 16, 32, 32, 4),
+    GEMMF32_MFMA_S(128, 128, 16, 64, 64, 4, 1, "_s1"),
+    GEMMF32_MFMA_S(128, 128, 16, 64, 64, 4, 2, "_s2"),
+    GEMMF32_MFMA_S(128, 128, 32, 64, 64, 2, 1, "_s1"),
+    GEMMF32_MFMA_S(256, 256, 32, 128, 128, 1, 1, "_s1"),
+    GEMMF32_MFMA_S(256, 128, 16, 128, 64, 2, 1, "_s1"),
+    GEMMF32_MFMA_S(128, 256, 16, 64, 128, 2, 1, "_s1"),
 };
 
 }  // namespace

@@ -45,8 +45,9 @@ constexpr int kGroupCols = 32;   // columns per wave: 16 lanes x float2
 // branch and the compiler can wait for each load precisely.  Columns past N
 // are read at a clamped address and replaced by 0.0 where they are used.
 // `tail`: this wave also takes the last K % 16 rows, masked element by element.
-// PAIR: one 8-byte load for the lane's two columns (B rows 16-byte aligned, N
-// even), else two 4-byte loads.  VA: A rows 16-byte aligned.
+// PAIR: one 8-byte load for the lane's two columns (B and its pitch 8-byte
+// aligned, N even), else two 4-byte loads.  VA: one 16-byte load of A per
+// super-block (any pitch), else four 4-byte loads.
 template <int U, bool PAIR, bool VA>
 __device__ __forceinline__ void stream_tile(const Problem& p, int lane, int n0, int first,
                                             int end, int step, bool tail,
@@ -85,7 +86,9 @@ __device__ __forceinline__ void stream_tile(const Problem& p, int lane, int n0, 
       }
     }
     if (VA) {
-      x.a = *reinterpret_cast<const float4*>(arow + k0);
+      // 16 bytes from a 4-byte aligned address: multi-dword global loads need
+      // dword alignment only, and this copy becomes one global_load_dwordx4
+      __builtin_memcpy(&x.a, arow + k0, sizeof(x.a));
     } else {
       x.a = make_float4(arow[k0], arow[k0 + 1], arow[k0 + 2], arow[k0 + 3]);
     }
@@ -179,7 +182,9 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4)
   const bool tail = (K % 16 != 0) && slice == slices - 1 && rg == (sb_end - sb_begin) % NRG;
 
   float out[2][4];
-  if (VB && (N % 2) == 0) {
+  const bool pair = VB && (N % 2) == 0 && (p.ldb % 2) == 0 &&
+                    (reinterpret_cast<uintptr_t>(p.B) & 7) == 0;
+  if (pair) {
     stream_tile<U, true, VA>(p, lane, n_wg + cg * kGroupCols, sb_begin + rg, sb_end, NRG,
                              tail, out);
   } else {

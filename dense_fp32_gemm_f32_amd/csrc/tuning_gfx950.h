@@ -25,7 +25,8 @@ constexpr int64_t kAnyM = INT64_C(0x7fffffff);
 
 constexpr TuningRow kTuningGfx950[] = {
     {16, 0, "skinny_w8_c4_u4_s0_vec"},
-    {kAnyM, 256, "mfma_128x128x16_w64x64_veca"},
+    {kAnyM, 768, "mfma_128x128x16_w64x64_s2_veca"},
+    {kAnyM, 256, "mfma_128x64x16_w64x32_veca"},
     {kAnyM, 0, "mfma_64x64x16_w32x32_veca"},
 };
 

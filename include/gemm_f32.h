@@ -39,8 +39,9 @@
  *
  * Errors.  Every function returns a status; no exceptions cross the ABI and
  * there is no global error state.  Arguments are checked before anything is
- * enqueued, in the order of the codes below (dimensions, pitches, pointers,
- * aliasing, device), so a bad call changes nothing.  Sizes above
+ * enqueued -- dimensions, pitches, NULL pointers, 4-byte alignment of the
+ * pointers (the natural alignment of float), aliasing, the device, and last
+ * whether the device can reach the pointers -- so a bad call changes nothing.  Sizes above
  * GEMM_F32_MAX_DIM in M, N or K are rejected as GEMM_F32_ERR_INVALID_DIM.
  */
 #ifndef GEMM_F32_H
@@ -67,7 +68,7 @@ enum gemm_f32_status {
   GEMM_F32_ERR_WORKSPACE = 6,     /* scratch workspace could not be allocated */
   GEMM_F32_ERR_LAUNCH = 7,        /* the kernel launch reported an error */
   GEMM_F32_ERR_BAD_KERNEL = 8,    /* unknown kernel index, or one that cannot run these arguments */
-  GEMM_F32_ERR_POINTER = 9        /* A, B or C is not memory the current device can access */
+  GEMM_F32_ERR_POINTER = 9        /* A, B or C not 4-byte aligned, or not memory the current device can access */
 };
 
 /*
@@ -101,8 +102,8 @@ const char *gemm_f32_status_string(int status);
  * gemm_f32_selected_kernel -- name of the tuning-table entry gemm_f32 would
  * run for these arguments ("empty", "fill_zero_k0", or a kernel name).  Pure
  * host logic: touches no device and enqueues nothing.  The pointers are only
- * inspected for 16-byte alignment.  Returns "invalid" for arguments gemm_f32
- * would reject on dimensions or pitches.
+ * inspected for alignment.  Returns "invalid" for arguments gemm_f32 would
+ * reject on dimensions or pitches.
  */
 const char *gemm_f32_selected_kernel(int64_t M, int64_t N, int64_t K,
                                      int64_t lda, int64_t ldb, int64_t ldc,
