@@ -1,5 +1,5 @@
 // C ABI of the gfx950 fp32 GEMM library: argument checks, the tuning-table
-// dispatcher, the skinny kernel's workspace, and the kernel table.
+// dispatcher, the workspace for K-slice partial sums, and the kernel table.
 //
 // The pages pass caller-created buffers and M, N, K to one GEMM entry point
 // ("WebGPU WGSL Compute Shaders: Custom Matrix Multiplication (GEMM)
@@ -26,19 +26,28 @@ using gemmf32::Problem;
 
 namespace {
 
-// ---- kernel table: MFMA variants, skinny variants, the naive kernel -------
-enum class Kind { Mfma, Skinny, Ref };
+// ---- kernel table: MFMA variants (whole K, then K split), skinny variants,
+// the naive kernel ----------------------------------------------------------
+enum class Kind { Mfma, MfmaSplitK, Skinny, Ref };
 struct Entry {
   Kind kind;
-  int sub;  // index within its family
-  const char* name;
+  int sub;           // index within its family
+  std::string name;  // never changes once the table is built
 };
+
+// "mfma_<tile>_<width>" -> "mfma_<tile>_sk_<width>"
+std::string split_k_name(const std::string& name) {
+  const size_t cut = name.rfind('_');
+  return name.substr(0, cut) + "_sk" + name.substr(cut);
+}
 
 const std::vector<Entry>& entries() {
   static const std::vector<Entry> table = [] {
     std::vector<Entry> t;
     for (int i = 0; i < gemmf32::mfma_variant_count(); ++i)
       t.push_back({Kind::Mfma, i, gemmf32::mfma_variant(i).name});
+    for (int i = 0; i < gemmf32::mfma_variant_count(); ++i)
+      t.push_back({Kind::MfmaSplitK, i, split_k_name(gemmf32::mfma_variant(i).name)});
     for (int i = 0; i < gemmf32::skinny_variant_count(); ++i)
       t.push_back({Kind::Skinny, i, gemmf32::skinny_variant(i).name});
     t.push_back({Kind::Ref, 0, "ref_naive"});
@@ -52,6 +61,28 @@ int find_entry(const std::string& name) {
   for (size_t i = 0; i < t.size(); ++i)
     if (name == t[i].name) return (int)i;
   return -1;
+}
+
+// K split of an MFMA entry: slices of whole K-tiles, enough workgroups to
+// fill the GPU when the tile grid alone does not (see tuning_gfx950.h).
+struct MfmaPlan {
+  int slices;
+  int kchunk;
+};
+MfmaPlan plan_mfma(const gemmf32::MfmaVariant& v, const Problem& p, bool split) {
+  const MfmaPlan whole{1, p.K};
+  if (!split) return whole;
+  const int64_t tiles = (int64_t)((p.M + v.bm - 1) / v.bm) * ((p.N + v.bn - 1) / v.bn);
+  const int64_t ktiles = (p.K + v.bk - 1) / v.bk;
+  if (tiles >= gemmf32::kSplitKBelowWorkgroups) return whole;
+  int64_t slices = (gemmf32::kSplitKTargetWorkgroups + tiles - 1) / tiles;
+  const int64_t cap = ktiles / gemmf32::kSplitKMinKTiles;
+  if (slices > cap) slices = cap;
+  if (slices <= 1) return whole;
+  const int64_t per = (ktiles + slices - 1) / slices;   // K-tiles per slice
+  slices = (ktiles + per - 1) / per;                     // no empty slice
+  if (slices <= 1) return whole;
+  return MfmaPlan{(int)slices, (int)(per * v.bk)};
 }
 
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
@@ -136,8 +167,8 @@ int check_pointer(const void* p, int dev) {
   }
 }
 
-// ---- skinny-kernel workspace, one per (device, stream) ----------------------
-// Holds the per-slice partial sums of the skinny kernel.  Kept for the life of
+// ---- workspace for K-slice partial sums, one per (device, stream) -----------
+// Holds the per-slice partial sums of the skinny and split-K MFMA kernels.  Kept for the life of
 // the process (or until gemm_f32_release_workspaces) and grown on demand.
 struct Workspace {
   void* ptr = nullptr;
@@ -187,9 +218,8 @@ bool log_enabled() {
 
 // Can entry e run these arguments?
 bool entry_accepts(const Entry& e, const Problem& p) {
-  if (e.kind == Kind::Mfma) {
-    const auto& v = gemmf32::mfma_variant(e.sub);
-    (void)v;   // 128-bit loads need only the 4-byte alignment checked up front
+  if (e.kind == Kind::Mfma || e.kind == Kind::MfmaSplitK) {
+    // 128-bit loads need only the 4-byte alignment checked up front
     return true;
   }
   if (e.kind == Kind::Skinny) {
@@ -202,12 +232,22 @@ bool entry_accepts(const Entry& e, const Problem& p) {
 int run_entry(const Entry& e, const Problem& p, int dev, hipStream_t s) {
   if (log_enabled())
     std::fprintf(stderr, "[gemm_f32] M=%d N=%d K=%d lda=%lld ldb=%lld ldc=%lld -> %s\n", p.M,
-                 p.N, p.K, (long long)p.lda, (long long)p.ldb, (long long)p.ldc, e.name);
+                 p.N, p.K, (long long)p.lda, (long long)p.ldb, (long long)p.ldc,
+                 e.name.c_str());
   hipError_t err = hipSuccess;
   switch (e.kind) {
     case Kind::Mfma:
-      err = gemmf32::mfma_variant(e.sub).launch(p, s);
+    case Kind::MfmaSplitK: {
+      const auto& v = gemmf32::mfma_variant(e.sub);
+      const MfmaPlan pl = plan_mfma(v, p, e.kind == Kind::MfmaSplitK);
+      float* partials = nullptr;
+      if (pl.slices > 1) {
+        const int rc = get_workspace(dev, s, (size_t)pl.slices * p.M * p.N, &partials);
+        if (rc != GEMM_F32_OK) return rc;
+      }
+      err = v.launch(p, pl.slices, pl.kchunk, partials, s);
       break;
+    }
     case Kind::Skinny: {
       const auto& v = gemmf32::skinny_variant(e.sub);
       const gemmf32::SkinnyPlan pl = v.plan(p, v.target_splits);
@@ -357,7 +397,7 @@ const char* gemm_f32_selected_kernel(int64_t M, int64_t N, int64_t K, int64_t ld
   if (name == "empty") return "empty";
   if (name == "fill_zero_k0") return "fill_zero_k0";
   const int idx = find_entry(name);
-  return idx < 0 ? "invalid" : entries()[idx].name;
+  return idx < 0 ? "invalid" : entries()[idx].name.c_str();
 }
 
 int gemm_f32_version(void) { return GEMM_F32_VERSION; }
@@ -367,7 +407,7 @@ int gemm_f32_kernel_count(void) { return (int)entries().size(); }
 const char* gemm_f32_kernel_name(int index) {
   const auto& t = entries();
   if (index < 0 || index >= (int)t.size()) return nullptr;
-  return t[index].name;
+  return t[index].name.c_str();
 }
 
 int gemm_f32_release_workspaces(void) {

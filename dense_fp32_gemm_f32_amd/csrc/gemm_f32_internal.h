@@ -19,12 +19,16 @@ struct Problem {
 };
 
 // ---- macro-tiled fp32 MFMA kernel --------------------------------------
+// slices == 1: one workgroup per output tile over all of K, writing C.
+// slices > 1: K is cut into slices of kchunk (a multiple of bk); slice s
+// writes its partial product to partials + s*M*N (pitch N) and a combine
+// dispatch sums the slices into C in slice order.
 struct MfmaVariant {
   const char* name;
   int bm, bn, bk;      // workgroup tile
   int wm, wn;          // wave tile
   bool vec_a, vec_b;   // 128-bit global loads of A / B (any pitch, 4-byte aligned)
-  hipError_t (*launch)(const Problem&, hipStream_t);
+  hipError_t (*launch)(const Problem&, int slices, int kchunk, float* partials, hipStream_t);
 };
 int mfma_variant_count();
 const MfmaVariant& mfma_variant(int i);
@@ -50,6 +54,9 @@ struct SkinnyVariant {
 };
 int skinny_variant_count();
 const SkinnyVariant& skinny_variant(int i);
+
+// ---- sum of K-slice partials: C = part[0] + part[1] + ... (slice order) ---
+hipError_t launch_combine(const Problem& p, int slices, const float* partials, hipStream_t s);
 
 // ---- naive reference and the K == 0 fill ----------------------------------
 hipError_t launch_ref(const Problem& p, hipStream_t s);

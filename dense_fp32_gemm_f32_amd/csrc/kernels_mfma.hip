@@ -117,16 +117,33 @@ __device__ __forceinline__ int swz_b(int k) { return ((k >> 2) & 1) << 5; }
 template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB, int kMinWaves, int SCHED>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     __attribute__((amdgpu_waves_per_eu(kMinWaves)))
-    mfma_gemm_kernel(Problem p, int tiles_m, int tiles_n) {
+    mfma_gemm_kernel(Problem p, int tiles_m, int tiles_n, int kchunk, float* part) {
   using C_ = Cfg<BM, BN, BK, WM, WN>;
   __shared__ __attribute__((aligned(16))) float lds_a[2][C_::kLdsA];
   __shared__ __attribute__((aligned(16))) float lds_b[2][C_::kLdsB];
 
   const int tid = threadIdx.x;
+
+  // Workgroup -> (K slice, tile).  Consecutive ids of one XCD stay within one
+  // slice, so neighbouring tiles of a slice share that XCD's L2.
+  const int tiles = tiles_m * tiles_n;
+  int lin = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  const int slice = lin / tiles;
+  lin -= slice * tiles;
+  if (part) {
+    // this slice is the GEMM of A[:, k0:k0+K'] and B[k0:k0+K', :] into its
+    // own packed partial buffer
+    const int k0 = slice * kchunk;
+    p.A += k0;
+    p.B += (int64_t)k0 * p.ldb;
+    p.K = min(kchunk, p.K - k0);
+    p.C = part + (size_t)slice * p.M * p.N;
+    p.ldc = p.N;
+  }
   const int M = p.M, N = p.N, K = p.K;
 
   int tm, tn;
-  tile_coords(xcd_contiguous_id(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+  tile_coords(lin, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const bool full_mn = (m0 + BM <= M) && (n0 + BN <= N);
 
@@ -328,19 +345,28 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB, int kMinWaves, int SCHED>
-hipError_t launch(const Problem& p, hipStream_t s) {
+hipError_t launch(const Problem& p, int slices, int kchunk, float* partials, hipStream_t s) {
   using C_ = Cfg<BM, BN, BK, WM, WN>;
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
-  if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (slices < 1 || tiles * slices > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (slices > 1) {
+    // every slice non-empty and whole K-tiles except the last
+    if (!partials || kchunk <= 0 || kchunk % BK != 0 ||
+        (int64_t)(slices - 1) * kchunk >= p.K || (int64_t)slices * kchunk < p.K)
+      return hipErrorInvalidValue;
+  }
   Problem pp = p;
-  int tm = tiles_m, tn = tiles_n;
-  void* args[] = {&pp, &tm, &tn};
-  return hipLaunchKernel(
+  int tm = tiles_m, tn = tiles_n, kc = kchunk;
+  float* part = slices > 1 ? partials : nullptr;
+  void* args[] = {&pp, &tm, &tn, &kc, &part};
+  const hipError_t err = hipLaunchKernel(
       reinterpret_cast<const void*>(
           &mfma_gemm_kernel<BM, BN, BK, WM, WN, VA, VB, kMinWaves, SCHED>),
-      dim3((unsigned)tiles), dim3(C_::kThreads), args, 0, s);
+      dim3((unsigned)(tiles * slices)), dim3(C_::kThreads), args, 0, s);
+  if (err != hipSuccess || slices == 1) return err;
+  return launch_combine(p, slices, partials, s);
 }
 
 #define GEMMF32_MFMA_S(BM, BN, BK, WM, WN, MW, SC, TAG)                                     \

@@ -219,49 +219,6 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4)
   }
 }
 
-// C[m][n] = sum over slices, in slice order, of part[slice][m][n].  A thread
-// owns four consecutive elements of the flattened M x N partial array (loaded
-// as one 16-byte chunk when M*N is a multiple of 4).
-__global__ void __launch_bounds__(256) skinny_combine_kernel(Problem p, int slices,
-                                                             const float* __restrict__ part) {
-  const int64_t mn = (int64_t)p.M * p.N;
-  const int64_t e0 = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
-  if (e0 >= mn) return;
-  const bool vec = (mn % 4) == 0;
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < slices; s0 += 4) {
-    float4 v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float* src = part + (size_t)(s0 + j) * mn + e0;
-      if (s0 + j >= slices) {
-        v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      } else if (vec) {
-        v[j] = *reinterpret_cast<const float4*>(src);
-      } else {
-        v[j].x = src[0];
-        v[j].y = e0 + 1 < mn ? src[1] : 0.f;
-        v[j].z = e0 + 2 < mn ? src[2] : 0.f;
-        v[j].w = e0 + 3 < mn ? src[3] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (s0 + j < slices) {
-        s[0] += v[j].x;
-        s[1] += v[j].y;
-        s[2] += v[j].z;
-        s[3] += v[j].w;
-      }
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t e = e0 + q;
-    if (e < mn) p.C[(e / p.N) * p.ldc + e % p.N] = s[q];
-  }
-}
-
 // Slices: enough workgroups for every CU (or `target` slices if given), each
 // slice at least one super-block.
 template <int CG>
@@ -292,11 +249,7 @@ hipError_t launch_tile(const Problem& p, const SkinnyPlan& pl, float* partials, 
       reinterpret_cast<const void*>(&skinny_tile_kernel<NW, CG, U, VA, VB>),
       dim3(pl.strips, pl.splits), dim3(NW * 64), args, 0, s);
   if (err != hipSuccess || pl.splits == 1) return err;
-  const int64_t mn = (int64_t)p.M * p.N;
-  const float* cpart = partials;
-  void* cargs[] = {&pp, &slices, &cpart};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&skinny_combine_kernel),
-                         dim3((unsigned)((mn + 1023) / 1024)), dim3(256), cargs, 0, s);
+  return launch_combine(p, slices, partials, s);
 }
 
 #define GEMMF32_SKINNY_TILE(NW, CG, U, S)                                                   \

@@ -27,7 +27,15 @@ constexpr TuningRow kTuningGfx950[] = {
     {16, 0, "skinny_w8_c4_u4_s0_vec"},
     {kAnyM, 768, "mfma_128x128x16_w64x64_s2_veca"},
     {kAnyM, 256, "mfma_128x64x16_w64x32_veca"},
-    {kAnyM, 0, "mfma_64x64x16_w32x32_veca"},
+    {kAnyM, 0, "mfma_64x64x16_w32x32_sk_veca"},
 };
+
+// K split of the "_sk_" MFMA entries: used only when the tile grid has fewer
+// than kSplitKBelowWorkgroups workgroups; then K is cut into slices of at
+// least kSplitKMinKTiles K-tiles so that tiles x slices reaches about
+// kSplitKTargetWorkgroups (four per CU).
+constexpr int64_t kSplitKBelowWorkgroups = 512;
+constexpr int64_t kSplitKTargetWorkgroups = 1024;
+constexpr int64_t kSplitKMinKTiles = 8;
 
 }  // namespace gemmf32

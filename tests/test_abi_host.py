@@ -105,7 +105,7 @@ def test_adjacent_but_not_overlapping_is_not_alias():
     (8, 3001, 1531, 1531, 3001, P16, Q16, "skinny_w8_c4"),
     (4096, 4096, 4096, 4096, 4096, P16, Q16, "mfma_128x128"),
     (2047, 3001, 1531, 1531, 3001, P16, Q16, "mfma_128x64"),
-    (512, 512, 512, 512, 512, P16, Q16, "mfma_64x64"),
+    (512, 512, 512, 512, 512, P16, Q16, "mfma_64x64x16_w32x32_sk"),
 ])
 def test_dispatcher_families(M, N, K, lda, ldb, A, B, expect):
     name = binding.gemm_f32_selected_kernel(M, N, K, lda, ldb, max(N, 1), A, B, R16)
@@ -142,3 +142,12 @@ def test_dispatcher_rejects_bad_arguments():
     sel = binding.gemm_f32_selected_kernel
     assert sel(-1, 4, 4, 4, 4, 4, P16, Q16, R16) == "invalid"
     assert sel(4, 4, 4, 3, 4, 4, P16, Q16, R16) == "invalid"
+
+
+def test_every_mfma_variant_has_a_split_k_twin():
+    names = binding.kernel_names()
+    whole = [n for n in names if n.startswith("mfma_") and "_sk_" not in n]
+    assert whole
+    for n in whole:
+        base, width = n.rsplit("_", 1)
+        assert f"{base}_sk_{width}" in names, n

@@ -77,6 +77,10 @@ def _kernel_case(name):
     vec_b = suffix in ("vec", "vecb")
     if name.startswith("skinny"):
         M, N, K = 13, 1000 + 3, 2050 + 7
+    elif "_sk_" in name:
+        # long enough for several K slices at BK = 16 and 32, the last one
+        # shorter and ending in a partial K-tile
+        M, N, K = 301, 263, 32 * 8 * 3 + 13
     elif name.startswith("mfma"):
         M, N, K = 301, 263, 139
     else:
@@ -110,6 +114,28 @@ def test_every_kernel_variant(gpu_lib, kname):
         else:
             H.assert_within_tol(C, C_ref, ABS, kname)
         H.check_outside_untouched(flat, M, N, ldc)
+
+
+@pytest.mark.parametrize("shape", [(33, 129, 2000), (512, 512, 512), (1, 64, 4096),
+                                   (200, 70, 1031), (1024, 1024, 1024)])
+def test_split_k_through_dispatcher(gpu_lib, shape):
+    """Grids too small to fill the GPU take the K-split MFMA path; its slice
+    partials are summed in a fixed order, so reruns are bitwise identical."""
+    M, N, K = shape
+    for integer in (True, False):
+        dist = "int2" if integer else "u11"
+        A, B = inputs.make_ab(M, N, K, dist, dist, 6100 + integer)
+        kname = gpu_lib.selected_kernel(A, B)
+        H.say(f"split-K {shape} int={integer} kernel={kname}")
+        C, flat, ldc = _run(gpu_lib, A, B, ldc=N + 3)
+        C_ref, ABS = H.oracle_of(A, B)
+        if integer:
+            H.assert_bitexact(C, C_ref, f"{shape} {kname}")
+        else:
+            H.assert_within_tol(C, C_ref, ABS, f"{shape} {kname}")
+        H.check_outside_untouched(flat, M, N, ldc)
+        C2, _, _ = _run(gpu_lib, A, B, ldc=N + 3)
+        assert np.array_equal(C, C2)
 
 
 EDGE_SIZES = [1, 2, 3, 31, 33, 64, 127, 129, 257]
