@@ -30,6 +30,8 @@
 //   accumulator register r of lane l: D[i = 8*(r/4) + 4*(l/32) + r%4][j = l % 32]
 #include "gemm_f32_internal.h"
 
+#include <type_traits>
+
 namespace gemmf32 {
 namespace {
 
@@ -82,7 +84,7 @@ struct Cfg {
   static_assert(BM % WM == 0 && BN % WN == 0, "wave tiles must divide the tile");
   static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
   static_assert(BN % 64 == 0, "the B swizzle needs 64-wide tile rows");
-  static_assert(BK == 8 || BK == 16 || BK == 32, "BK in {8, 16, 32}");
+  static_assert(BK == 8 || BK == 16 || BK == 32 || BK == 64, "BK in {8, 16, 32, 64}");
   static_assert((BM * BK / 4) % kThreads == 0 && (BK * BN / 4) % kThreads == 0,
                 "tile loads divide evenly over the threads");
   static constexpr int kLdsA = BM * BK;   // [m][k], k contiguous, 16-byte chunks swizzled
@@ -114,6 +116,8 @@ __device__ __forceinline__ int swz_b(int k) { return ((k >> 2) & 1) << 5; }
 //          second half.
 // SCHED 2: as 1, and the wave runs at raised priority while it issues memory
 //          instructions, lowered again for the MFMAs.
+// SCHED 3, 4, 5: software pipeline with fragments read one k group ahead
+//          and global loads two K-tiles ahead (described at the loop).
 template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB, int kMinWaves, int SCHED>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     __attribute__((amdgpu_waves_per_eu(kMinWaves)))
@@ -305,25 +309,198 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     }
   };
 
+  // Fragments of one 8-wide k group, held in registers one group ahead of
+  // the MFMAs that use them (SCHED >= 3).
+  struct Frag {
+    float4 a[C_::kFragM];
+    float b[4][C_::kFragN];
+  };
+  auto read_frag = [&](Frag& f, int buf, int q) {
+    const float* la = lds_a[buf];
+    const float* lb = lds_b[buf];
+#pragma unroll
+    for (int i = 0; i < C_::kFragM; ++i)
+      f.a[i] = *reinterpret_cast<const float4*>(&la[a_off[i][q]]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int j = 0; j < C_::kFragN; ++j) f.b[s][j] = lb[(8 * q + 4 * lk + s) * BN + b_off[j]];
+  };
+  // MFMA steps [s0, s1) of a group's fragments
+  auto mfma_frag = [&](const Frag& f, int s0, int s1) {
+#pragma unroll
+    for (int s = s0; s < s1; ++s)
+#pragma unroll
+      for (int i = 0; i < C_::kFragM; ++i) {
+        const float a = s == 0 ? f.a[i].x : s == 1 ? f.a[i].y : s == 2 ? f.a[i].z : f.a[i].w;
+#pragma unroll
+        for (int j = 0; j < C_::kFragN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, f.b[s][j], acc[i][j], 0, 0, 0);
+      }
+  };
+
+  // Single instructions of the pipelined loop, so that SCHED 5 can place each
+  // one between two MFMAs.  Op `idx` of a group's fragment reads: A block
+  // idx (one ds_read_b128), then for B block j the k rows s = 0, 1 and then
+  // s = 2, 3 (two b32 reads the compiler pairs into one instruction).
+  auto read_one = [&](Frag& f, int buf, int q, int idx) {
+    if (idx < C_::kFragM) {
+      f.a[idx] = *reinterpret_cast<const float4*>(&lds_a[buf][a_off[idx][q]]);
+    } else {
+      const int j = (idx - C_::kFragM) / 2, s0 = 2 * ((idx - C_::kFragM) % 2);
+      const float* lb = lds_b[buf];
+      f.b[s0][j] = lb[(8 * q + 4 * lk + s0) * BN + b_off[j]];
+      f.b[s0 + 1][j] = lb[(8 * q + 4 * lk + s0 + 1) * BN + b_off[j]];
+    }
+  };
+  // MFMA number idx of a group, in the order of mfma_frag
+  auto mfma_one = [&](const Frag& f, int idx) {
+    const int s = idx / (C_::kFragM * C_::kFragN);
+    const int i = (idx / C_::kFragN) % C_::kFragM, j = idx % C_::kFragN;
+    const float a = s == 0 ? f.a[i].x : s == 1 ? f.a[i].y : s == 2 ? f.a[i].z : f.a[i].w;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, f.b[s][j], acc[i][j], 0, 0, 0);
+  };
+  // global load number idx of a whole interior K-tile (A chunks, then B)
+  auto load_one_full = [&](int k0, int idx) {
+    if (idx < C_::kVecA) {
+      const float* src = a_ptr[idx] + k0;
+      ra[idx] = VA ? load4(src) : make_float4(src[0], src[1], src[2], src[3]);
+    } else {
+      const int v = idx - C_::kVecA;
+      const float* src = b_ptr[v] + (int64_t)k0 * p.ldb;
+      rb[v] = VB ? load4(src) : make_float4(src[0], src[1], src[2], src[3]);
+    }
+  };
+  // LDS write number idx of store_tiles
+  auto store_one = [&](int buf, int idx) {
+    if (idx < C_::kVecA) {
+      const int e = tid + idx * C_::kThreads;
+      const int row = e / C_::kChunksA, c = e % C_::kChunksA;
+      *reinterpret_cast<float4*>(&lds_a[buf][row * BK + 4 * (c ^ swz_a<C_::kChunksA>(row))]) =
+          ra[idx];
+    } else {
+      const int v = idx - C_::kVecA;
+      const int e = tid + v * C_::kThreads;
+      const int krow = e / C_::kChunksB, nc = (e % C_::kChunksB) * 4;
+      *reinterpret_cast<float4*>(&lds_b[buf][krow * BN + (nc ^ swz_b(krow))]) = rb[v];
+    }
+  };
+
   // ---- K loop: double-buffered LDS, one barrier per K-tile ---------------
   const int ktiles = (K + BK - 1) / BK;
   constexpr int kGroups = BK / 8;
-  constexpr int kHalf = SCHED == 0 ? kGroups : (kGroups + 1) / 2;
-  load_tiles(0);
-  store_tiles(0);
-  __syncthreads();
-  for (int t = 0; t < ktiles; ++t) {
-    const int cur = t & 1;
-    const bool more = t + 1 < ktiles;
-    if (SCHED == 2) __builtin_amdgcn_s_setprio(1);
-    if (more) load_tiles((t + 1) * BK);
-    if (SCHED == 2) __builtin_amdgcn_s_setprio(0);
-    compute(cur, 0, kHalf);
-    if (SCHED == 2) __builtin_amdgcn_s_setprio(1);
-    if (more) store_tiles(cur ^ 1);
-    if (SCHED == 2) __builtin_amdgcn_s_setprio(0);
-    compute(cur, kHalf, kGroups);
+  if constexpr (SCHED < 3) {
+    constexpr int kHalf = SCHED == 0 ? kGroups : (kGroups + 1) / 2;
+    load_tiles(0);
+    store_tiles(0);
     __syncthreads();
+    for (int t = 0; t < ktiles; ++t) {
+      const int cur = t & 1;
+      const bool more = t + 1 < ktiles;
+      if (SCHED == 2) __builtin_amdgcn_s_setprio(1);
+      if (more) load_tiles((t + 1) * BK);
+      if (SCHED == 2) __builtin_amdgcn_s_setprio(0);
+      compute(cur, 0, kHalf);
+      if (SCHED == 2) __builtin_amdgcn_s_setprio(1);
+      if (more) store_tiles(cur ^ 1);
+      if (SCHED == 2) __builtin_amdgcn_s_setprio(0);
+      compute(cur, kHalf, kGroups);
+      __syncthreads();
+    }
+  } else {
+    // Software pipeline: the fragments of group q + 1 are read while the
+    // MFMAs of group q run; the global loads of tile t + 2 are issued right
+    // after the barrier that ends tile t's LDS reads, and written to LDS
+    // during tile t + 1 (SCHED 3, 5: with the reads of its last group;
+    // SCHED 4: in the middle of the last group's MFMAs, just before the
+    // barrier).  sched_barrier keeps the compiler from moving MFMAs across
+    // the phases.
+    // SCHED 5 runs the K-tiles whose loads are all whole interior tiles in a
+    // loop without branches, where the LDS reads, LDS writes and global loads
+    // are issued one or two after each MFMA instead of in bursts.
+    static_assert(kGroups % 2 == 0, "fragment ping-pong needs an even group count");
+    constexpr int kStoreQ = SCHED == 4 ? kGroups - 1 : kGroups - 2;
+    constexpr int kMfmaPerGroup = 4 * C_::kFragM * C_::kFragN;
+    constexpr int kReadsPerGroup = C_::kFragM + 2 * C_::kFragN;   // b128 A, paired b32 B
+    constexpr int kTileLoads = C_::kVecA + C_::kVecB;
+    Frag f0, f1;
+    load_tiles(0);
+    store_tiles(0);
+    __syncthreads();
+    read_frag(f0, 0, 0);
+    if (ktiles > 1) load_tiles(BK);
+    auto step = [&](int t, auto fast_tag) {
+      constexpr bool kFast = decltype(fast_tag)::value;
+      const int cur = t & 1;
+      const bool more = kFast || t + 1 < ktiles;
+#pragma unroll
+      for (int q = 0; q < kGroups; ++q) {
+        Frag& fc = (q & 1) ? f1 : f0;
+        Frag& fn = (q & 1) ? f0 : f1;
+        if constexpr (kFast) {
+          // one LDS read / LDS write / global load after each MFMA
+          constexpr int kHalf = kMfmaPerGroup / 2;
+          if (q < kGroups - 1) {
+            constexpr int kWritesPer = (kTileLoads + kMfmaPerGroup - 1) / kMfmaPerGroup;
+#pragma unroll
+            for (int i = 0; i < kMfmaPerGroup; ++i) {
+              mfma_one(fc, i);
+              if (i < kReadsPerGroup) read_one(fn, cur, q + 1, i);
+              if (q == kStoreQ) {
+#pragma unroll
+                for (int w = 0; w < kWritesPer; ++w)
+                  if (i * kWritesPer + w < kTileLoads) store_one(cur ^ 1, i * kWritesPer + w);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < kHalf; ++i) mfma_one(fc, i);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q == kStoreQ) store_tiles(cur ^ 1);
+            __syncthreads();
+            constexpr int kLoadsPer = (kTileLoads + kHalf - 1) / kHalf;
+            constexpr int kReadsPer = (kReadsPerGroup + kHalf - 1) / kHalf;
+#pragma unroll
+            for (int i = 0; i < kHalf; ++i) {
+              mfma_one(fc, kHalf + i);
+#pragma unroll
+              for (int r = 0; r < kReadsPer; ++r)
+                if (i * kReadsPer + r < kReadsPerGroup) read_one(fn, cur ^ 1, 0, i * kReadsPer + r);
+#pragma unroll
+              for (int l = 0; l < kLoadsPer; ++l)
+                if (i * kLoadsPer + l < kTileLoads) load_one_full((t + 2) * BK, i * kLoadsPer + l);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        } else if (q < kGroups - 1) {
+          read_frag(fn, cur, q + 1);
+          if (q == kStoreQ && more) store_tiles(cur ^ 1);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_frag(fc, 0, 4);
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          mfma_frag(fc, 0, 2);
+          __builtin_amdgcn_sched_barrier(0);
+          if (q == kStoreQ && more) store_tiles(cur ^ 1);
+          __syncthreads();
+          if (more) {
+            read_frag(fn, cur ^ 1, 0);
+            if (t + 2 < ktiles) load_tiles((t + 2) * BK);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_frag(fc, 2, 4);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    int t = 0;
+    if (SCHED == 5 && full_mn) {
+      // whole interior K-tiles up to t + 2: no masks, no branches
+      const int kfull = K / BK;
+      for (; t + 2 < kfull; ++t) step(t, std::true_type{});
+    }
+    for (; t < ktiles; ++t) step(t, std::false_type{});
   }
 
   // ---- masked epilogue ----------------------------------------------------
@@ -395,6 +572,28 @@ const MfmaVariant kVariants[] = {
     GEMMF32_MFMA_S(256, 256, 32, 128, 128, 1, 1, "_s1"),
     GEMMF32_MFMA_S(256, 128, 16, 128, 64, 2, 1, "_s1"),
     GEMMF32_MFMA_S(128, 256, 16, 64, 128, 2, 1, "_s1"),
+    GEMMF32_MFMA_S(128, 128, 16, 64, 64, 3, 3, "_p3"),
+    GEMMF32_MFMA_S(128, 128, 16, 64, 64, 3, 4, "_p4"),
+    GEMMF32_MFMA_S(128, 128, 32, 64, 64, 2, 3, "_p3"),
+    GEMMF32_MFMA_S(128, 128, 32, 64, 64, 2, 4, "_p4"),
+    GEMMF32_MFMA_S(256, 128, 16, 128, 64, 2, 3, "_p3"),
+    GEMMF32_MFMA_S(256, 128, 32, 128, 64, 1, 3, "_p3"),
+    GEMMF32_MFMA_S(128, 64, 16, 64, 32, 4, 3, "_p3"),
+    GEMMF32_MFMA_S(128, 64, 32, 64, 32, 4, 3, "_p3"),
+    GEMMF32_MFMA_S(64, 64, 16, 32, 32, 4, 3, "_p3"),
+    GEMMF32_MFMA_S(64, 64, 32, 32, 32, 4, 3, "_p3"),
+    GEMMF32_MFMA_S(128, 128, 64, 64, 64, 1, 3, "_p3"),
+    GEMMF32_MFMA_S(128, 64, 64, 64, 32, 1, 3, "_p3"),
+    GEMMF32_MFMA_S(64, 64, 64, 32, 32, 2, 3, "_p3"),
+    GEMMF32_MFMA_S(128, 128, 64, 64, 64, 1, 5, "_p5"),
+    GEMMF32_MFMA_S(128, 128, 32, 64, 64, 2, 5, "_p5"),
+    GEMMF32_MFMA_S(128, 128, 16, 64, 64, 3, 5, "_p5"),
+    GEMMF32_MFMA_S(256, 128, 16, 128, 64, 2, 5, "_p5"),
+    GEMMF32_MFMA_S(256, 128, 32, 128, 64, 1, 5, "_p5"),
+    GEMMF32_MFMA_S(128, 64, 32, 64, 32, 4, 5, "_p5"),
+    GEMMF32_MFMA_S(128, 64, 64, 64, 32, 1, 5, "_p5"),
+    GEMMF32_MFMA_S(64, 64, 64, 32, 32, 2, 5, "_p5"),
+    GEMMF32_MFMA_S(64, 64, 32, 32, 32, 4, 5, "_p5"),
 };
 
 }  // namespace

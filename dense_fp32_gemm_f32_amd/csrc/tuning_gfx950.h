@@ -25,8 +25,9 @@ constexpr int64_t kAnyM = INT64_C(0x7fffffff);
 
 constexpr TuningRow kTuningGfx950[] = {
     {16, 0, "skinny_w8_c4_u4_s0_vec"},
-    {kAnyM, 768, "mfma_128x128x16_w64x64_s2_veca"},
-    {kAnyM, 256, "mfma_128x64x16_w64x32_veca"},
+    {kAnyM, 768, "mfma_256x128x16_w128x64_p5_vec"},
+    {kAnyM, 192, "mfma_128x64x32_w64x32_p5_vec"},
+    {kAnyM, 48, "mfma_64x64x32_w32x32_p5_vec"},
     {kAnyM, 0, "mfma_64x64x16_w32x32_sk_veca"},
 };
 

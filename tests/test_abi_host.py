@@ -103,9 +103,10 @@ def test_adjacent_but_not_overlapping_is_not_alias():
     (3, 8192, 8192, 8192, 8192, P16, Q16, "skinny_w8_c4"),
     (16, 4096, 4096, 4096, 4096, P16, Q16, "skinny_w8_c4"),
     (8, 3001, 1531, 1531, 3001, P16, Q16, "skinny_w8_c4"),
-    (4096, 4096, 4096, 4096, 4096, P16, Q16, "mfma_128x128"),
+    (4096, 4096, 4096, 4096, 4096, P16, Q16, "mfma_256x128"),
     (2047, 3001, 1531, 1531, 3001, P16, Q16, "mfma_128x64"),
     (512, 512, 512, 512, 512, P16, Q16, "mfma_64x64x16_w32x32_sk"),
+    (1024, 1024, 1024, 1024, 1024, P16, Q16, "mfma_64x64x32"),
 ])
 def test_dispatcher_families(M, N, K, lda, ldb, A, B, expect):
     name = binding.gemm_f32_selected_kernel(M, N, K, lda, ldb, max(N, 1), A, B, R16)
