@@ -216,17 +216,23 @@ bool log_enabled() {
   return on;
 }
 
-// Can entry e run these arguments?
-bool entry_accepts(const Entry& e, const Problem& p) {
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Can entry e run these arguments?  (128-bit loads through registers need only
+// the 4-byte alignment checked up front; direct-to-LDS loads need more.)
+bool accepts(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+             const void* A, const void* B) {
   if (e.kind == Kind::Mfma || e.kind == Kind::MfmaSplitK) {
-    // 128-bit loads need only the 4-byte alignment checked up front
-    return true;
+    const auto& v = gemmf32::mfma_variant(e.sub);
+    if (!v.lds_dma) return true;
+    return K % v.bk == 0 && lda % 4 == 0 && ldb % 4 == 0 && N % 4 == 0 && aligned16(A) &&
+           aligned16(B);
   }
-  if (e.kind == Kind::Skinny) {
-    const auto& v = gemmf32::skinny_variant(e.sub);
-    return p.M <= v.mr;
-  }
+  if (e.kind == Kind::Skinny) return M <= gemmf32::skinny_variant(e.sub).mr;
   return true;
+}
+bool entry_accepts(const Entry& e, const Problem& p) {
+  return accepts(e, p.M, p.N, p.K, p.lda, p.ldb, p.A, p.B);
 }
 
 int run_entry(const Entry& e, const Problem& p, int dev, hipStream_t s) {
@@ -275,21 +281,12 @@ std::string select_name(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ld
                         const void* A, const void* B) {
   if (M == 0 || N == 0) return "empty";
   if (K == 0) return "fill_zero_k0";
-  // 128-bit loads need only 4-byte aligned rows, which every accepted call has
-  const bool va = aligned4(A), vb = aligned4(B);
-  (void)lda;
-  (void)ldb;
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   for (const auto& row : gemmf32::kTuningGfx950) {
     if (M > row.max_m || tiles < row.min_tiles) continue;
-    std::string name = row.kernel;
-    const size_t cut = name.rfind('_');
-    const std::string base = name.substr(0, cut), width = name.substr(cut + 1);
-    // keep only the 128-bit loads the operands allow
-    const bool want_a = width == "vec" || width == "veca";
-    const bool want_b = width == "vec" || width == "vecb";
-    const bool a = want_a && va, b = want_b && vb;
-    return base + (a && b ? "_vec" : a ? "_veca" : b ? "_vecb" : "_scalar");
+    // a row whose kernel cannot take these arguments defers to the next one
+    const int idx = find_entry(row.kernel);
+    if (idx >= 0 && accepts(entries()[idx], M, N, K, lda, ldb, A, B)) return row.kernel;
   }
   return "ref_naive";
 }

@@ -28,10 +28,15 @@ struct MfmaVariant {
   int bm, bn, bk;      // workgroup tile
   int wm, wn;          // wave tile
   bool vec_a, vec_b;   // 128-bit global loads of A / B (any pitch, 4-byte aligned)
+  // Direct global -> LDS loads.  These need A and B 16-byte aligned, lda, ldb
+  // and N multiples of 4 and K a multiple of bk.
+  bool lds_dma;
   hipError_t (*launch)(const Problem&, int slices, int kchunk, float* partials, hipStream_t);
 };
-int mfma_variant_count();
+int mfma_variant_count();          // both kinds below
 const MfmaVariant& mfma_variant(int i);
+int mfma_dma_variant_count();      // the direct-to-LDS kernels
+const MfmaVariant& mfma_dma_variant(int i);
 
 // ---- skinny-M kernel (column tiles x K slices, then a combine) ------------
 struct SkinnyPlan {

@@ -28,87 +28,15 @@
 //   A operand, lane l: A[i = l % 32][k = l / 32]
 //   B operand, lane l: B[k = l / 32][j = l % 32]
 //   accumulator register r of lane l: D[i = 8*(r/4) + 4*(l/32) + r%4][j = l % 32]
-#include "gemm_f32_internal.h"
-
 #include <type_traits>
+
+#include "gemm_f32_internal.h"
+#include "mfma_common.h"
 
 namespace gemmf32 {
 namespace {
 
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-
-// 16 bytes from a float address that is only 4-byte aligned.  Multi-dword
-// global loads on gfx950 need dword alignment only, and the compiler emits one
-// global_load_dwordx4 for this copy, so rows with any pitch load at 128 bits.
-__device__ __forceinline__ float4 load4(const float* p) {
-  float4 v;
-  __builtin_memcpy(&v, p, sizeof(v));
-  return v;
-}
-
-constexpr int kNumXcd = 8;   // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int kGroupM = 8;   // tile rows per raster group
-
-// Workgroups are dealt to the XCDs round-robin by id.  Renumber so that each
-// XCD owns one contiguous range of tile ids; neighbouring tiles then share
-// that XCD's L2.  A bijection on [0, n) for any n.
-__device__ __forceinline__ int xcd_contiguous_id(int bid, int n) {
-  const int q = n / kNumXcd, r = n % kNumXcd;
-  const int x = bid % kNumXcd, idx = bid / kNumXcd;
-  return x * q + min(x, r) + idx;
-}
-
-// Grouped raster: kGroupM tile rows are swept together along N.
-__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n,
-                                            int& tm, int& tn) {
-  const int per_group = kGroupM * tiles_n;
-  const int g = t / per_group;
-  const int first_m = g * kGroupM;
-  const int gm = min(tiles_m - first_m, kGroupM);
-  const int r = t - g * per_group;
-  tm = first_m + r % gm;
-  tn = r / gm;
-}
-
-template <int BM, int BN, int BK, int WM, int WN>
-struct Cfg {
-  static constexpr int kWavesM = BM / WM;
-  static constexpr int kWavesN = BN / WN;
-  static constexpr int kThreads = kWavesM * kWavesN * 64;
-  static constexpr int kFragM = WM / 32;
-  static constexpr int kFragN = WN / 32;
-  static constexpr int kChunksA = BK / 4;   // float4 chunks per A-tile row
-  static constexpr int kChunksB = BN / 4;   // float4 chunks per B-tile row
-  static constexpr int kVecA = BM * BK / 4 / kThreads;
-  static constexpr int kVecB = BK * BN / 4 / kThreads;
-  static_assert(BM % WM == 0 && BN % WN == 0, "wave tiles must divide the tile");
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "32x32 MFMA blocks");
-  static_assert(BN % 64 == 0, "the B swizzle needs 64-wide tile rows");
-  static_assert(BK == 8 || BK == 16 || BK == 32 || BK == 64, "BK in {8, 16, 32, 64}");
-  static_assert((BM * BK / 4) % kThreads == 0 && (BK * BN / 4) % kThreads == 0,
-                "tile loads divide evenly over the threads");
-  static constexpr int kLdsA = BM * BK;   // [m][k], k contiguous, 16-byte chunks swizzled
-  static constexpr int kLdsB = BK * BN;   // [k][n], n contiguous, swizzled
-};
-
-// A tile in LDS: row m holds BK floats as kChunks 16-byte chunks; logical
-// chunk c of row m sits at chunk c ^ swz_a(m).  Sixteen consecutive rows with
-// the same logical chunk then cover all 64 banks, so both the 128-bit
-// fragment reads (one row per lane) and the 128-bit tile writes are free of
-// bank conflicts.
-template <int kChunks>
-__device__ __forceinline__ int swz_a(int m) {
-  return (m / (16 / kChunks)) % kChunks;
-}
-// B tile in LDS: n of row k is XORed with 32 when bit 2 of k is set, so the
-// rows k and k + 4 read together by one fragment land in opposite bank halves.
-__device__ __forceinline__ int swz_b(int k) { return ((k >> 2) & 1) << 5; }
-
-// MFMA k-slot assignment.  One ds_read_b128 gives lane l four consecutive k
-// of its A row: k = 8q + 4*(l/32) + s for s = 0..3.  MFMA step s therefore
-// multiplies, in k-slot h = l/32, the term k = 8q + 4h + s; the B fragment of
-// step s supplies B[8q + 4h + s][n] in the same slot.  Each k of the 8-wide
-// group is used exactly once, so the sum is the same dot product.
+using namespace mfma;
 
 // SCHED 0: the next K-tile is written to LDS after all MFMAs of this one.
 // SCHED 1: it is written after the first half of them, so the write, the
@@ -360,15 +288,29 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     const float a = s == 0 ? f.a[i].x : s == 1 ? f.a[i].y : s == 2 ? f.a[i].z : f.a[i].w;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, f.b[s][j], acc[i][j], 0, 0, 0);
   };
-  // global load number idx of a whole interior K-tile (A chunks, then B)
-  auto load_one_full = [&](int k0, int idx) {
+  // Global load number idx (A chunks, then B) of a K-tile that lies inside
+  // K, for any output tile.  Rows of A past M and columns of B past N are
+  // read at the clamped addresses set up above and left unmasked: they only
+  // reach rows or columns of C that the epilogue does not store.  NPART: this
+  // tile has a B chunk that straddles column N (N % 4 != 0); its B chunks are
+  // then read element by element with each column clamped to N - 1, so no
+  // read passes the end of a row.
+  auto load_one_any = [&](int k0, int idx, auto npart_tag) {
+    constexpr bool kNPart = decltype(npart_tag)::value;
     if (idx < C_::kVecA) {
       const float* src = a_ptr[idx] + k0;
       ra[idx] = VA ? load4(src) : make_float4(src[0], src[1], src[2], src[3]);
     } else {
       const int v = idx - C_::kVecA;
       const float* src = b_ptr[v] + (int64_t)k0 * p.ldb;
-      rb[v] = VB ? load4(src) : make_float4(src[0], src[1], src[2], src[3]);
+      if constexpr (kNPart) {
+        const float* row = src - (b_ncol[v] < N ? b_ncol[v] : 0);
+        const int c = b_ncol[v];
+        rb[v] = make_float4(row[min(c, N - 1)], row[min(c + 1, N - 1)], row[min(c + 2, N - 1)],
+                            row[min(c + 3, N - 1)]);
+      } else {
+        rb[v] = VB ? load4(src) : make_float4(src[0], src[1], src[2], src[3]);
+      }
     }
   };
   // LDS write number idx of store_tiles
@@ -415,8 +357,8 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     // SCHED 4: in the middle of the last group's MFMAs, just before the
     // barrier).  sched_barrier keeps the compiler from moving MFMAs across
     // the phases.
-    // SCHED 5 runs the K-tiles whose loads are all whole interior tiles in a
-    // loop without branches, where the LDS reads, LDS writes and global loads
+    // SCHED 5 runs the K-tiles whose loads all lie inside K in a loop without
+    // branches (for edge tiles too, see load_one_any), where the LDS reads, LDS writes and global loads
     // are issued one or two after each MFMA instead of in bursts.
     static_assert(kGroups % 2 == 0, "fragment ping-pong needs an even group count");
     constexpr int kStoreQ = SCHED == 4 ? kGroups - 1 : kGroups - 2;
@@ -429,7 +371,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     __syncthreads();
     read_frag(f0, 0, 0);
     if (ktiles > 1) load_tiles(BK);
-    auto step = [&](int t, auto fast_tag) {
+    auto step = [&](int t, auto fast_tag, auto npart_tag) {
       constexpr bool kFast = decltype(fast_tag)::value;
       const int cur = t & 1;
       const bool more = kFast || t + 1 < ktiles;
@@ -469,7 +411,8 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
                 if (i * kReadsPer + r < kReadsPerGroup) read_one(fn, cur ^ 1, 0, i * kReadsPer + r);
 #pragma unroll
               for (int l = 0; l < kLoadsPer; ++l)
-                if (i * kLoadsPer + l < kTileLoads) load_one_full((t + 2) * BK, i * kLoadsPer + l);
+                if (i * kLoadsPer + l < kTileLoads)
+                  load_one_any((t + 2) * BK, i * kLoadsPer + l, npart_tag);
               __builtin_amdgcn_sched_barrier(0);
             }
           }
@@ -495,12 +438,16 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
       }
     };
     int t = 0;
-    if (SCHED == 5 && full_mn) {
-      // whole interior K-tiles up to t + 2: no masks, no branches
+    if (SCHED == 5) {
+      // K-tiles up to t + 2 inside K: no masks, no branches
       const int kfull = K / BK;
-      for (; t + 2 < kfull; ++t) step(t, std::true_type{});
+      if (n0 + BN > N && N % 4 != 0) {
+        for (; t + 2 < kfull; ++t) step(t, std::true_type{}, std::true_type{});
+      } else {
+        for (; t + 2 < kfull; ++t) step(t, std::true_type{}, std::false_type{});
+      }
     }
-    for (; t < ktiles; ++t) step(t, std::false_type{});
+    for (; t < ktiles; ++t) step(t, std::false_type{}, std::false_type{});
   }
 
   // ---- masked epilogue ----------------------------------------------------
@@ -546,15 +493,15 @@ hipError_t launch(const Problem& p, int slices, int kchunk, float* partials, hip
   return launch_combine(p, slices, partials, s);
 }
 
-#define GEMMF32_MFMA_S(BM, BN, BK, WM, WN, MW, SC, TAG)                                     \
-  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_vec", BM, BN, BK, WM, WN, true, true,   \
-   &launch<BM, BN, BK, WM, WN, true, true, MW, SC>},                                         \
-  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_veca", BM, BN, BK, WM, WN, true, false, \
-   &launch<BM, BN, BK, WM, WN, true, false, MW, SC>},                                        \
-  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_vecb", BM, BN, BK, WM, WN, false, true, \
-   &launch<BM, BN, BK, WM, WN, false, true, MW, SC>},                                        \
-  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_scalar", BM, BN, BK, WM, WN, false,    \
-   false, &launch<BM, BN, BK, WM, WN, false, false, MW, SC>}
+#define GEMMF32_MFMA_S(BM, BN, BK, WM, WN, MW, SC, TAG)                                      \
+  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_vec", BM, BN, BK, WM, WN, true, true,    \
+   false, &launch<BM, BN, BK, WM, WN, true, true, MW, SC>},                                    \
+  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_veca", BM, BN, BK, WM, WN, true, false,  \
+   false, &launch<BM, BN, BK, WM, WN, true, false, MW, SC>},                                   \
+  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_vecb", BM, BN, BK, WM, WN, false, true,  \
+   false, &launch<BM, BN, BK, WM, WN, false, true, MW, SC>},                                   \
+  {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_scalar", BM, BN, BK, WM, WN, false,     \
+   false, false, &launch<BM, BN, BK, WM, WN, false, false, MW, SC>}
 #define GEMMF32_MFMA(BM, BN, BK, WM, WN, MW) GEMMF32_MFMA_S(BM, BN, BK, WM, WN, MW, 0, "")
 
 const MfmaVariant kVariants[] = {
@@ -598,7 +545,12 @@ const MfmaVariant kVariants[] = {
 
 }  // namespace
 
-int mfma_variant_count() { return (int)(sizeof(kVariants) / sizeof(kVariants[0])); }
-const MfmaVariant& mfma_variant(int i) { return kVariants[i]; }
+int mfma_variant_count() {
+  return (int)(sizeof(kVariants) / sizeof(kVariants[0])) + mfma_dma_variant_count();
+}
+const MfmaVariant& mfma_variant(int i) {
+  const int n = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
+  return i < n ? kVariants[i] : mfma_dma_variant(i - n);
+}
 
 }  // namespace gemmf32

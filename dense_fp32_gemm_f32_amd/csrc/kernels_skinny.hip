@@ -162,7 +162,7 @@ __device__ __forceinline__ void stream_tile(const Problem& p, int lane, int n0, 
 // LDS in row-group order and the result goes to C (one slice) or to the
 // slice's partial sums.
 template <int NW, int CG, int U, bool VA, bool VB>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 16 ? 4 : 2)))
     skinny_tile_kernel(Problem p, int sb_per_slice, int slices, float* __restrict__ part) {
   constexpr int NRG = NW / CG;
   static_assert(NW % CG == 0, "whole row groups");
@@ -275,6 +275,11 @@ const SkinnyVariant kVariants[] = {
     GEMMF32_SKINNY_TILE(8, 2, 4, 0),
     GEMMF32_SKINNY_TILE(4, 4, 4, 0),
     GEMMF32_SKINNY_TILE(16, 8, 4, 0),
+    GEMMF32_SKINNY_TILE(8, 4, 8, 0),     // 8 super-blocks in flight per wave
+    GEMMF32_SKINNY_TILE(8, 4, 6, 0),
+    GEMMF32_SKINNY_TILE(8, 8, 8, 0),
+    GEMMF32_SKINNY_TILE(8, 4, 4, 8),     // 8 K slices: two workgroups per CU
+    GEMMF32_SKINNY_TILE(8, 4, 8, 8),
 };
 
 }  // namespace

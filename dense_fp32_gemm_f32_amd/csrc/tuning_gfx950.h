@@ -1,14 +1,16 @@
 // Tuning table for gfx950 (MI355X): which kernel gemm_f32 runs for a shape.
 //
-// The first row whose bounds hold wins.  A row names the kernel measured
-// fastest for 16-byte aligned operands; when the operands do not allow its
-// 128-bit loads the dispatcher falls back to the variant that they do allow
-// ("_vec" -> "_veca" / "_vecb" -> "_scalar").
+// The first row whose bounds hold and whose kernel can take the arguments
+// wins.  Rows come in pairs: the kernel with direct-to-LDS loads (needs
+// 16-byte aligned A and B, lda, ldb and N multiples of 4 and K a multiple of
+// its K-tile), then the register-staged kernel that takes any 4-byte aligned
+// operands.  The choices are the fastest measured per shape class with
+// dense_fp32_gemm_f32_amd/tune.py.
 //
 // Columns:
 //   max_m       the row applies when M <= max_m
 //   min_tiles   ... and the grid of 128 x 128 tiles has at least this many tiles
-//   kernel      kernel family (a name prefix in the kernel table)
+//   kernel      a name in the kernel table
 #pragma once
 
 #include <cstdint>
@@ -25,9 +27,13 @@ constexpr int64_t kAnyM = INT64_C(0x7fffffff);
 
 constexpr TuningRow kTuningGfx950[] = {
     {16, 0, "skinny_w8_c4_u4_s0_vec"},
+    {kAnyM, 768, "mfma_128x256x16_w64x128_d6_vec"},
     {kAnyM, 768, "mfma_256x128x16_w128x64_p5_vec"},
-    {kAnyM, 192, "mfma_128x64x32_w64x32_p5_vec"},
+    {kAnyM, 192, "mfma_128x128x16_w64x64_d6_vec"},
+    {kAnyM, 192, "mfma_64x64x32_w32x32_p5_vec"},
+    {kAnyM, 48, "mfma_64x64x32_w32x32_d6_vec"},
     {kAnyM, 48, "mfma_64x64x32_w32x32_p5_vec"},
+    {kAnyM, 0, "mfma_64x64x32_w32x32_d6_sk_vec"},
     {kAnyM, 0, "mfma_64x64x16_w32x32_sk_veca"},
 };
 

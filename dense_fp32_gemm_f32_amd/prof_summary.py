@@ -84,6 +84,8 @@ def main(argv=None):
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--algo-bytes", type=float, required=True)
     ap.add_argument("--flops", type=float, required=True)
+    ap.add_argument("--mfma-cycles", type=int, default=0,
+                    help="cycles one MFMA of the kernel occupies the pipe (32x32x2 f32: 64)")
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--out", required=True)
     args = ap.parse_args(argv)
@@ -131,11 +133,25 @@ def main(argv=None):
         lines += ["## Core counters (first matched kernel, mean per dispatch)", "",
                   "| counter | value |", "|---|---|"]
         lines += [f"| {k} | {v:.6g} |" for k, v in sorted(c.items())]
-        if "GRBM_GUI_ACTIVE" in c and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        if "GRBM_GUI_ACTIVE" in c:
             xcd_cycles = c["GRBM_GUI_ACTIVE"] / 8.0     # summed over the 8 XCDs
-            util = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * 1024.0)
-            lines += ["", f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/8 x 1024 SIMDs) "
-                          f"= {100 * util:.1f}%"]
+            lines.append("")
+            dur = durations(Path(args.trace))
+            if n in dur:
+                lines.append(f"Clock while the kernel runs = GRBM_GUI_ACTIVE/8 / average duration "
+                             f"= {xcd_cycles / dur[n][1]:.3f} GHz")
+            busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+            if busy is not None and busy < 2.0 ** 31 * 0.999:
+                util = busy / (xcd_cycles * 1024.0)
+                lines.append(f"MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/8 x 1024 SIMDs) "
+                             f"= {100 * util:.1f}%")
+            elif busy is not None:
+                lines.append("SQ_VALU_MFMA_BUSY_CYCLES reads 2^31 (the counter saturates on launches "
+                             "this long); see the issue-based figure instead.")
+            if "SQ_INSTS_MFMA" in c and args.mfma_cycles:
+                util = c["SQ_INSTS_MFMA"] * args.mfma_cycles / (xcd_cycles * 1024.0)
+                lines.append(f"MFMA pipe occupancy from issue = SQ_INSTS_MFMA x {args.mfma_cycles} "
+                             f"cycles / (GRBM_GUI_ACTIVE/8 x 1024 SIMDs) = {100 * util:.1f}%")
         if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_LDS_IDX_ACTIVE"):
             lines += [f"LDS bank-conflict cycles / LDS active cycles = "
                       f"{c['SQ_LDS_BANK_CONFLICT'] / c['SQ_LDS_IDX_ACTIVE']:.3f}"]

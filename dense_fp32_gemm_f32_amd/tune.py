@@ -6,15 +6,17 @@ tuning table in ``csrc/tuning_gfx950.h`` is chosen from).
 
 A shape is MxNxK (row-major, packed pitches, 16-byte aligned bases).  Each
 kernel that accepts the shape runs ``--warmup`` times, then ``--reps`` times
-with a HIP event pair on the launch stream around each call.  Inputs rotate
-over enough copies to exceed the 256 MB last-level cache when B is large, so
-bandwidth-bound shapes stream from HBM.  Prints one line per (shape, kernel).
+with a HIP event pair on the launch stream around each call, the candidates
+taking turns (after --spin-ms of load to settle the clocks); the median is
+reported.  Inputs rotate over enough copies to exceed the 256 MB last-level
+cache when B is large, so bandwidth-bound shapes stream from HBM.  Prints one line per (shape, kernel).
 """
 from __future__ import annotations
 
 import argparse
 import json
 import sys
+import time
 
 
 def parse_shape(s: str):
@@ -28,6 +30,8 @@ def main(argv=None):
     ap.add_argument("--filter", default="", help="comma-separated kernel-name prefixes")
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--spin-ms", type=float, default=300.0,
+                    help="keep the GPU busy this long before timing a shape")
     ap.add_argument("--json", default="")
     ap.add_argument("--with-torch", action="store_true",
                     help="also time torch.matmul in fp32 (vendor library, context only)")
@@ -59,6 +63,7 @@ def main(argv=None):
                  if not prefixes or any(n.startswith(p) for p in prefixes)]
         if args.with_torch:
             cands.append((-1, "torch.matmul"))
+        calls = []
         for idx, name in cands:
             if idx >= 0:
                 s = stream.cuda_stream
@@ -75,26 +80,46 @@ def main(argv=None):
                 def call(i):
                     torch.matmul(As[i % copies], Bs[i % copies], out=Cs[i % copies])
                     return 0
+            calls.append((name, call))
+        if not calls:
+            continue
+        # settle the clocks: keep the GPU busy for --spin-ms before timing
+        torch.cuda.synchronize()
+        t_end = time.perf_counter() + args.spin_ms * 1e-3
+        i = 0
+        while time.perf_counter() < t_end:
+            for _, call in calls:
+                call(i)
+            i += 1
+            torch.cuda.synchronize()
+        for _, call in calls:
             for i in range(args.warmup):
                 call(i)
-            torch.cuda.synchronize()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.reps)]
-            for i in range(args.reps):
-                evs[i][0].record(stream)
-                call(i)
-                evs[i][1].record(stream)
-            torch.cuda.synchronize()
-            ms = [a.elapsed_time(b) for a, b in evs]
+        torch.cuda.synchronize()
+        # round-robin over the candidates so that clock drift hits all alike
+        evs = {name: [] for name, _ in calls}
+        for r in range(args.reps):
+            for name, call in calls:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                call(r)
+                b.record(stream)
+                evs[name].append((a, b))
+        torch.cuda.synchronize()
+        for name, _ in calls:
+            ms = sorted(a.elapsed_time(b) for a, b in evs[name])
             mean = sum(ms) / len(ms)
+            med = ms[len(ms) // 2]
             row = {"shape": f"{M}x{N}x{K}", "kernel": name, "default": name == default,
-                   "mean_us": round(mean * 1e3, 2), "min_us": round(min(ms) * 1e3, 2),
-                   "tflops": round(flops / (mean * 1e-3) / 1e12, 2),
-                   "gbs": round(algo_bytes / (mean * 1e-3) / 1e9, 1)}
+                   "mean_us": round(mean * 1e3, 2), "median_us": round(med * 1e3, 2),
+                   "min_us": round(ms[0] * 1e3, 2),
+                   "tflops": round(flops / (med * 1e-3) / 1e12, 2),
+                   "gbs": round(algo_bytes / (med * 1e-3) / 1e9, 1)}
             rows.append(row)
             print(f"{row['shape']:>16} {name:<40} {'*' if row['default'] else ' '} "
-                  f"{row['mean_us']:>10.2f} us  min {row['min_us']:>10.2f}  "
-                  f"{row['tflops']:>8.2f} TFLOP/s  {row['gbs']:>9.1f} GB/s", flush=True)
+                  f"median {row['median_us']:>10.2f} us  mean {row['mean_us']:>10.2f}  "
+                  f"min {row['min_us']:>10.2f}  {row['tflops']:>8.2f} TFLOP/s  "
+                  f"{row['gbs']:>9.1f} GB/s", flush=True)
         del As, Bs, Cs
         torch.cuda.empty_cache()
     if args.json:

@@ -103,10 +103,10 @@ def test_adjacent_but_not_overlapping_is_not_alias():
     (3, 8192, 8192, 8192, 8192, P16, Q16, "skinny_w8_c4"),
     (16, 4096, 4096, 4096, 4096, P16, Q16, "skinny_w8_c4"),
     (8, 3001, 1531, 1531, 3001, P16, Q16, "skinny_w8_c4"),
-    (4096, 4096, 4096, 4096, 4096, P16, Q16, "mfma_256x128"),
-    (2047, 3001, 1531, 1531, 3001, P16, Q16, "mfma_128x64"),
-    (512, 512, 512, 512, 512, P16, Q16, "mfma_64x64x16_w32x32_sk"),
-    (1024, 1024, 1024, 1024, 1024, P16, Q16, "mfma_64x64x32"),
+    (4096, 4096, 4096, 4096, 4096, P16, Q16, "mfma_128x256x16_w64x128_d6"),
+    (2047, 3001, 1531, 1531, 3001, P16, Q16, "mfma_64x64x32_w32x32_p5"),
+    (512, 512, 512, 512, 512, P16, Q16, "mfma_64x64x32_w32x32_d6_sk"),
+    (1024, 1024, 1024, 1024, 1024, P16, Q16, "mfma_64x64x32_w32x32_d6"),
 ])
 def test_dispatcher_families(M, N, K, lda, ldb, A, B, expect):
     name = binding.gemm_f32_selected_kernel(M, N, K, lda, ldb, max(N, 1), A, B, R16)
@@ -128,9 +128,26 @@ def test_dispatcher_picks_128_bit_loads_for_any_pitch():
             name = sel(M, N, K, lda, ldb, ldc, pa, pb, R16)
             assert name in names, name
             assert not name.endswith("_scalar"), name
-    # pointers that are not 4-byte aligned get the element-wise variant (and
-    # gemm_f32 itself rejects them, see below)
-    assert sel(64, 64, 64, 64, 64, 64, P16 + 2, Q16 + 2, R16).endswith("_scalar")
+
+
+
+def test_direct_to_lds_kernels_only_for_aligned_operands():
+    """Kernels with direct-to-LDS loads need 16-byte aligned A and B, lda, ldb
+    and N multiples of 4 and K a multiple of their K-tile; otherwise the
+    dispatcher takes the register-staged kernel of the same shape class."""
+    sel = binding.gemm_f32_selected_kernel
+    assert "_d6_" in sel(4096, 4096, 4096, 4096, 4096, 4096, P16, Q16, R16)
+    assert "_d6_" in sel(1024, 1024, 1024, 1024, 1024, 1024, P16, Q16, R16)
+    assert "_d6_" in sel(512, 512, 512, 512, 512, 512, P16, Q16, R16)
+    for args in [(4096, 4096, 4096, 4097, 4096, 4096, P16, Q16),      # lda % 4
+                 (4096, 4096, 4096, 4096, 4098, 4096, P16, Q16),      # ldb % 4
+                 (4096, 4095, 4096, 4096, 4096, 4096, P16, Q16),      # N % 4
+                 (4096, 4096, 4100, 4100, 4096, 4096, P16, Q16),      # K % 16
+                 (4096, 4096, 4096, 4096, 4096, 4096, P16 + 4, Q16),  # A 4-byte aligned
+                 (4096, 4096, 4096, 4096, 4096, 4096, P16, Q16 + 8)]: # B 8-byte aligned
+        M, N, K, lda, ldb, ldc, pa, pb = args
+        name = sel(M, N, K, lda, ldb, ldc, pa, pb, R16)
+        assert name.startswith("mfma_") and "_d6_" not in name, (args, name)
 
 
 def test_misaligned_pointers_are_rejected():

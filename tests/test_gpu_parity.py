@@ -77,6 +77,11 @@ def _kernel_case(name):
     vec_b = suffix in ("vec", "vecb")
     if name.startswith("skinny"):
         M, N, K = 13, 1000 + 3, 2050 + 7
+    elif "_d6_" in name:
+        # direct-to-LDS loads: N, K, lda, ldb multiples of 4 (K of 64), ragged M
+        # and N edges; with "_sk_", a last K slice shorter than the others
+        M, N, K = 301, 264, 64 * 25 if "_sk_" in name else 192
+        return M, N, K, K + 4, N + 4
     elif "_sk_" in name:
         # long enough for several K slices at BK = 16 and 32, the last one
         # shorter and ending in a partial K-tile
