@@ -5,7 +5,8 @@
         --match mfma_gemm_kernel --trace OUT/trace --fetch OUT/fetch --write OUT/write \
         [--sq OUT/sq] --command "..." --out profiles/mfma_gemm_square_4096.md
 
---trace: a ``--kernel-trace --stats`` run; --fetch / --write: ``--pmc FETCH_SIZE`` and
+--trace: a ``--kernel-trace --stats`` run (durations are taken from its
+per-dispatch trace, optionally leaving out the first --skip dispatches); --fetch / --write: ``--pmc FETCH_SIZE`` and
 ``--pmc WRITE_SIZE`` runs of ``prof_workload`` (which ends with a copy of known
 size); --sq: an optional run with SQ/GRBM counters.  HBM bytes per launch are
 the kernel's FETCH_SIZE and WRITE_SIZE (KiB) scaled by the ratio of the copy's
@@ -51,13 +52,18 @@ def counters(d: Path):
     return out
 
 
-def durations(d: Path):
-    """{kernel name: (calls, avg ns, min ns, max ns)} from a --stats run."""
+def durations(d: Path, skip: int = 0):
+    """{kernel name: (calls, avg ns, min ns, max ns)} from a --kernel-trace run,
+    leaving out the first `skip` dispatches of each kernel (clock warm-up)."""
+    per = defaultdict(list)
+    with open(_find(d, "kernel_trace.csv")) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    for r in rows:
+        per[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     res = {}
-    with open(_find(d, "kernel_stats.csv")) as f:
-        for r in csv.DictReader(f):
-            res[r["Name"]] = (int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
-                              float(r["MaxNs"]))
+    for name, ds in per.items():
+        ds = ds[skip:] if len(ds) > skip else ds
+        res[name] = (len(ds), sum(ds) / len(ds), min(ds), max(ds))
     return res
 
 
@@ -82,6 +88,8 @@ def main(argv=None):
     ap.add_argument("--write")
     ap.add_argument("--sq")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--skip", type=int, default=0,
+                    help="leave out the first SKIP dispatches of each kernel from the durations")
     ap.add_argument("--algo-bytes", type=float, required=True)
     ap.add_argument("--flops", type=float, required=True)
     ap.add_argument("--mfma-cycles", type=int, default=0,
@@ -94,9 +102,11 @@ def main(argv=None):
     lines += ["Commands (from the repository root on the MI355X box):", ""]
     lines += [f"    {c}" for c in args.command] + [""]
 
-    dur = durations(Path(args.trace))
+    dur = durations(Path(args.trace), args.skip)
     names = pick(dur, args.match)
     lines += ["## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+              f"Durations from the trace, leaving out the first {args.skip} dispatches of each "
+              "kernel (clock warm-up).", "",
               "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
     tot_avg = 0.0
     for n in names:
@@ -136,7 +146,7 @@ def main(argv=None):
         if "GRBM_GUI_ACTIVE" in c:
             xcd_cycles = c["GRBM_GUI_ACTIVE"] / 8.0     # summed over the 8 XCDs
             lines.append("")
-            dur = durations(Path(args.trace))
+            dur = durations(Path(args.trace), args.skip)
             if n in dur:
                 lines.append(f"Clock while the kernel runs = GRBM_GUI_ACTIVE/8 / average duration "
                              f"= {xcd_cycles / dur[n][1]:.3f} GHz")
