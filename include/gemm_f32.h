@@ -27,9 +27,11 @@
  * Memory and ownership.  A, B and C are caller-owned device memory that the
  * current HIP device can access (hipMalloc or a torch CUDA/HIP tensor).  The
  * library keeps no reference to them after the call returns.  It owns only
- * its code objects and, for the skinny-M kernel, a scratch workspace (per
- * device and stream, allocated on first need, freed by
- * gemm_f32_release_workspaces or at unload).  C must not overlap A or B.
+ * its code objects and, for the kernels that split K over workgroups (the
+ * skinny-M kernel and the K-split MFMA entries), a scratch workspace of
+ * per-slice partial sums (per device and stream, allocated on first need,
+ * freed by gemm_f32_release_workspaces or at unload).  C must not overlap A
+ * or B.
  *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
  * stream).  Work is enqueued on it and the call returns without waiting; the
@@ -73,8 +75,14 @@ enum gemm_f32_status {
 
 /*
  * gemm_f32 -- C = A x B with the kernel the dispatcher picks from the gfx950
- * tuning table (macro-tiled MFMA kernel, skinny-M split-K kernel, or the
- * K == 0 fill).  Arguments as described above.
+ * tuning table (a macro-tiled MFMA kernel, with K split over workgroups for
+ * small grids; the skinny-M kernel for M <= 16; or the K == 0 fill).  The
+ * tiled kernels follow "Optimizing a WebGPU Matmul Kernel using Subgroups"
+ * (sections 2-8: workgroup tiles, coalesced and 128-bit loads, shared-memory
+ * tiles, register blocking, a matrix instruction) and the guarded tiles of
+ * the GEMM Optimization Guide (section 4); the K split and its second pass
+ * follow "GPU compute shaders" (How it works, step 6).  Arguments as
+ * described above.
  */
 int gemm_f32(int64_t M, int64_t N, int64_t K,
              const float *A, int64_t lda,
@@ -118,8 +126,10 @@ int gemm_f32_version(void);
  * gemm_f32_kernel_name returns NULL for an index out of range.
  * gemm_f32_run_kernel runs entry `index` exactly as gemm_f32 would run it if
  * the dispatcher had picked it; entries that cannot handle the arguments
- * (e.g. a vector-load variant with an unaligned pitch, or a skinny variant
- * with too many rows) return GEMM_F32_ERR_BAD_KERNEL and enqueue nothing.
+ * (a direct-to-LDS variant, named "..._d6_...", without 16-byte aligned A and
+ * B, lda, ldb and N multiples of 4 and K a multiple of its K-tile; or a
+ * skinny variant with more than 16 rows) return GEMM_F32_ERR_BAD_KERNEL and
+ * enqueue nothing.
  */
 int gemm_f32_kernel_count(void);
 const char *gemm_f32_kernel_name(int index);
