@@ -15,6 +15,10 @@ from the 256 MB last-level cache) and reported under "secondary".
 
 cpu_baseline: the CPU oracle (binary64 triple loop) timed on a bounded sample
 of the same workload (the first R rows of A), scaled to GFLOP/s.
+
+--configs: one JSON line per workload instead (median and min of 20 timed
+calls, rate and fraction of peak, bitwise rerun check, and the oracle's time
+on the host with the GPU result's agreement with it).
 """
 from __future__ import annotations
 
@@ -41,6 +45,9 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--configs", action="store_true",
+                    help="instead of the single headline line, print one JSON line per "
+                         "workload (median/min time, rate, reruns, oracle time and agreement)")
     return ap.parse_args()
 
 
@@ -104,12 +111,86 @@ def cpu_baseline(w, target_s):
                       f"accumulation), {dt:.2f} s wall"}
 
 
+def cpu_baseline_config(w, C_gpu, C_gpu_int):
+    """The oracle over the whole workload on the host cores: its time, and how
+    the GPU results of the same inputs compare with it (float: max of
+    |dC| / sum|a||b|; integer inputs: bit-exact)."""
+    import numpy as np
+    import oracle
+    from dense_fp32_gemm_f32_amd import inputs
+    A, B = inputs.workload_inputs(w)
+    t0 = time.perf_counter()
+    C_ref, _, ABS = oracle.gemm(A.numpy(), B.numpy(), want_f64=True)
+    dt = time.perf_counter() - t0
+    err = np.abs(C_gpu.astype(np.float64) - C_ref.astype(np.float64))
+    ratio = float(np.max(np.where(ABS > 0, err / np.where(ABS > 0, ABS, 1.0), err)))
+    Ai, Bi = inputs.workload_inputs(w, integer=True)
+    Ci_ref, _, _ = oracle.gemm(Ai.numpy(), Bi.numpy(), want_f64=True)
+    return {"oracle_s": round(dt, 3), "oracle_cores": oracle.max_threads(),
+            "oracle_gflops": round(w.flops / dt / 1e9, 3),
+            "max_err_ratio": ratio, "int_bitexact": bool(np.array_equal(C_gpu_int, Ci_ref))}
+
+
+def per_config(args):
+    """One JSON line per workload (the per-config record of the measurement
+    plan): 5 warm-up calls, then 20 event-timed calls; median and min."""
+    import torch
+    from dense_fp32_gemm_f32_amd import binding, inputs
+    binding.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    props = torch.cuda.get_device_properties(dev)
+    for name, w in inputs.WORKLOADS.items():
+        copies = 4 if name == inputs.SKINNY else 1   # stream B from HBM, not the cache
+        As, Bs, Cs = [], [], []
+        for c in range(copies):
+            a, b = (inputs.workload_inputs(w) if c == 0 else
+                    inputs.make_ab(w.M, w.N, w.K, w.dist_a, w.dist_b, w.seed + 100 * c))
+            As.append(a.to(dev))
+            Bs.append(b.to(dev))
+            Cs.append(torch.empty((w.M, w.N), device=dev))
+        kname = binding.selected_kernel(As[0], Bs[0], Cs[0])
+        _, per = time_launches(lambda i: binding.gemm(As[i % copies], Bs[i % copies],
+                                                      Cs[i % copies]), 20, 5, stream)
+        per = sorted(per)
+        t_med, t_min = per[len(per) // 2], per[0]
+        C1 = binding.gemm(As[0], Bs[0]).cpu()
+        C2 = binding.gemm(As[0], Bs[0]).cpu()
+        ai, bi = inputs.workload_inputs(w, integer=True)
+        Ci = binding.gemm(ai.to(dev), bi.to(dev)).cpu()
+        torch.cuda.synchronize()
+        rec = {"config": name, "M": w.M, "N": w.N, "K": w.K, "lda": w.K, "ldb": w.N,
+               "ldc": w.N, "seed": w.seed, "kernel_entry": kname,
+               "t_median_us": round(t_med * 1e3, 2), "t_min_us": round(t_min * 1e3, 2),
+               "gflops": round(w.flops / (t_med * 1e-3) / 1e9, 1),
+               "pct_mfma_peak": round(100 * w.flops / (t_med * 1e-3) / 1e12
+                                      / PEAK_FP32_MFMA_TFLOPS, 2),
+               "gbps": round(w.algo_bytes / (t_med * 1e-3) / 1e9, 1),
+               "pct_hbm_peak": round(100 * w.algo_bytes / (t_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+               "repro_bitexact": bool(torch.equal(C1, C2)),
+               "traffic": traffic_for(kname),
+               "device": {"name": props.name, "CUs": props.multi_processor_count,
+                          "arch": getattr(props, "gcnArchName", ""),
+                          "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
+                          "peak_tbps": PEAK_HBM_GBS / 1e3}}
+        if not args.no_cpu_baseline:
+            rec.update(cpu_baseline_config(w, C1.numpy(), Ci.numpy()))
+        print(json.dumps(rec), flush=True)
+        del As, Bs, Cs
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path; run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.configs:
+        per_config(args)
+        return
 
     import torch
     from dense_fp32_gemm_f32_amd import binding, inputs
