@@ -157,3 +157,83 @@ int oracle_gemm_elems(int64_t M, int64_t N, int64_t K,
   }
   return ORACLE_OK;
 }
+
+/*
+ * oracle_gemm_ex_f64acc -- the same product with either operand stored
+ * transposed, and the BLAS-style update C = alpha * op(A) op(B) + beta * C.
+ *
+ * Readings (the pages define only C = A x B): op(A)[i][k] is A[i*lda + k]
+ * when transA is 0 and A[k*lda + i] when it is 1 (A then stored K x M, the
+ * pre-transposed operand that "Optimizing a WebGPU Matmul Kernel using
+ * Subgroups" section 7 uses for B); op(B)[k][j] is B[k*ldb + j] or, when
+ * transB is 1, B[j*ldb + k] (B stored N x K).  alpha and beta are binary32
+ * values.  When beta is 0, C's input is not read (so NaN there does not
+ * propagate), as in BLAS.
+ *
+ *   S[i][j]  = sum over k, ascending, of op(A)[i][k] * op(B)[k][j]   (binary64, exact products)
+ *   Cd[i][j] = alpha * S[i][j] + beta * Cin[i][j]                    (binary64)
+ *   C[i][j]  = (float)Cd[i][j]
+ *   ABS[i][j]= |alpha| * sum over k of |products| + |beta * Cin[i][j]|
+ *
+ *   Cin, ldcin     the input C (read only when beta != 0; may alias C)
+ * Pitches: lda >= (transA ? M : K), ldb >= (transB ? K : N).
+ */
+int oracle_gemm_ex_f64acc(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                          float alpha, const float *A, int64_t lda,
+                          const float *B, int64_t ldb, float beta,
+                          const float *Cin, int64_t ldcin,
+                          float *C, int64_t ldc,
+                          double *Cd, int64_t ldcd,
+                          double *ABS, int64_t ldabs) {
+  if (M < 0 || N < 0 || K < 0) return ORACLE_BAD_ARG;
+  if (M == 0 || N == 0) return ORACLE_OK;
+  if (lda < (transA ? M : K) || ldb < (transB ? K : N)) return ORACLE_BAD_ARG;
+  if (C && ldc < N) return ORACLE_BAD_ARG;
+  if (Cd && ldcd < N) return ORACLE_BAD_ARG;
+  if (ABS && ldabs < N) return ORACLE_BAD_ARG;
+  if (K > 0 && (!A || !B)) return ORACLE_BAD_ARG;
+  if (beta != 0.0f && (!Cin || ldcin < N)) return ORACLE_BAD_ARG;
+
+  int failed = 0;
+#pragma omp parallel
+  {
+    double *acc = (double *)malloc((size_t)N * sizeof(double));
+    double *mag = (double *)malloc((size_t)N * sizeof(double));
+    if (!acc || !mag) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+      if (!acc || !mag) continue;
+      for (int64_t j = 0; j < N; ++j) {
+        acc[j] = 0.0;
+        mag[j] = 0.0;
+      }
+      for (int64_t k = 0; k < K; ++k) {
+        const double a = (double)(transA ? A[k * lda + i] : A[i * lda + k]);
+        for (int64_t j = 0; j < N; ++j) {
+          const double b = (double)(transB ? B[j * ldb + k] : B[k * ldb + j]);
+          const double p = a * b;
+          acc[j] += p;
+          mag[j] += fabs(p);
+        }
+      }
+      for (int64_t j = 0; j < N; ++j) {
+        double v = (double)alpha * acc[j];
+        double m = fabs((double)alpha) * mag[j];
+        if (beta != 0.0f) {
+          const double c = (double)beta * (double)Cin[i * ldcin + j];
+          v += c;
+          m += fabs(c);
+        }
+        if (C) C[i * ldc + j] = (float)v;
+        if (Cd) Cd[i * ldcd + j] = v;
+        if (ABS) ABS[i * ldabs + j] = m;
+      }
+    }
+    free(acc);
+    free(mag);
+  }
+  return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}

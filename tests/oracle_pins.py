@@ -251,3 +251,98 @@ def run_all(fn):
     for p in ALL_PINS:
         errs += p(fn)
     return errs
+
+
+# --- the extended operation: alpha * op(A) op(B) + beta * C ---------------------
+#
+# Each ``pin_ex_*`` takes ``fn_ex(A, B, trans_a, trans_b, alpha, beta, C_in) ->
+# (C, Cd, ABS)`` with the contract of ``oracle.gemm_ex``.
+
+TRANS = [(False, False), (False, True), (True, False), (True, True)]
+
+
+def _stored(X, trans):
+    """The buffer a caller passes for op(X) = X (trans false) or X^T."""
+    return np.ascontiguousarray(X.T) if trans else X
+
+
+def pin_ex_integer_bruteforce(fn_ex):
+    """Small integers, integer alpha and beta, every layout: C is exactly
+    alpha * (A @ B) + beta * C_in, computed in int64 with no floating point."""
+    errs = []
+    for (m, n, k, seed) in [(13, 9, 21, 301), (16, 16, 16, 302), (1, 7, 5, 303), (6, 1, 9, 304)]:
+        A, B = _ints(m, k, seed), _ints(k, n, seed + 10)
+        Cin = _ints(m, n, seed + 20, -5, 5)
+        for (ta, tb) in TRANS:
+            for (alpha, beta) in [(1, 0), (2, 1), (-1, -3), (0, 1)]:
+                C, _, _ = fn_ex(_stored(A, ta), _stored(B, tb), ta, tb, float(alpha),
+                                float(beta), Cin)
+                want = alpha * _exact_int(A, B) + beta * Cin.astype(np.int64)
+                if not np.array_equal(C.astype(np.int64), want):
+                    errs += _fail("ex-integer", f"{m}x{n}x{k} trans={ta},{tb} "
+                                                f"alpha={alpha} beta={beta}")
+    return errs
+
+
+def pin_ex_float_layouts(fn_ex):
+    """alpha = 1, beta = 0: every layout gives, bit for bit, the product of
+    the explicitly transposed operands under the plain oracle contract (C, Cd
+    and ABS), which the pins above fix."""
+    import oracle
+    errs = []
+    A, B = inputs.make_ab(19, 23, 37, "normal", "u11", 311)
+    A, B = _np(A), _np(B)
+    C0, Cd0, ABS0 = oracle.gemm(A, B)
+    for (ta, tb) in TRANS:
+        C, Cd, ABS = fn_ex(_stored(A, ta), _stored(B, tb), ta, tb, 1.0, 0.0, None)
+        if not (np.array_equal(C, C0) and np.array_equal(Cd, Cd0) and np.array_equal(ABS, ABS0)):
+            errs += _fail("ex-layouts", f"trans={ta},{tb} differs from the plain product")
+    return errs
+
+
+def pin_ex_beta_zero_ignores_c(fn_ex):
+    """beta = 0: the input C is not read, so NaN there does not reach C."""
+    A, B = _ints(7, 11, 321), _ints(11, 5, 322)
+    Cin = np.full((7, 5), np.nan, np.float32)
+    C, _, _ = fn_ex(A, B, False, False, 3.0, 0.0, Cin)
+    if not np.all(np.isfinite(C)):
+        return _fail("ex-beta0", "NaN of the input C reached C with beta = 0")
+    return [] if np.array_equal(C.astype(np.int64), 3 * _exact_int(A, B)) else \
+        _fail("ex-beta0", "C != 3 A B")
+
+
+def pin_ex_alpha_zero(fn_ex):
+    """alpha = 0, beta = 1: C is the input C bit for bit (any A, B)."""
+    A, B = inputs.make_ab(9, 8, 30, "normal", "normal", 331)
+    Cin = _np(inputs.uniform_matrix(9, 8, 332))
+    C, _, ABS = fn_ex(_np(A), _np(B), False, False, 0.0, 1.0, Cin)
+    errs = [] if np.array_equal(C, Cin) else _fail("ex-alpha0", "C != C_in")
+    if not np.array_equal(ABS, np.abs(Cin.astype(np.float64))):
+        errs += _fail("ex-alpha0", "ABS != |C_in|")
+    return errs
+
+
+def pin_ex_pitch(fn_ex):
+    """Transposed operands with padded pitches (padding = NaN) give the same C."""
+    errs = []
+    A, B = inputs.make_ab(21, 17, 26, "u11", "u11", 341)
+    for (ta, tb) in TRANS:
+        As, Bs = _stored(_np(A), ta), _stored(_np(B), tb)
+        Ap = _np(inputs.embed(torch.from_numpy(As), As.shape[1] + 3))[:, :As.shape[1]]
+        Bp = _np(inputs.embed(torch.from_numpy(Bs), Bs.shape[1] + 5))[:, :Bs.shape[1]]
+        C1, _, _ = fn_ex(As, Bs, ta, tb, 1.5, 0.0, None)
+        C2, _, _ = fn_ex(Ap, Bp, ta, tb, 1.5, 0.0, None)
+        if not np.all(np.isfinite(C2)) or not np.array_equal(C1, C2):
+            errs += _fail("ex-pitch", f"trans={ta},{tb}: C depends on the row pitch")
+    return errs
+
+
+EX_PINS = [pin_ex_integer_bruteforce, pin_ex_float_layouts, pin_ex_beta_zero_ignores_c,
+           pin_ex_alpha_zero, pin_ex_pitch]
+
+
+def run_all_ex(fn_ex):
+    errs = []
+    for p in EX_PINS:
+        errs += p(fn_ex)
+    return errs

@@ -138,3 +138,70 @@ def test_thread_count_does_not_change_result():
     finally:
         oracle.set_threads(n0)
     assert np.array_equal(C1, C2) and np.array_equal(Cd1, Cd2)
+
+
+# ---- the extended operation: alpha * op(A) op(B) + beta * C -------------------
+
+def oracle_ex_fn(A, B, ta, tb, alpha, beta, C_in):
+    return oracle.gemm_ex(A, B, trans_a=ta, trans_b=tb, alpha=alpha, beta=beta, C_in=C_in)
+
+
+@pytest.mark.parametrize("pin", pins.EX_PINS, ids=lambda p: p.__name__)
+def test_oracle_ex_passes_pin(pin):
+    errs = pin(oracle_ex_fn)
+    assert not errs, "\n".join(errs)
+
+
+def _ex_variant(mistake):
+    """gemm_ex-like numpy function with one planted mistake."""
+    def fn(A, B, ta, tb, alpha, beta, C_in):
+        if mistake == "ignore_trans_a":
+            ta_eff = False
+        elif mistake == "swap_trans":
+            ta_eff = tb
+        else:
+            ta_eff = ta
+        tb_eff = ta if mistake == "swap_trans" else tb
+        opa = A.T if ta_eff else A
+        opb = B.T if tb_eff else B
+        if opa.shape[1] != opb.shape[0]:
+            opa = A.T if ta else A
+            opb = B.T if tb else B
+        # binary64 sum in ascending k, as the oracle's definition has it
+        M, K = opa.shape
+        S = np.zeros((M, opb.shape[1]), np.float64)
+        mag = np.zeros_like(S)
+        for k in range(K):
+            p = opa[:, k:k + 1].astype(np.float64) * opb[k:k + 1, :].astype(np.float64)
+            S += p
+            mag += np.abs(p)
+        a = np.float64(np.float32(alpha))
+        b = np.float64(np.float32(beta))
+        if mistake == "alpha_ignored":
+            a = 1.0
+        Cd = a * S
+        ABS = abs(a) * mag
+        if mistake == "beta_read_when_zero" or b != 0:
+            c = b * C_in.astype(np.float64) if C_in is not None else 0.0
+            if mistake == "beta_times_product":
+                Cd = Cd * b
+            else:
+                Cd = Cd + c
+                ABS = ABS + np.abs(c)
+        return Cd.astype(np.float32), Cd, ABS
+    return fn
+
+
+EX_MISTAKES = ["ignore_trans_a", "swap_trans", "alpha_ignored", "beta_read_when_zero",
+               "beta_times_product"]
+
+
+def test_ex_correct_variant_passes_all_pins():
+    errs = pins.run_all_ex(_ex_variant("none"))
+    assert not errs, "\n".join(errs)
+
+
+@pytest.mark.parametrize("mistake", EX_MISTAKES)
+def test_ex_pins_catch_planted_mistake(mistake):
+    errs = pins.run_all_ex(_ex_variant(mistake))
+    assert errs, f"no pin caught the planted mistake {mistake!r}"
