@@ -27,9 +27,10 @@ STATUS_NAMES = {
     6: "GEMM_F32_ERR_WORKSPACE", 7: "GEMM_F32_ERR_LAUNCH", 8: "GEMM_F32_ERR_BAD_KERNEL",
     9: "GEMM_F32_ERR_POINTER",
 }
-EXPORTS = ["gemm_f32", "gemm_f32_ref_gpu", "gemm_f32_status_string",
-           "gemm_f32_selected_kernel", "gemm_f32_version", "gemm_f32_kernel_count",
-           "gemm_f32_kernel_name", "gemm_f32_run_kernel", "gemm_f32_release_workspaces"]
+EXPORTS = ["gemm_f32", "gemm_f32_ex", "gemm_f32_ref_gpu", "gemm_f32_status_string",
+           "gemm_f32_selected_kernel", "gemm_f32_selected_kernel_ex", "gemm_f32_version",
+           "gemm_f32_kernel_count", "gemm_f32_kernel_name", "gemm_f32_run_kernel",
+           "gemm_f32_run_kernel_ex", "gemm_f32_release_workspaces"]
 
 
 class GemmError(RuntimeError):
@@ -59,6 +60,15 @@ def load():
         getattr(lib, name).restype = ctypes.c_int
     lib.gemm_f32_run_kernel.argtypes = [ctypes.c_int, *gemm_args]
     lib.gemm_f32_run_kernel.restype = ctypes.c_int
+    f32, ci = ctypes.c_float, ctypes.c_int
+    ex_args = [ci, ci, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, vp]
+    lib.gemm_f32_ex.argtypes = ex_args
+    lib.gemm_f32_ex.restype = ctypes.c_int
+    lib.gemm_f32_run_kernel_ex.argtypes = [ci, *ex_args]
+    lib.gemm_f32_run_kernel_ex.restype = ctypes.c_int
+    lib.gemm_f32_selected_kernel_ex.argtypes = [ci, ci, i64, i64, i64, i64, i64, i64, f32, f32,
+                                                vp, vp, vp]
+    lib.gemm_f32_selected_kernel_ex.restype = ctypes.c_char_p
     lib.gemm_f32_status_string.argtypes = [ctypes.c_int]
     lib.gemm_f32_status_string.restype = ctypes.c_char_p
     lib.gemm_f32_selected_kernel.argtypes = [i64, i64, i64, i64, i64, i64, vp, vp, vp]
@@ -79,6 +89,23 @@ def load():
 
 def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
     return load().gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    return load().gemm_f32_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                              stream)
+
+
+def gemm_f32_run_kernel_ex(index, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                           stream=0) -> int:
+    return load().gemm_f32_run_kernel_ex(index, transA, transB, M, N, K, alpha, A, lda, B, ldb,
+                                         beta, C, ldc, stream)
+
+
+def gemm_f32_selected_kernel_ex(transA, transB, M, N, K, lda, ldb, ldc, alpha=1.0, beta=0.0,
+                                A=0, B=0, C=0) -> str:
+    return load().gemm_f32_selected_kernel_ex(transA, transB, M, N, K, lda, ldb, ldc, alpha,
+                                              beta, A, B, C).decode()
 
 
 def gemm_f32_ref_gpu(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
@@ -184,6 +211,54 @@ def run_kernel(index_or_name, A, B, C=None):
     if rc != GEMM_F32_OK:
         raise GemmError(rc, f"gemm_f32_run_kernel({index_or_name})")
     return C
+
+
+def _args_ex(A, B, C, trans_a, trans_b):
+    import torch
+    M, K = (A.shape[1], A.shape[0]) if trans_a else tuple(A.shape)
+    K2, N = (B.shape[1], B.shape[0]) if trans_b else tuple(B.shape)
+    if K != K2:
+        raise ValueError(f"inner sizes differ: op(A) is {M}x{K}, op(B) is {K2}x{N}")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if tuple(C.shape) != (M, N):
+        raise ValueError(f"C must be {M}x{N}, got {tuple(C.shape)}")
+    lda, ldb, ldc = _pitch(A, "A"), _pitch(B, "B"), _pitch(C, "C")
+    if not (A.device == B.device == C.device):
+        raise ValueError("A, B and C must be on one device")
+    stream = torch.cuda.current_stream(A.device).cuda_stream
+    return (M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, stream), C
+
+
+def gemm_ex(A, B, C=None, *, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, kernel=None):
+    """C = alpha * op(A) @ op(B) + beta * C on the GPU; A and B are the stored
+    matrices (A is K x M when trans_a, B is N x K when trans_b).  ``kernel``
+    runs one named (or indexed) kernel of the table instead of the
+    dispatcher's.  Returns C."""
+    (M, N, K, a, lda, b, ldb, c, ldc, stream), C = _args_ex(A, B, C, trans_a, trans_b)
+    ta, tb = int(bool(trans_a)), int(bool(trans_b))
+    with _device(A):
+        if kernel is None:
+            rc = gemm_f32_ex(ta, tb, M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, stream)
+        else:
+            index = kernel_index(kernel) if isinstance(kernel, str) else int(kernel)
+            rc = gemm_f32_run_kernel_ex(index, ta, tb, M, N, K, alpha, a, lda, b, ldb, beta, c,
+                                        ldc, stream)
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc, "gemm_f32_ex" if kernel is None else f"gemm_f32_run_kernel_ex({kernel})")
+    return C
+
+
+def selected_kernel_ex(A, B, C=None, *, trans_a=False, trans_b=False, alpha=1.0,
+                       beta=0.0) -> str:
+    M, K = (A.shape[1], A.shape[0]) if trans_a else tuple(A.shape)
+    N = B.shape[0] if trans_b else B.shape[1]
+    lda = max(A.stride(0), A.shape[1], 1)
+    ldb = max(B.stride(0), B.shape[1], 1)
+    ldc = N if C is None else max(C.stride(0), N)
+    return gemm_f32_selected_kernel_ex(int(bool(trans_a)), int(bool(trans_b)), M, N, K, lda,
+                                       ldb, max(ldc, 1), alpha, beta, A.data_ptr(),
+                                       B.data_ptr(), 0 if C is None else C.data_ptr())
 
 
 def selected_kernel(A, B, C=None) -> str:

@@ -28,7 +28,7 @@ namespace {
 
 // ---- kernel table: MFMA variants (whole K, then K split), skinny variants,
 // the naive kernel ----------------------------------------------------------
-enum class Kind { Mfma, MfmaSplitK, Skinny, Ref };
+enum class Kind { Mfma, MfmaSplitK, MfmaEx, Skinny, Ref };
 struct Entry {
   Kind kind;
   int sub;           // index within its family
@@ -48,6 +48,8 @@ const std::vector<Entry>& entries() {
       t.push_back({Kind::Mfma, i, gemmf32::mfma_variant(i).name});
     for (int i = 0; i < gemmf32::mfma_variant_count(); ++i)
       t.push_back({Kind::MfmaSplitK, i, split_k_name(gemmf32::mfma_variant(i).name)});
+    for (int i = 0; i < gemmf32::mfma_ex_variant_count(); ++i)
+      t.push_back({Kind::MfmaEx, i, gemmf32::mfma_ex_variant(i).name});
     for (int i = 0; i < gemmf32::skinny_variant_count(); ++i)
       t.push_back({Kind::Skinny, i, gemmf32::skinny_variant(i).name});
     t.push_back({Kind::Ref, 0, "ref_naive"});
@@ -87,17 +89,29 @@ MfmaPlan plan_mfma(const gemmf32::MfmaVariant& v, const Problem& p, bool split) 
 
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
+// The operation around the product: C = alpha * op(A) op(B) + beta * C, with
+// op(A) = A^T when ta (A stored K x M) and op(B) = B^T when tb (B stored N x K).
+struct Op {
+  bool ta = false, tb = false;
+  float alpha = 1.f, beta = 0.f;
+  bool plain() const { return !ta && !tb && alpha == 1.f && beta == 0.f; }
+};
+
 // ---- argument checks (host only, nothing enqueued) -------------------------
-int check_args(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
-               int64_t ldb, const float* C, int64_t ldc) {
+int check_args(const Op& op, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+               const float* B, int64_t ldb, const float* C, int64_t ldc) {
   const int64_t kMax = GEMM_F32_MAX_DIM;
   if (M < 0 || N < 0 || K < 0 || M > kMax || N > kMax || K > kMax)
     return GEMM_F32_ERR_INVALID_DIM;
-  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+  // stored shapes: A is a_rows x a_cols, B is b_rows x b_cols
+  const int64_t a_rows = op.ta ? K : M, a_cols = op.ta ? M : K;
+  const int64_t b_rows = op.tb ? N : K, b_cols = op.tb ? K : N;
+  if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) ||
+      ldc < (N > 1 ? N : 1))
     return GEMM_F32_ERR_INVALID_LD;
   // byte extents must stay far from overflow
   const int64_t kMaxElems = INT64_C(1) << 60;
-  if ((M > 0 && lda > kMaxElems / M) || (K > 0 && ldb > kMaxElems / K) ||
+  if ((a_rows > 0 && lda > kMaxElems / a_rows) || (b_rows > 0 && ldb > kMaxElems / b_rows) ||
       (M > 0 && ldc > kMaxElems / M))
     return GEMM_F32_ERR_INVALID_LD;
   const bool has_a = M > 0 && K > 0, has_b = K > 0 && N > 0, has_c = M > 0 && N > 0;
@@ -107,11 +121,11 @@ int check_args(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, con
   if (has_c) {
     const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(((M - 1) * ldc + N) * 4);
     if (has_a) {
-      const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)(((M - 1) * lda + K) * 4);
+      const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)(((a_rows - 1) * lda + a_cols) * 4);
       if (c0 < a1 && a0 < c1) return GEMM_F32_ERR_ALIAS;
     }
     if (has_b) {
-      const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(((K - 1) * ldb + N) * 4);
+      const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(((b_rows - 1) * ldb + b_cols) * 4);
       if (c0 < b1 && b0 < c1) return GEMM_F32_ERR_ALIAS;
     }
   }
@@ -220,8 +234,14 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Can entry e run these arguments?  (128-bit loads through registers need only
 // the 4-byte alignment checked up front; direct-to-LDS loads need more.)
-bool accepts(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
-             const void* A, const void* B) {
+bool accepts(const Entry& e, const Op& op, int64_t M, int64_t N, int64_t K, int64_t lda,
+             int64_t ldb, const void* A, const void* B) {
+  if (e.kind == Kind::MfmaEx) {
+    const auto& v = gemmf32::mfma_ex_variant(e.sub);
+    return v.trans_a == op.ta && v.trans_b == op.tb;
+  }
+  // every other kernel computes the plain product C = A B
+  if (!op.plain()) return false;
   if (e.kind == Kind::Mfma || e.kind == Kind::MfmaSplitK) {
     const auto& v = gemmf32::mfma_variant(e.sub);
     if (!v.lds_dma) return true;
@@ -231,11 +251,11 @@ bool accepts(const Entry& e, int64_t M, int64_t N, int64_t K, int64_t lda, int64
   if (e.kind == Kind::Skinny) return M <= gemmf32::skinny_variant(e.sub).mr;
   return true;
 }
-bool entry_accepts(const Entry& e, const Problem& p) {
-  return accepts(e, p.M, p.N, p.K, p.lda, p.ldb, p.A, p.B);
+bool entry_accepts(const Entry& e, const Op& op, const Problem& p) {
+  return accepts(e, op, p.M, p.N, p.K, p.lda, p.ldb, p.A, p.B);
 }
 
-int run_entry(const Entry& e, const Problem& p, int dev, hipStream_t s) {
+int run_entry(const Entry& e, const Op& op, const Problem& p, int dev, hipStream_t s) {
   if (log_enabled())
     std::fprintf(stderr, "[gemm_f32] M=%d N=%d K=%d lda=%lld ldb=%lld ldc=%lld -> %s\n", p.M,
                  p.N, p.K, (long long)p.lda, (long long)p.ldb, (long long)p.ldc,
@@ -265,6 +285,9 @@ int run_entry(const Entry& e, const Problem& p, int dev, hipStream_t s) {
       err = v.launch(p, pl, partials, s);
       break;
     }
+    case Kind::MfmaEx:
+      err = gemmf32::mfma_ex_variant(e.sub).launch(p, op.alpha, op.beta, s);
+      break;
     case Kind::Ref:
       err = gemmf32::launch_ref(p, s);
       break;
@@ -277,16 +300,23 @@ int run_entry(const Entry& e, const Problem& p, int dev, hipStream_t s) {
 }
 
 // ---- the dispatcher ---------------------------------------------------------
-std::string select_name(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
-                        const void* A, const void* B) {
+std::string select_name(const Op& op, int64_t M, int64_t N, int64_t K, int64_t lda,
+                        int64_t ldb, const void* A, const void* B) {
   if (M == 0 || N == 0) return "empty";
   if (K == 0) return "fill_zero_k0";
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  if (!op.plain()) {
+    static const char* const kLayout[2][2] = {{"_nn", "_nt"}, {"_tn", "_tt"}};
+    for (const auto& row : gemmf32::kTuningGfx950Ex) {
+      if (tiles < row.min_tiles) continue;
+      return std::string(row.kernel) + kLayout[op.ta][op.tb];
+    }
+  }
   for (const auto& row : gemmf32::kTuningGfx950) {
     if (M > row.max_m || tiles < row.min_tiles) continue;
     // a row whose kernel cannot take these arguments defers to the next one
     const int idx = find_entry(row.kernel);
-    if (idx >= 0 && accepts(entries()[idx], M, N, K, lda, ldb, A, B)) return row.kernel;
+    if (idx >= 0 && accepts(entries()[idx], op, M, N, K, lda, ldb, A, B)) return row.kernel;
   }
   return "ref_naive";
 }
@@ -297,10 +327,10 @@ struct Prepared {
   Problem p;
 };
 
-Prepared prepare(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
-                 int64_t ldb, float* C, int64_t ldc) {
+Prepared prepare(const Op& op, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                 const float* B, int64_t ldb, float* C, int64_t ldc) {
   Prepared r{};
-  r.status = check_args(M, N, K, A, lda, B, ldb, C, ldc);
+  r.status = check_args(op, M, N, K, A, lda, B, ldb, C, ldc);
   if (r.status != GEMM_F32_OK) return r;
   r.p = Problem{A, B, C, lda, ldb, ldc, (int)M, (int)N, (int)K};
   if (M == 0 || N == 0) return r;
@@ -314,34 +344,87 @@ Prepared prepare(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, c
   return r;
 }
 
+// K == 0: C = beta * C (an empty sum), or +0.0 when beta == 0.
+int run_k0(const Op& op, const Problem& p, hipStream_t s) {
+  if (gemmf32::launch_scale(p, op.beta, s) != hipSuccess) {
+    (void)hipGetLastError();
+    return GEMM_F32_ERR_LAUNCH;
+  }
+  return GEMM_F32_OK;
+}
+
+int gemm_impl(const Op& op, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+              const float* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+  Prepared r = prepare(op, M, N, K, A, lda, B, ldb, C, ldc);
+  if (r.status != GEMM_F32_OK || M == 0 || N == 0) return r.status;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) return run_k0(op, r.p, s);
+  const int idx = find_entry(select_name(op, M, N, K, lda, ldb, A, B));
+  if (idx < 0) return GEMM_F32_ERR_BAD_KERNEL;
+  return run_entry(entries()[idx], op, r.p, r.dev, s);
+}
+
+int run_kernel_impl(int index, const Op& op, int64_t M, int64_t N, int64_t K, const float* A,
+                    int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                    void* stream) {
+  const auto& t = entries();
+  if (index < 0 || index >= (int)t.size()) return GEMM_F32_ERR_BAD_KERNEL;
+  Prepared r = prepare(op, M, N, K, A, lda, B, ldb, C, ldc);
+  if (r.status != GEMM_F32_OK || M == 0 || N == 0) return r.status;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) return run_k0(op, r.p, s);
+  if (!entry_accepts(t[index], op, r.p)) return GEMM_F32_ERR_BAD_KERNEL;
+  return run_entry(t[index], op, r.p, r.dev, s);
+}
+
+const char* selected_impl(const Op& op, int64_t M, int64_t N, int64_t K, int64_t lda,
+                          int64_t ldb, int64_t ldc, const void* A, const void* B) {
+  const int64_t kMax = GEMM_F32_MAX_DIM;
+  if (M < 0 || N < 0 || K < 0 || M > kMax || N > kMax || K > kMax) return "invalid";
+  const int64_t a_cols = op.ta ? M : K, b_cols = op.tb ? K : N;
+  if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) ||
+      ldc < (N > 1 ? N : 1))
+    return "invalid";
+  const std::string name = select_name(op, M, N, K, lda, ldb, A, B);
+  if (name == "empty") return "empty";
+  if (name == "fill_zero_k0") return "fill_zero_k0";
+  const int idx = find_entry(name);
+  return idx < 0 ? "invalid" : entries()[idx].name.c_str();
+}
+
+Op make_op(int transA, int transB, float alpha, float beta) {
+  Op op;
+  op.ta = transA != 0;
+  op.tb = transB != 0;
+  op.alpha = alpha;
+  op.beta = beta;
+  return op;
+}
+
 }  // namespace
 
 extern "C" {
 
 int gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
              int64_t ldb, float* C, int64_t ldc, void* stream) {
-  Prepared r = prepare(M, N, K, A, lda, B, ldb, C, ldc);
-  if (r.status != GEMM_F32_OK || M == 0 || N == 0) return r.status;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (K == 0) {
-    if (gemmf32::launch_fill_zero(r.p, s) != hipSuccess) {
-      (void)hipGetLastError();
-      return GEMM_F32_ERR_LAUNCH;
-    }
-    return GEMM_F32_OK;
-  }
-  const int idx = find_entry(select_name(M, N, K, lda, ldb, A, B));
-  if (idx < 0) return GEMM_F32_ERR_BAD_KERNEL;
-  return run_entry(entries()[idx], r.p, r.dev, s);
+  return gemm_impl(Op{}, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_f32_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                int64_t ldc, void* stream) {
+  return gemm_impl(make_op(transA, transB, alpha, beta), M, N, K, A, lda, B, ldb, C, ldc,
+                   stream);
 }
 
 int gemm_f32_ref_gpu(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                      const float* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
-  Prepared r = prepare(M, N, K, A, lda, B, ldb, C, ldc);
+  const Op op;
+  Prepared r = prepare(op, M, N, K, A, lda, B, ldb, C, ldc);
   if (r.status != GEMM_F32_OK || M == 0 || N == 0) return r.status;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t err =
-      K == 0 ? gemmf32::launch_fill_zero(r.p, s) : gemmf32::launch_ref(r.p, s);
+      K == 0 ? gemmf32::launch_scale(r.p, 0.f, s) : gemmf32::launch_ref(r.p, s);
   if (err != hipSuccess) {
     (void)hipGetLastError();
     return GEMM_F32_ERR_LAUNCH;
@@ -352,20 +435,14 @@ int gemm_f32_ref_gpu(int64_t M, int64_t N, int64_t K, const float* A, int64_t ld
 int gemm_f32_run_kernel(int index, int64_t M, int64_t N, int64_t K, const float* A,
                         int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
                         void* stream) {
-  const auto& t = entries();
-  if (index < 0 || index >= (int)t.size()) return GEMM_F32_ERR_BAD_KERNEL;
-  Prepared r = prepare(M, N, K, A, lda, B, ldb, C, ldc);
-  if (r.status != GEMM_F32_OK || M == 0 || N == 0) return r.status;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (K == 0) {
-    if (gemmf32::launch_fill_zero(r.p, s) != hipSuccess) {
-      (void)hipGetLastError();
-      return GEMM_F32_ERR_LAUNCH;
-    }
-    return GEMM_F32_OK;
-  }
-  if (!entry_accepts(t[index], r.p)) return GEMM_F32_ERR_BAD_KERNEL;
-  return run_entry(t[index], r.p, r.dev, s);
+  return run_kernel_impl(index, Op{}, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_f32_run_kernel_ex(int index, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                           float alpha, const float* A, int64_t lda, const float* B,
+                           int64_t ldb, float beta, float* C, int64_t ldc, void* stream) {
+  return run_kernel_impl(index, make_op(transA, transB, alpha, beta), M, N, K, A, lda, B, ldb,
+                         C, ldc, stream);
 }
 
 const char* gemm_f32_status_string(int status) {
@@ -387,14 +464,15 @@ const char* gemm_f32_status_string(int status) {
 const char* gemm_f32_selected_kernel(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
                                      int64_t ldc, const void* A, const void* B, const void* C) {
   (void)C;
-  const int64_t kMax = GEMM_F32_MAX_DIM;
-  if (M < 0 || N < 0 || K < 0 || M > kMax || N > kMax || K > kMax) return "invalid";
-  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1)) return "invalid";
-  const std::string name = select_name(M, N, K, lda, ldb, A, B);
-  if (name == "empty") return "empty";
-  if (name == "fill_zero_k0") return "fill_zero_k0";
-  const int idx = find_entry(name);
-  return idx < 0 ? "invalid" : entries()[idx].name.c_str();
+  return selected_impl(Op{}, M, N, K, lda, ldb, ldc, A, B);
+}
+
+const char* gemm_f32_selected_kernel_ex(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                                        int64_t lda, int64_t ldb, int64_t ldc, float alpha,
+                                        float beta, const void* A, const void* B,
+                                        const void* C) {
+  (void)C;
+  return selected_impl(make_op(transA, transB, alpha, beta), M, N, K, lda, ldb, ldc, A, B);
 }
 
 int gemm_f32_version(void) { return GEMM_F32_VERSION; }

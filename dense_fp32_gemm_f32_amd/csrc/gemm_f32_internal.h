@@ -38,6 +38,18 @@ const MfmaVariant& mfma_variant(int i);
 int mfma_dma_variant_count();      // the direct-to-LDS kernels
 const MfmaVariant& mfma_dma_variant(int i);
 
+// ---- MFMA kernel for C = alpha * op(A) op(B) + beta * C ------------------
+// trans_a: A stored K x M (op(A) = A^T); trans_b: B stored N x K.  The
+// Problem's lda / ldb are the pitches of the stored matrices.
+struct MfmaExVariant {
+  const char* name;
+  int bm, bn, bk;
+  bool trans_a, trans_b;
+  hipError_t (*launch)(const Problem&, float alpha, float beta, hipStream_t);
+};
+int mfma_ex_variant_count();
+const MfmaExVariant& mfma_ex_variant(int i);
+
 // ---- skinny-M kernel (column tiles x K slices, then a combine) ------------
 struct SkinnyPlan {
   int splits;              // K slices (workgroups along K for one column tile)
@@ -65,6 +77,7 @@ hipError_t launch_combine(const Problem& p, int slices, const float* partials, h
 
 // ---- naive reference and the K == 0 fill ----------------------------------
 hipError_t launch_ref(const Problem& p, hipStream_t s);
-hipError_t launch_fill_zero(const Problem& p, hipStream_t s);
+// C = beta * C over the M x N window (C = +0.0 when beta == 0; C not read then)
+hipError_t launch_scale(const Problem& p, float beta, hipStream_t s);
 
 }  // namespace gemmf32

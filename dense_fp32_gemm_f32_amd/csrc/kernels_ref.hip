@@ -1,4 +1,4 @@
-// The naive reference kernel and the K == 0 fill.
+// The naive reference kernel and the K == 0 fill (C = beta * C).
 //
 // Reference kernel: one thread per element of C, as in section 1 (Naive) of
 // "Optimizing a WebGPU Matmul Kernel using Subgroups", with 16 x 16
@@ -29,11 +29,14 @@ __global__ void __launch_bounds__(kRefTile * kRefTile) ref_gemm_kernel(Problem p
   }
 }
 
-__global__ void __launch_bounds__(256) fill_zero_kernel(Problem p) {
+// An empty sum (K == 0): C = beta * C, or +0.0 without reading C when beta == 0.
+__global__ void __launch_bounds__(256) scale_kernel(Problem p, float beta) {
   const int col = blockIdx.x * 256 + threadIdx.x;
   if (col >= p.N) return;
-  for (int64_t row = blockIdx.y; row < p.M; row += gridDim.y)
-    p.C[row * p.ldc + col] = 0.f;
+  for (int64_t row = blockIdx.y; row < p.M; row += gridDim.y) {
+    float* c = p.C + row * p.ldc + col;
+    *c = beta == 0.f ? 0.f : beta * *c;
+  }
 }
 
 }  // namespace
@@ -48,13 +51,14 @@ hipError_t launch_ref(const Problem& p, hipStream_t s) {
                          dim3((unsigned)gx, (unsigned)gy), dim3(kRefTile, kRefTile), args, 0, s);
 }
 
-hipError_t launch_fill_zero(const Problem& p, hipStream_t s) {
+hipError_t launch_scale(const Problem& p, float beta, hipStream_t s) {
   const int64_t gx = (p.N + 255) / 256;
   int64_t gy = p.M;
   if (gy > kMaxGridY) gy = kMaxGridY;
   Problem pp = p;
-  void* args[] = {&pp};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fill_zero_kernel),
+  float b = beta;
+  void* args[] = {&pp, &b};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&scale_kernel),
                          dim3((unsigned)gx, (unsigned)gy), dim3(256), args, 0, s);
 }
 

@@ -37,6 +37,20 @@ constexpr TuningRow kTuningGfx950[] = {
     {kAnyM, 0, "mfma_64x64x16_w32x32_sk_veca"},
 };
 
+// C = alpha * op(A) op(B) + beta * C with a transposed operand or alpha, beta
+// other than 1, 0: the first row with at least min_tiles tiles of 128 x 128
+// names the tile; the layout suffix (_nn, _nt, _tn, _tt) comes from the call.
+struct TuningRowEx {
+  int64_t min_tiles;
+  const char* kernel;
+};
+constexpr TuningRowEx kTuningGfx950Ex[] = {
+    {768, "mfmaex_256x128x16_w128x64"},
+    {192, "mfmaex_128x128x16_w64x64"},
+    {48, "mfmaex_128x64x32_w64x32"},
+    {0, "mfmaex_64x64x32_w32x32"},
+};
+
 // K split of the "_sk_" MFMA entries: used only when the tile grid has fewer
 // than kSplitKBelowWorkgroups workgroups; then K is cut into slices of at
 // least kSplitKMinKTiles K-tiles so that tiles x slices reaches about

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GEMM_F32_VERSION 1
+#define GEMM_F32_VERSION 2
 
 /* Largest accepted M, N or K (2^31 - 2^16: tile arithmetic stays in int32). */
 #define GEMM_F32_MAX_DIM INT64_C(2147418112)
@@ -91,6 +91,34 @@ int gemm_f32(int64_t M, int64_t N, int64_t K,
              void *stream);
 
 /*
+ * gemm_f32_ex -- C = alpha * op(A) op(B) + beta * C, the BLAS-style form for
+ * row-major storage.  op(A) is A (stored M x K, element (i, k) at A[i*lda + k])
+ * when transA == 0, and A^T (A stored K x M, element (i, k) at A[k*lda + i])
+ * otherwise; op(B) is B (stored K x N) when transB == 0 and B^T (B stored
+ * N x K, element (k, j) at B[j*ldb + k]) otherwise.  lda and ldb are the
+ * pitches of the stored matrices: lda >= max(1, transA ? M : K), ldb >=
+ * max(1, transB ? K : N).  When beta == 0 the input C is not read (so NaN or
+ * Inf there does not propagate); otherwise it is read once per element.
+ * K == 0 gives C = beta * C.  alpha multiplies the product of the inputs.
+ *
+ * The pages define only C = A x B; the transposed operands follow the
+ * pre-transposed B of "Optimizing a WebGPU Matmul Kernel using Subgroups"
+ * (section 7) and the BLAS convention, alpha and beta a fused epilogue (one
+ * memory pass fewer, "GPU compute shaders", Performance section).  The plain
+ * case (transA = transB = 0, alpha = 1, beta = 0) runs exactly what gemm_f32
+ * runs.  Same checks and errors as gemm_f32, with the pitches checked against
+ * the stored shapes.
+ */
+int gemm_f32_ex(int transA, int transB,
+                int64_t M, int64_t N, int64_t K,
+                float alpha,
+                const float *A, int64_t lda,
+                const float *B, int64_t ldb,
+                float beta,
+                float *C, int64_t ldc,
+                void *stream);
+
+/*
  * gemm_f32_ref_gpu -- the same operation with the naive one-thread-per-output
  * kernel ("Optimizing a WebGPU Matmul Kernel using Subgroups", sections 1-3:
  * one invocation per element of C, adjacent threads on adjacent columns, k
@@ -117,6 +145,13 @@ const char *gemm_f32_selected_kernel(int64_t M, int64_t N, int64_t K,
                                      int64_t lda, int64_t ldb, int64_t ldc,
                                      const void *A, const void *B, const void *C);
 
+/* gemm_f32_selected_kernel for gemm_f32_ex's arguments. */
+const char *gemm_f32_selected_kernel_ex(int transA, int transB,
+                                        int64_t M, int64_t N, int64_t K,
+                                        int64_t lda, int64_t ldb, int64_t ldc,
+                                        float alpha, float beta,
+                                        const void *A, const void *B, const void *C);
+
 /* Library version (GEMM_F32_VERSION). */
 int gemm_f32_version(void);
 
@@ -139,6 +174,21 @@ int gemm_f32_run_kernel(int index,
                         const float *B, int64_t ldb,
                         float *C, int64_t ldc,
                         void *stream);
+
+/*
+ * gemm_f32_run_kernel_ex -- gemm_f32_run_kernel with gemm_f32_ex's arguments.
+ * The "mfmaex_..._<ab>" entries take the layout ab (n: stored as is, t:
+ * stored transposed) with any alpha and beta; every other entry takes only
+ * transA = transB = 0, alpha = 1, beta = 0.  Otherwise GEMM_F32_ERR_BAD_KERNEL.
+ */
+int gemm_f32_run_kernel_ex(int index, int transA, int transB,
+                           int64_t M, int64_t N, int64_t K,
+                           float alpha,
+                           const float *A, int64_t lda,
+                           const float *B, int64_t ldb,
+                           float beta,
+                           float *C, int64_t ldc,
+                           void *stream);
 
 /*
  * gemm_f32_release_workspaces -- free every scratch workspace the library

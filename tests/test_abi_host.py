@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert binding.gemm_f32_version() == 1
+    assert binding.gemm_f32_version() == 2
 
 
 def test_status_strings():
@@ -169,3 +169,49 @@ def test_every_mfma_variant_has_a_split_k_twin():
     for n in whole:
         base, width = n.rsplit("_", 1)
         assert f"{base}_sk_{width}" in names, n
+
+
+# ---- the extended operation (gemm_f32_ex) -------------------------------------
+
+LAYOUTS = {(0, 0): "_nn", (0, 1): "_nt", (1, 0): "_tn", (1, 1): "_tt"}
+
+
+@pytest.mark.parametrize("ta,tb", list(LAYOUTS))
+def test_ex_dispatcher_picks_the_layout_kernel(ta, tb):
+    sel = binding.gemm_f32_selected_kernel_ex
+    names = binding.kernel_names()
+    for (M, N, K) in [(4096, 4096, 4096), (2047, 3001, 1531), (512, 512, 512), (8, 8192, 8192),
+                      (1, 3, 5)]:
+        lda = M if ta else K
+        ldb = K if tb else N
+        name = sel(ta, tb, M, N, K, lda, ldb, N, 1.5, 0.5, P16, Q16, R16)
+        assert name in names and name.startswith("mfmaex_"), name
+        assert name.endswith(LAYOUTS[(ta, tb)]), name
+
+
+def test_ex_plain_case_runs_what_gemm_f32_runs():
+    for (M, N, K) in [(4096, 4096, 4096), (2047, 3001, 1531), (512, 512, 512), (8, 8192, 8192)]:
+        plain = binding.gemm_f32_selected_kernel(M, N, K, K, N, N, P16, Q16, R16)
+        ex = binding.gemm_f32_selected_kernel_ex(0, 0, M, N, K, K, N, N, 1.0, 0.0, P16, Q16, R16)
+        assert plain == ex
+        # alpha or beta other than 1, 0 takes the extended kernel
+        assert binding.gemm_f32_selected_kernel_ex(0, 0, M, N, K, K, N, N, 2.0, 0.0, P16, Q16,
+                                                   R16).startswith("mfmaex_")
+
+
+def test_ex_pitches_are_checked_against_the_stored_shapes():
+    f = binding.gemm_f32_ex
+    # A stored K x M when transposed: lda must cover M, not K
+    assert f(1, 0, 100, 50, 30, 1.0, P16, 30, Q16, 50, 0.0, R16, 50, 0) == 2
+    # B stored N x K when transposed: ldb must cover K
+    assert f(0, 1, 100, 50, 30, 1.0, P16, 30, Q16, 29, 0.0, R16, 50, 0) == 2
+    assert f(0, 1, 100, 50, 30, 1.0, P16, 30, Q16, 50, 0.0, R16, 49, 0) == 2
+    assert f(0, 0, -1, 50, 30, 1.0, P16, 30, Q16, 50, 0.0, R16, 50, 0) == 1
+    assert f(1, 1, 100, 50, 30, 1.0, 0, 100, Q16, 30, 0.0, R16, 50, 0) == 3
+
+
+def test_ex_alias_uses_the_stored_extent():
+    f = binding.gemm_f32_ex
+    # A stored 30 x 100 (transposed) ends 12000 bytes after P16; C right after is fine,
+    # C inside it is not
+    assert f(1, 0, 100, 50, 30, 1.0, P16, 100, Q16, 50, 0.0, P16 + 11996, 50, 0) == 4
