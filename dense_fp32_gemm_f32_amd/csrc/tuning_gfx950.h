@@ -45,9 +45,8 @@ struct TuningRowEx {
   const char* kernel;
 };
 constexpr TuningRowEx kTuningGfx950Ex[] = {
-    {768, "mfmaex_256x128x16_w128x64"},
-    {192, "mfmaex_128x128x16_w64x64"},
-    {48, "mfmaex_128x64x32_w64x32"},
+    {768, "mfmaex_128x128x16_w64x64"},
+    {192, "mfmaex_128x64x32_w64x32"},
     {0, "mfmaex_64x64x32_w32x32"},
 };
 

@@ -35,6 +35,11 @@ def main(argv=None):
     ap.add_argument("--json", default="")
     ap.add_argument("--with-torch", action="store_true",
                     help="also time torch.matmul in fp32 (vendor library, context only)")
+    ap.add_argument("--layout", default="nn", choices=["nn", "nt", "tn", "tt"],
+                    help="op(A) op(B): n = stored as is, t = stored transposed "
+                         "(gemm_f32_ex kernels); the plain kernels run only for nn")
+    ap.add_argument("--alpha", type=float, default=1.0)
+    ap.add_argument("--beta", type=float, default=0.0)
     args = ap.parse_args(argv)
 
     import torch
@@ -51,14 +56,19 @@ def main(argv=None):
         b_bytes = 4 * K * N
         copies = max(1, min(4, -(-1024 * 2 ** 20 // max(b_bytes, 1)))) if b_bytes > 32 * 2 ** 20 else 1
         As, Bs, Cs = [], [], []
+        ta, tb = args.layout[0] == "t", args.layout[1] == "t"
         for c in range(copies):
             a, b = inputs.make_ab(M, N, K, "u11", "u11", 9000 + c)
-            As.append(a.to(dev))
-            Bs.append(b.to(dev))
-            Cs.append(torch.empty((M, N), device=dev))
+            # the stored operands: A^T (K x M) and B^T (N x K) when transposed
+            As.append((a.t().contiguous() if ta else a).to(dev))
+            Bs.append((b.t().contiguous() if tb else b).to(dev))
+            Cs.append(torch.zeros((M, N), device=dev))
+        lda, ldb = (M if ta else K), (K if tb else N)
         flops = 2.0 * M * N * K
         algo_bytes = 4.0 * (M * K + K * N + M * N)
-        default = binding.selected_kernel(As[0], Bs[0], Cs[0])
+        default = binding.gemm_f32_selected_kernel_ex(
+            int(ta), int(tb), M, N, K, lda, ldb, N, args.alpha, args.beta,
+            As[0].data_ptr(), Bs[0].data_ptr(), Cs[0].data_ptr())
         cands = [(i, n) for i, n in enumerate(names)
                  if not prefixes or any(n.startswith(p) for p in prefixes)]
         if args.with_torch:
@@ -70,15 +80,22 @@ def main(argv=None):
 
                 def call(i, idx=idx):
                     a, b, c = As[i % copies], Bs[i % copies], Cs[i % copies]
-                    return binding.gemm_f32_run_kernel(idx, M, N, K, a.data_ptr(), K,
-                                                       b.data_ptr(), N, c.data_ptr(), N, s)
+                    return binding.gemm_f32_run_kernel_ex(
+                        idx, int(ta), int(tb), M, N, K, args.alpha, a.data_ptr(), lda,
+                        b.data_ptr(), ldb, args.beta, c.data_ptr(), N, s)
                 if call(0) != 0:
                     continue   # kernel does not accept this shape
             else:
                 torch.backends.cuda.matmul.allow_tf32 = False
 
                 def call(i):
-                    torch.matmul(As[i % copies], Bs[i % copies], out=Cs[i % copies])
+                    a = As[i % copies].t() if ta else As[i % copies]
+                    b = Bs[i % copies].t() if tb else Bs[i % copies]
+                    if args.alpha == 1.0 and args.beta == 0.0:
+                        torch.matmul(a, b, out=Cs[i % copies])
+                    else:
+                        torch.addmm(Cs[i % copies], a, b, beta=args.beta, alpha=args.alpha,
+                                    out=Cs[i % copies])
                     return 0
             calls.append((name, call))
         if not calls:
@@ -110,7 +127,8 @@ def main(argv=None):
             ms = sorted(a.elapsed_time(b) for a, b in evs[name])
             mean = sum(ms) / len(ms)
             med = ms[len(ms) // 2]
-            row = {"shape": f"{M}x{N}x{K}", "kernel": name, "default": name == default,
+            row = {"shape": f"{M}x{N}x{K}", "layout": args.layout, "kernel": name,
+                   "default": name == default,
                    "mean_us": round(mean * 1e3, 2), "median_us": round(med * 1e3, 2),
                    "min_us": round(ms[0] * 1e3, 2),
                    "tflops": round(flops / (med * 1e-3) / 1e12, 2),
