@@ -240,6 +240,11 @@ bool accepts(const Entry& e, const Op& op, int64_t M, int64_t N, int64_t K, int6
     const auto& v = gemmf32::mfma_ex_variant(e.sub);
     return v.trans_a == op.ta && v.trans_b == op.tb;
   }
+  if (e.kind == Kind::Skinny) {
+    // any alpha and beta; the layout the kernel was built for
+    const auto& v = gemmf32::skinny_variant(e.sub);
+    return M <= v.mr && v.trans_a == op.ta && v.trans_b == op.tb;
+  }
   // every other kernel computes the plain product C = A B
   if (!op.plain()) return false;
   if (e.kind == Kind::Mfma || e.kind == Kind::MfmaSplitK) {
@@ -248,7 +253,6 @@ bool accepts(const Entry& e, const Op& op, int64_t M, int64_t N, int64_t K, int6
     return K % v.bk == 0 && lda % 4 == 0 && ldb % 4 == 0 && N % 4 == 0 && aligned16(A) &&
            aligned16(B);
   }
-  if (e.kind == Kind::Skinny) return M <= gemmf32::skinny_variant(e.sub).mr;
   return true;
 }
 bool entry_accepts(const Entry& e, const Op& op, const Problem& p) {
@@ -282,7 +286,7 @@ int run_entry(const Entry& e, const Op& op, const Problem& p, int dev, hipStream
         const int rc = get_workspace(dev, s, pl.partial_floats, &partials);
         if (rc != GEMM_F32_OK) return rc;
       }
-      err = v.launch(p, pl, partials, s);
+      err = v.launch(p, pl, partials, op.alpha, op.beta, s);
       break;
     }
     case Kind::MfmaEx:
@@ -306,6 +310,11 @@ std::string select_name(const Op& op, int64_t M, int64_t N, int64_t K, int64_t l
   if (K == 0) return "fill_zero_k0";
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   if (!op.plain()) {
+    for (const auto& row : gemmf32::kTuningGfx950Skinny) {
+      if (M > row.max_m || row.ta != op.ta || row.tb != op.tb) continue;
+      const int idx = find_entry(row.kernel);
+      if (idx >= 0 && accepts(entries()[idx], op, M, N, K, lda, ldb, A, B)) return row.kernel;
+    }
     static const char* const kLayout[2][2] = {{"_nn", "_nt"}, {"_tn", "_tt"}};
     for (const auto& row : gemmf32::kTuningGfx950Ex) {
       if (tiles < row.min_tiles) continue;

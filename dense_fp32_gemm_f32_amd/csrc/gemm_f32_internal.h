@@ -50,11 +50,15 @@ struct MfmaExVariant {
 int mfma_ex_variant_count();
 const MfmaExVariant& mfma_ex_variant(int i);
 
-// ---- skinny-M kernel (column tiles x K slices, then a combine) ------------
+// ---- skinny-M kernels (M <= 16) --------------------------------------------
+// Two kernels: B stored K x N (column tiles x K slices, MFMA; kernels_skinny.hip)
+// and B stored N x K (rows of B^T streamed whole; kernels_skinny_t.hip).  Both
+// take A as is or transposed (trans_a) and write C = alpha * A B + beta * C,
+// directly or through the K-slice partials and the combine.
 struct SkinnyPlan {
   int splits;              // K slices (workgroups along K for one column tile)
-  int kslice;              // 16-row super-blocks per slice
-  int strips;              // column tiles
+  int kslice;              // K per slice, in the kernel's units (see its plan)
+  int strips;              // workgroups along N
   size_t partial_floats;   // workspace floats for the partial sums (0 if splits == 1)
   size_t lds_bytes;        // dynamic LDS
 };
@@ -62,18 +66,24 @@ struct SkinnyVariant {
   const char* name;
   int mr;              // rows of A handled (M <= mr)
   int waves;           // waves per workgroup
-  int unroll;          // super-blocks in flight per wave
+  int unroll;          // loads in flight per wave
   bool vec_a;          // 128-bit loads of A (needs 16-byte A rows)
   bool vec_b;          // wide loads of B (needs 16-byte B rows)
   int target_splits;   // K slices (0 = choose from the shape)
+  bool trans_a, trans_b;
   SkinnyPlan (*plan)(const Problem&, int target_splits);
-  hipError_t (*launch)(const Problem&, const SkinnyPlan&, float* partials, hipStream_t);
+  hipError_t (*launch)(const Problem&, const SkinnyPlan&, float* partials, float alpha,
+                       float beta, hipStream_t);
 };
-int skinny_variant_count();
+int skinny_variant_count();          // both kernels
 const SkinnyVariant& skinny_variant(int i);
+int skinny_t_variant_count();        // B stored N x K
+const SkinnyVariant& skinny_t_variant(int i);
 
 // ---- sum of K-slice partials: C = part[0] + part[1] + ... (slice order) ---
-hipError_t launch_combine(const Problem& p, int slices, const float* partials, hipStream_t s);
+// With alpha and beta: C = alpha * (sum of slices) + beta * C (C not read when beta == 0).
+hipError_t launch_combine(const Problem& p, int slices, const float* partials, hipStream_t s,
+                          float alpha = 1.f, float beta = 0.f);
 
 // ---- naive reference and the K == 0 fill ----------------------------------
 hipError_t launch_ref(const Problem& p, hipStream_t s);

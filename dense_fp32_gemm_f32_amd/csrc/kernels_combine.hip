@@ -16,13 +16,15 @@ constexpr int kPerThread = 4;
 constexpr int kColsPerBlock = kThreads * kPerThread;
 constexpr int kMaxGridY = 65535;
 
-// C[m][n] = part[0][m][n] + part[1][m][n] + ... in slice order, with part
+// C[m][n] = alpha * (part[0][m][n] + part[1][m][n] + ...) + beta * C[m][n],
+// the slices added in slice order (C not read when beta == 0), with part
 // packed (pitch N) and slice s at part + s*M*N.  Block (x, y) covers columns
 // [1024 x, 1024 x + 1024) of rows y, y + gridDim.y, ...; a thread owns four
 // consecutive columns, loaded as one 16-byte chunk per slice when N is a
 // multiple of 4 (then every row of every slice starts 16-byte aligned).
 __global__ void __launch_bounds__(kThreads) combine_kernel(Problem p, int slices,
-                                                          const float* __restrict__ part) {
+                                                          const float* __restrict__ part,
+                                                          float alpha, float beta) {
   const int N = p.N;
   const int n0 = blockIdx.x * kColsPerBlock + kPerThread * threadIdx.x;
   if (n0 >= N) return;
@@ -59,14 +61,19 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(Problem p, int slices
     }
     float* dst = p.C + (int64_t)m * p.ldc + n0;
 #pragma unroll
-    for (int q = 0; q < kPerThread; ++q)
-      if (n0 + q < N) dst[q] = s[q];
+    for (int q = 0; q < kPerThread; ++q) {
+      if (n0 + q < N) {
+        const float v = alpha * s[q];
+        dst[q] = beta == 0.f ? v : v + beta * dst[q];
+      }
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_combine(const Problem& p, int slices, const float* partials, hipStream_t s) {
+hipError_t launch_combine(const Problem& p, int slices, const float* partials, hipStream_t s,
+                          float alpha, float beta) {
   if (slices < 1 || !partials) return hipErrorInvalidValue;
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   const unsigned bx = (unsigned)((p.N + kColsPerBlock - 1) / kColsPerBlock);
@@ -74,7 +81,8 @@ hipError_t launch_combine(const Problem& p, int slices, const float* partials, h
   Problem pp = p;
   int sl = slices;
   const float* part = partials;
-  void* args[] = {&pp, &sl, &part};
+  float a = alpha, b = beta;
+  void* args[] = {&pp, &sl, &part, &a, &b};
   return hipLaunchKernel(reinterpret_cast<const void*>(&combine_kernel), dim3(bx, by),
                          dim3(kThreads), args, 0, s);
 }

@@ -48,7 +48,7 @@ constexpr int kGroupCols = 32;   // columns per wave: 16 lanes x float2
 // PAIR: one 8-byte load for the lane's two columns (B and its pitch 8-byte
 // aligned, N even), else two 4-byte loads.  VA: one 16-byte load of A per
 // super-block (any pitch), else four 4-byte loads.
-template <int U, bool PAIR, bool VA>
+template <int U, bool PAIR, bool VA, bool TA>
 __device__ __forceinline__ void stream_tile(const Problem& p, int lane, int n0, int first,
                                             int end, int step, bool tail,
                                             float (&out)[2][4]) {
@@ -61,7 +61,11 @@ __device__ __forceinline__ void stream_tile(const Problem& p, int lane, int n0, 
   const int col_p = c0_ok ? col : N - 2;   // PAIR only: N even, so col and col + 1 agree
   const bool a_row_ok = i16 < M;
   const int64_t ldb = p.ldb;
-  const float* arow = p.A + (int64_t)(a_row_ok ? i16 : M - 1) * p.lda + 4 * kr;
+  // element (m, k) of op(A): A[m * lda + k], or A[k * lda + m] when TA (A
+  // stored K x M); arow points at (this lane's row, k = 4 kr)
+  const int64_t a_kstride = TA ? p.lda : 1;
+  const float* arow = TA ? p.A + (a_row_ok ? i16 : M - 1) + (int64_t)(4 * kr) * p.lda
+                         : p.A + (int64_t)(a_row_ok ? i16 : M - 1) * p.lda + 4 * kr;
   const float* bl[4];   // this lane's B row s of super-block 0
 #pragma unroll
   for (int s = 0; s < 4; ++s) bl[s] = p.B + (int64_t)(4 * kr + s) * ldb;
@@ -85,7 +89,10 @@ __device__ __forceinline__ void stream_tile(const Problem& p, int lane, int n0, 
         x.b[s].y = __builtin_nontemporal_load(r + col_y);
       }
     }
-    if (VA) {
+    if (TA) {
+      const float* a = arow + (int64_t)k0 * a_kstride;
+      x.a = make_float4(a[0], a[a_kstride], a[2 * a_kstride], a[3 * a_kstride]);
+    } else if (VA) {
       // 16 bytes from a 4-byte aligned address: multi-dword global loads need
       // dword alignment only, and this copy becomes one global_load_dwordx4
       __builtin_memcpy(&x.a, arow + k0, sizeof(x.a));
@@ -145,7 +152,7 @@ __device__ __forceinline__ void stream_tile(const Problem& p, int lane, int n0, 
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int k = k0 + 4 * kr + s;
-      av[s] = arow[(k < K ? k : K - 1) - 4 * kr];
+      av[s] = arow[(int64_t)((k < K ? k : K - 1) - 4 * kr) * a_kstride];
     }
     x.a = make_float4(av[0], av[1], av[2], av[3]);
     mfma4(x, 0, true, false, k0);
@@ -161,9 +168,10 @@ __device__ __forceinline__ void stream_tile(const Problem& p, int lane, int n0, 
 // [sb_begin, sb_end) of its K slice (blockIdx.y).  The row groups are added in
 // LDS in row-group order and the result goes to C (one slice) or to the
 // slice's partial sums.
-template <int NW, int CG, int U, bool VA, bool VB>
+template <int NW, int CG, int U, bool VA, bool VB, bool TA>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 16 ? 4 : 2)))
-    skinny_tile_kernel(Problem p, int sb_per_slice, int slices, float* __restrict__ part) {
+    skinny_tile_kernel(Problem p, int sb_per_slice, int slices, float* __restrict__ part,
+                       float alpha, float beta) {
   constexpr int NRG = NW / CG;
   static_assert(NW % CG == 0, "whole row groups");
   __shared__ __attribute__((aligned(16))) float red[NW][2][4][64];
@@ -185,11 +193,11 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW
   const bool pair = VB && (N % 2) == 0 && (p.ldb % 2) == 0 &&
                     (reinterpret_cast<uintptr_t>(p.B) & 7) == 0;
   if (pair) {
-    stream_tile<U, true, VA>(p, lane, n_wg + cg * kGroupCols, sb_begin + rg, sb_end, NRG,
-                             tail, out);
+    stream_tile<U, true, VA, TA>(p, lane, n_wg + cg * kGroupCols, sb_begin + rg, sb_end, NRG,
+                                 tail, out);
   } else {
-    stream_tile<U, false, VA>(p, lane, n_wg + cg * kGroupCols, sb_begin + rg, sb_end, NRG,
-                              tail, out);
+    stream_tile<U, false, VA, TA>(p, lane, n_wg + cg * kGroupCols, sb_begin + rg, sb_end, NRG,
+                                  tail, out);
   }
 
 #pragma unroll
@@ -214,7 +222,14 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW
     if (m < M && n < N) {
       float s = red[g][c][r][l];
       for (int w = 1; w < NRG; ++w) s += red[w * CG + g][c][r][l];
-      dst[(int64_t)m * ld + n] = s;
+      float* d = dst + (int64_t)m * ld + n;
+      if (slices == 1) {
+        // C = alpha * sum + beta * C (C not read when beta == 0)
+        const float v = alpha * s;
+        *d = beta == 0.f ? v : v + beta * *d;
+      } else {
+        *d = s;
+      }
     }
   }
 }
@@ -237,33 +252,39 @@ SkinnyPlan plan_tile(const Problem& p, int target) {
   return pl;
 }
 
-template <int NW, int CG, int U, bool VA, bool VB>
-hipError_t launch_tile(const Problem& p, const SkinnyPlan& pl, float* partials, hipStream_t s) {
+template <int NW, int CG, int U, bool VA, bool VB, bool TA>
+hipError_t launch_tile(const Problem& p, const SkinnyPlan& pl, float* partials, float alpha,
+                       float beta, hipStream_t s) {
   if (pl.strips <= 0 || pl.splits < 1 || pl.splits > 65535) return hipErrorInvalidConfiguration;
   if (pl.splits > 1 && !partials) return hipErrorInvalidValue;
   Problem pp = p;
   int per = pl.kslice, slices = pl.splits;
   float* part = partials;
-  void* args[] = {&pp, &per, &slices, &part};
+  float a = alpha, b = beta;
+  void* args[] = {&pp, &per, &slices, &part, &a, &b};
   hipError_t err = hipLaunchKernel(
-      reinterpret_cast<const void*>(&skinny_tile_kernel<NW, CG, U, VA, VB>),
+      reinterpret_cast<const void*>(&skinny_tile_kernel<NW, CG, U, VA, VB, TA>),
       dim3(pl.strips, pl.splits), dim3(NW * 64), args, 0, s);
   if (err != hipSuccess || pl.splits == 1) return err;
-  return launch_combine(p, slices, partials, s);
+  return launch_combine(p, slices, partials, s, alpha, beta);
 }
 
 #define GEMMF32_SKINNY_TILE(NW, CG, U, S)                                                   \
-  {"skinny_w" #NW "_c" #CG "_u" #U "_s" #S "_vec", 16, NW, U, true, true, S,                \
-   &plan_tile<CG>, &launch_tile<NW, CG, U, true, true>},                                    \
-  {"skinny_w" #NW "_c" #CG "_u" #U "_s" #S "_veca", 16, NW, U, true, false, S,              \
-   &plan_tile<CG>, &launch_tile<NW, CG, U, true, false>},                                   \
-  {"skinny_w" #NW "_c" #CG "_u" #U "_s" #S "_vecb", 16, NW, U, false, true, S,              \
-   &plan_tile<CG>, &launch_tile<NW, CG, U, false, true>},                                   \
-  {"skinny_w" #NW "_c" #CG "_u" #U "_s" #S "_scalar", 16, NW, U, false, false, S,           \
-   &plan_tile<CG>, &launch_tile<NW, CG, U, false, false>}
+  {"skinny_w" #NW "_c" #CG "_u" #U "_s" #S "_vec", 16, NW, U, true, true, S, false, false,  \
+   &plan_tile<CG>, &launch_tile<NW, CG, U, true, true, false>},                             \
+  {"skinny_w" #NW "_c" #CG "_u" #U "_s" #S "_veca", 16, NW, U, true, false, S, false, false, \
+   &plan_tile<CG>, &launch_tile<NW, CG, U, true, false, false>},                            \
+  {"skinny_w" #NW "_c" #CG "_u" #U "_s" #S "_vecb", 16, NW, U, false, true, S, false, false, \
+   &plan_tile<CG>, &launch_tile<NW, CG, U, false, true, false>},                            \
+  {"skinny_w" #NW "_c" #CG "_u" #U "_s" #S "_scalar", 16, NW, U, false, false, S, false,     \
+   false, &plan_tile<CG>, &launch_tile<NW, CG, U, false, false, false>}
+// A stored transposed (K x M), B as is
+#define GEMMF32_SKINNY_TILE_TA(NW, CG, U, S)                                                \
+  {"skinny_w" #NW "_c" #CG "_u" #U "_s" #S "_tn", 16, NW, U, false, true, S, true, false,   \
+   &plan_tile<CG>, &launch_tile<NW, CG, U, false, true, true>}
 
 // Name: skinny_w<waves>_c<column groups of 32>_u<super-blocks in flight>_s<K
-// slices, 0 = from the shape>_<load widths>.
+// slices, 0 = from the shape>_<load widths>, or _tn for A stored transposed.
 const SkinnyVariant kVariants[] = {
     GEMMF32_SKINNY_TILE(16, 1, 4, 1),    // 32 columns, all of K: no partial sums
     GEMMF32_SKINNY_TILE(8, 1, 4, 1),
@@ -280,11 +301,17 @@ const SkinnyVariant kVariants[] = {
     GEMMF32_SKINNY_TILE(8, 8, 8, 0),
     GEMMF32_SKINNY_TILE(8, 4, 4, 8),     // 8 K slices: two workgroups per CU
     GEMMF32_SKINNY_TILE(8, 4, 8, 8),
+    GEMMF32_SKINNY_TILE_TA(8, 4, 4, 0),
 };
 
 }  // namespace
 
-int skinny_variant_count() { return (int)(sizeof(kVariants) / sizeof(kVariants[0])); }
-const SkinnyVariant& skinny_variant(int i) { return kVariants[i]; }
+int skinny_variant_count() {
+  return (int)(sizeof(kVariants) / sizeof(kVariants[0])) + skinny_t_variant_count();
+}
+const SkinnyVariant& skinny_variant(int i) {
+  const int n = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
+  return i < n ? kVariants[i] : skinny_t_variant(i - n);
+}
 
 }  // namespace gemmf32

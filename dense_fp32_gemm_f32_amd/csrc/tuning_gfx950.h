@@ -50,6 +50,22 @@ constexpr TuningRowEx kTuningGfx950Ex[] = {
     {0, "mfmaex_64x64x32_w32x32"},
 };
 
+// M <= 16 with a transposed operand or alpha, beta other than 1, 0: the first
+// row whose max_m and layout match (ta: A stored K x M, tb: B stored N x K).
+struct TuningRowSkinny {
+  int64_t max_m;
+  bool ta, tb;
+  const char* kernel;
+};
+constexpr TuningRowSkinny kTuningGfx950Skinny[] = {
+    {16, false, false, "skinny_w8_c4_u4_s0_vec"},
+    {16, true, false, "skinny_w8_c4_u4_s0_tn"},
+    {8, false, true, "skinnyt_m8_j4_u2_nt"},
+    {16, false, true, "skinnyt_m16_j4_u2_nt"},
+    {8, true, true, "skinnyt_m8_j4_u2_tt"},
+    {16, true, true, "skinnyt_m16_j4_u2_tt"},
+};
+
 // K split of the "_sk_" MFMA entries: used only when the tile grid has fewer
 // than kSplitKBelowWorkgroups workgroups; then K is cut into slices of at
 // least kSplitKMinKTiles K-tiles so that tiles x slices reaches about

@@ -185,8 +185,13 @@ def test_ex_dispatcher_picks_the_layout_kernel(ta, tb):
         lda = M if ta else K
         ldb = K if tb else N
         name = sel(ta, tb, M, N, K, lda, ldb, N, 1.5, 0.5, P16, Q16, R16)
-        assert name in names and name.startswith("mfmaex_"), name
-        assert name.endswith(LAYOUTS[(ta, tb)]), name
+        assert name in names, name
+        if M <= 16:
+            assert name.startswith("skinny"), name
+            if (ta, tb) != (0, 0):
+                assert name.endswith(LAYOUTS[(ta, tb)]), name
+        else:
+            assert name.startswith("mfmaex_") and name.endswith(LAYOUTS[(ta, tb)]), name
 
 
 def test_ex_plain_case_runs_what_gemm_f32_runs():
@@ -194,9 +199,11 @@ def test_ex_plain_case_runs_what_gemm_f32_runs():
         plain = binding.gemm_f32_selected_kernel(M, N, K, K, N, N, P16, Q16, R16)
         ex = binding.gemm_f32_selected_kernel_ex(0, 0, M, N, K, K, N, N, 1.0, 0.0, P16, Q16, R16)
         assert plain == ex
-        # alpha or beta other than 1, 0 takes the extended kernel
-        assert binding.gemm_f32_selected_kernel_ex(0, 0, M, N, K, K, N, N, 2.0, 0.0, P16, Q16,
-                                                   R16).startswith("mfmaex_")
+        # alpha or beta other than 1, 0: the extended MFMA kernel, or for M <= 16
+        # the skinny kernel (whose epilogue takes alpha and beta)
+        name = binding.gemm_f32_selected_kernel_ex(0, 0, M, N, K, K, N, N, 2.0, 0.0, P16, Q16,
+                                                   R16)
+        assert name.startswith("skinny_" if M <= 16 else "mfmaex_"), name
 
 
 def test_ex_pitches_are_checked_against_the_stored_shapes():

@@ -56,20 +56,33 @@ def _case(lib, M, N, K, ta, tb, alpha, beta, integer, seed, kernel=None, pads=(3
 
 
 def _ex_kernels():
+    """The kernels built for the extended operation: the MFMA ones in every
+    layout, and the skinny-M ones built for a transposed layout."""
     try:
         from dense_fp32_gemm_f32_amd import binding
-        return [n for n in binding.kernel_names() if n.startswith("mfmaex_")]
+        return [n for n in binding.kernel_names()
+                if n.startswith("mfmaex_") or n.endswith(("_tn", "_nt", "_tt"))]
     except Exception:  # library not built: the fixture fails the test loudly
         return ["<library missing>"]
+
+
+def _shapes_for(kname):
+    if kname.startswith("skinnyt_m"):
+        mr = int(kname.split("_")[1][1:])
+        # ragged N and K; the second shape has few columns, so K is split
+        return [(min(mr, 7), 1003, 2057), (mr, 37, 8200)]
+    if kname.startswith("skinny"):
+        return [(13, 1003, 2057), (3, 130, 777)]
+    # ragged edges in M, N and K; M, N not multiples of 4 (element-wise edge
+    # loads of a transposed operand); long enough for the branch-free loop
+    return [(301, 263, 139), (130, 70, 333)]
 
 
 @pytest.mark.parametrize("kname", _ex_kernels())
 def test_every_ex_kernel(gpu_lib, kname):
     lay = kname.rsplit("_", 1)[-1]
     ta, tb = lay[0] == "t", lay[1] == "t"
-    # ragged edges in M, N and K; M, N not multiples of 4 (element-wise edge
-    # loads of a transposed operand); long enough for the branch-free loop
-    for (M, N, K) in [(301, 263, 139), (130, 70, 333)]:
+    for (M, N, K) in _shapes_for(kname):
         _case(gpu_lib, M, N, K, ta, tb, 2.0, -1.0, True, 7001, kernel=kname)
         _case(gpu_lib, M, N, K, ta, tb, 1.0, 0.0, True, 7002, kernel=kname)
         _case(gpu_lib, M, N, K, ta, tb, 1.5, 0.5, False, 7003, kernel=kname)
@@ -77,7 +90,7 @@ def test_every_ex_kernel(gpu_lib, kname):
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
 @pytest.mark.parametrize("shape", [(512, 512, 512), (1000, 999, 777), (8, 1024, 2048),
-                                   (1, 1, 1), (5, 3, 2), (257, 129, 64)])
+                                   (16, 300, 1000), (1, 1, 1), (5, 3, 2), (257, 129, 64)])
 def test_ex_through_dispatcher(gpu_lib, ta, tb, shape):
     M, N, K = shape
     _case(gpu_lib, M, N, K, ta, tb, -2.0, 3.0, True, 7100 + M)
