@@ -26,6 +26,10 @@ namespace {
 
 using mfma::load4;
 
+// four floats at a 4-byte aligned address, as one non-temporal 128-bit load
+// (multi-dword global loads need dword alignment only)
+typedef float floatx4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
 constexpr int kWavesPerGroup = 4;
 constexpr int kChunk = 256;   // k per wave-wide load: 64 lanes x 4
 
@@ -76,11 +80,9 @@ __global__ void __launch_bounds__(kWavesPerGroup * 64)
     const int k = kb + kChunk * q + 4 * lane;
 #pragma unroll
     for (int c = 0; c < JC; ++c) {
-      const float* s = brow[c] + k;
-      x.b[c].x = __builtin_nontemporal_load(s + 0);
-      x.b[c].y = __builtin_nontemporal_load(s + 1);
-      x.b[c].z = __builtin_nontemporal_load(s + 2);
-      x.b[c].w = __builtin_nontemporal_load(s + 3);
+      const floatx4_a4 v =
+          __builtin_nontemporal_load(reinterpret_cast<const floatx4_a4*>(brow[c] + k));
+      x.b[c] = make_float4(v.x, v.y, v.z, v.w);
     }
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
@@ -211,6 +213,9 @@ const SkinnyVariant kTVariants[] = {
     GEMMF32_SKINNY_T(8, 8, 2),
     GEMMF32_SKINNY_T(8, 4, 4),
     GEMMF32_SKINNY_T(16, 4, 2),
+    GEMMF32_SKINNY_T(8, 8, 1),
+    GEMMF32_SKINNY_T(8, 4, 3),
+    GEMMF32_SKINNY_T(8, 2, 4),
 };
 
 }  // namespace
