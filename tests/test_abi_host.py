@@ -222,3 +222,8 @@ def test_ex_alias_uses_the_stored_extent():
     # A stored 30 x 100 (transposed) ends 12000 bytes after P16; C right after is fine,
     # C inside it is not
     assert f(1, 0, 100, 50, 30, 1.0, P16, 100, Q16, 50, 0.0, P16 + 11996, 50, 0) == 4
+
+
+def test_kernel_names_are_unique():
+    names = binding.kernel_names()
+    assert len(names) == len(set(names)), [n for n in names if names.count(n) > 1][:5]
