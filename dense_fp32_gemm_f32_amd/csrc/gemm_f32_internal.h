@@ -51,8 +51,10 @@ int mfma_ex_variant_count();
 const MfmaExVariant& mfma_ex_variant(int i);
 
 // ---- skinny-M kernels (M <= 16) --------------------------------------------
-// Two kernels: B stored K x N (column tiles x K slices, MFMA; kernels_skinny.hip)
-// and B stored N x K (rows of B^T streamed whole; kernels_skinny_t.hip).  Both
+// Three kernels: B stored K x N (column tiles x K slices, MFMA; kernels_skinny.hip),
+// the same with KiB row runs when B's rows are 16-byte aligned
+// (kernels_skinny_rows.hip), and B stored N x K (rows of B^T streamed whole;
+// kernels_skinny_t.hip).  Both
 // take A as is or transposed (trans_a) and write C = alpha * A B + beta * C,
 // directly or through the K-slice partials and the combine.
 struct SkinnyPlan {
@@ -74,11 +76,15 @@ struct SkinnyVariant {
   SkinnyPlan (*plan)(const Problem&, int target_splits);
   hipError_t (*launch)(const Problem&, const SkinnyPlan&, float* partials, float alpha,
                        float beta, hipStream_t);
+  // needs B 16-byte aligned with N and ldb multiples of 4 (whole float4 row runs)
+  bool b16 = false;
 };
-int skinny_variant_count();          // both kernels
+int skinny_variant_count();          // all three kernels
 const SkinnyVariant& skinny_variant(int i);
 int skinny_t_variant_count();        // B stored N x K
 const SkinnyVariant& skinny_t_variant(int i);
+int skinny_rows_variant_count();     // B stored K x N, KiB row runs
+const SkinnyVariant& skinny_rows_variant(int i);
 
 // ---- sum of K-slice partials: C = part[0] + part[1] + ... (slice order) ---
 // With alpha and beta: C = alpha * (sum of slices) + beta * C (C not read when beta == 0).

@@ -1,0 +1,305 @@
+// Skinny-M fp32 GEMM (M <= 16) reading B in whole-KiB row runs.
+//
+// For a few rows of A the product is a stream over B: each element of B is
+// used at most 16 times, so the time is reading B once from HBM.  This kernel
+// is for B stored K x N with N and the pitch multiples of 4 and B 16-byte
+// aligned.  Then every load of a wave reads 1 KiB of one row of B (64 lanes x
+// float4, 256 consecutive columns), the access pattern MI355X streams
+// fastest, and the waves of a workgroup read neighbouring KiB of the same
+// rows.
+//
+// The contraction runs on v_mfma_f32_4x4x1_16b_f32, 16 independent 4x4x1
+// outer products per instruction.  Read as C^T = B^T A^T:
+//   MFMA A operand, lane l: B[k][n0 + 4 l + c]            (block l/4, row l%4)
+//   MFMA B operand, lane l: A[4 h + l % 4][k]             (block l/4, col l%4)
+//   accumulator register r of lane l, for column phase c and row quad h:
+//     C[4 h + l % 4][n0 + 16 (l / 4) + 4 r + c]
+// so one float4 load of B feeds four MFMAs per quad of rows of A, and the
+// four registers of the four column phases are 16 consecutive columns of C.
+// (Lane maps checked on MI355X with an index probe.)
+//
+// Work split: a workgroup owns CG x 256 columns and one K slice; its waves
+// are CG column groups x RG row groups, and row group g takes the quads of
+// four rows g, g + RG, ... of the slice.  The slice of A (zero-padded to 4 MQ
+// rows and to whole quads) is staged in LDS once; the first loads of B are
+// issued before it so the stream starts at once.  The row groups are added
+// in LDS in row-group order; the slice result goes to C (one slice) or to the
+// slice's partial sums, which the combine kernel adds in slice order -- the
+// "combine groups" second pass of "GPU compute shaders" (How it works, step
+// 6), with a fixed order so reruns are bitwise identical (its Pitfalls).
+#include "gemm_f32_internal.h"
+
+namespace gemmf32 {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kColsPerWave = 256;    // 64 lanes x 4 columns
+constexpr int kTargetWorkgroups = 256;
+constexpr int kMaxLdsBytes = 64 * 1024;
+
+template <int CG, int RG, int MQ>
+struct RowsCfg {
+  static constexpr int kWaves = CG * RG;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kRows = 4 * MQ;                 // rows of A held (M <= kRows)
+  static constexpr int kAccPerLane = MQ * 4 * 4;       // [h][c] x 4 registers
+  // row-group partials parked in LDS at the end (row groups 1 .. RG-1)
+  static constexpr int kRedBytes = (RG - 1) * CG * kAccPerLane * 64 * 4;
+  static constexpr int kQuadBytes = kRows * 4 * 4;     // A slice bytes per quad of k
+  // A elements staged per thread; a slice holds at most kMaxQuads quads
+  static constexpr int kStage = 8;
+  static constexpr int kStageBytes = kStage * kThreads * 4;
+  static constexpr int kMaxQuads = kStageBytes / kQuadBytes;
+  static_assert(kRedBytes <= kMaxLdsBytes && kStageBytes <= kMaxLdsBytes,
+                "staging and the row-group reduction must fit the LDS budget");
+};
+
+template <int CG, int RG, int U, int MQ, bool TA>
+__global__ void __launch_bounds__(CG * RG * 64)
+    skinny_rows_kernel(Problem p, int kslice, int slices, float* __restrict__ part, float alpha,
+                       float beta) {
+  using Cfg = RowsCfg<CG, RG, MQ>;
+  constexpr int MR = Cfg::kRows;
+  extern __shared__ __attribute__((aligned(16))) float lds[];
+
+  const int M = p.M, N = p.N, K = p.K;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int cg = wave % CG, rg = wave / CG;
+  const int n_w = (blockIdx.x * CG + cg) * kColsPerWave;
+  const int slice = blockIdx.y;
+  const int kb = slice * kslice;
+  const int ke = min(K, kb + kslice);
+  const int nq = (ke - kb + 3) >> 2;                           // quads in the slice, >= 1
+  const int my_nq = nq > rg ? (nq - rg + RG - 1) / RG : 0;     // quads of this wave
+
+  // this lane's four columns; past N the address is clamped (N % 4 == 0) and
+  // the results of those columns are never stored
+  const int ncol = n_w + 4 * lane;
+  const float* bcol = p.B + (ncol < N ? ncol : N - 4);
+  const int64_t ldb = p.ldb;
+
+  struct Quad {
+    floatx4 b[4];
+  };
+  // j-th quad of this wave (past the last: the last again, multiplied as zeros)
+  auto load = [&](Quad& x, int j) {
+    const int jj = j < my_nq ? j : (my_nq > 0 ? my_nq - 1 : 0);
+    const int k = kb + 4 * (rg + RG * jj);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kk = k + s < ke ? k + s : ke - 1;
+      x.b[s] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(bcol + kk * ldb));
+    }
+  };
+
+  // ---- stage this slice of A: lds[(q * MR + m) * 4 + s] = A(m, kb + 4 q + s),
+  // zero for rows m >= M and for k >= ke (the plan keeps the slice within
+  // kStage elements per thread).  These loads are issued before the first
+  // loads of B, so waiting for them does not wait for B.
+  const int64_t lda = p.lda;
+  float av[Cfg::kStage];
+  bool aok[Cfg::kStage];
+#pragma unroll
+  for (int i = 0; i < Cfg::kStage; ++i) {
+    const int e = tid + i * Cfg::kThreads;
+    const int s = e & 3, m = (e >> 2) % MR, q = (e >> 2) / MR;
+    const int k = kb + 4 * q + s;
+    const int mc = m < M ? m : M - 1, kc = k < ke ? k : ke - 1;   // in-bounds address
+    av[i] = TA ? p.A[(int64_t)kc * lda + mc] : p.A[(int64_t)mc * lda + kc];
+    aok[i] = m < M && k < ke;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  Quad x[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) load(x[u], u);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < Cfg::kStage; ++i) {
+    // the loads above are unconditional: the value is consumed here, after
+    // the loads of B, so it cannot be sunk into a branch of its own
+    asm volatile("" : "+v"(av[i]));
+    lds[tid + i * Cfg::kThreads] = aok[i] ? av[i] : 0.f;
+  }
+  __syncthreads();
+
+  floatx4 acc[MQ][4];
+#pragma unroll
+  for (int h = 0; h < MQ; ++h)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[h][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const int mlane = lane & 3;
+  auto compute = [&](const Quad& xq, int j) {
+    const bool jv = j < my_nq;                 // the same for the whole wave
+    const int q = rg + RG * (jv ? j : 0);
+    const int k0 = kb + 4 * q;
+    floatx4 a[MQ];
+#pragma unroll
+    for (int h = 0; h < MQ; ++h)
+      a[h] = *reinterpret_cast<const floatx4*>(&lds[(q * MR + 4 * h + mlane) * 4]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      // rows past the slice (a clamped re-read) contribute exact zeros
+      const bool ok = jv && (k0 + s < ke);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float bv = ok ? xq.b[s][c] : 0.f;
+#pragma unroll
+        for (int h = 0; h < MQ; ++h)
+          acc[h][c] = __builtin_amdgcn_mfma_f32_4x4x1f32(bv, ok ? a[h][s] : 0.f, acc[h][c],
+                                                          0, 0, 0);
+      }
+    }
+  };
+
+  // Each quad is multiplied and its registers refilled with the quad U ahead,
+  // so U quads stay in flight.  The last two rounds refill only quads that
+  // exist: B is read once, with no loads past the slice.
+  int j0 = 0;
+  for (; j0 + 2 * U <= my_nq; j0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      compute(x[u], j0 + u);
+      load(x[u], j0 + u + U);
+      // keep the rotation in program order: the other U - 1 quads stay in
+      // flight while this one is multiplied
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    compute(x[u], j0 + u);
+    if (j0 + u + U < my_nq) load(x[u], j0 + u + U);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (j0 + U + u < my_nq) compute(x[u], j0 + U + u);
+
+  // ---- add the row groups in row-group order (LDS reused) -------------------
+  if (RG > 1) {
+    __syncthreads();   // every wave is done with the staged A
+    if (rg > 0) {
+      float* red = lds + ((rg - 1) * CG + cg) * Cfg::kAccPerLane * 64;
+#pragma unroll
+      for (int h = 0; h < MQ; ++h)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[((h * 4 + c) * 4 + r) * 64 + lane] = acc[h][c][r];
+    }
+    __syncthreads();
+    if (rg > 0) return;
+#pragma unroll
+    for (int g = 1; g < RG; ++g) {
+      const float* red = lds + ((g - 1) * CG + cg) * Cfg::kAccPerLane * 64;
+#pragma unroll
+      for (int h = 0; h < MQ; ++h)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[h][c][r] += red[((h * 4 + c) * 4 + r) * 64 + lane];
+    }
+  }
+
+  // ---- write: lane l holds C[4 h + l % 4][n_w + 16 (l / 4) + 4 r + c] --------
+  const int nb = n_w + 16 * (lane >> 2);
+#pragma unroll
+  for (int h = 0; h < MQ; ++h) {
+    const int m = 4 * h + mlane;
+    if (m >= M) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = nb + 4 * r;
+      if (n >= N) continue;   // N % 4 == 0: the four columns are all in or all out
+      if (slices == 1) {
+        // C = alpha * sum + beta * C (C not read when beta == 0)
+        float* d = p.C + (int64_t)m * p.ldc + n;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float v = alpha * acc[h][c][r];
+          d[c] = beta == 0.f ? v : v + beta * d[c];
+        }
+      } else {
+        float* d = part + ((size_t)slice * M + m) * N + n;   // 16-byte aligned: N % 4 == 0
+        *reinterpret_cast<floatx4*>(d) =
+            floatx4{acc[h][0][r], acc[h][1][r], acc[h][2][r], acc[h][3][r]};
+      }
+    }
+  }
+}
+
+// Slices: enough workgroups for every CU (or `target` slices), each slice at
+// least 4 quads per row group, and its staged A within the LDS budget.
+template <int CG, int RG, int MQ>
+SkinnyPlan plan_rows(const Problem& p, int target) {
+  using Cfg = RowsCfg<CG, RG, MQ>;
+  SkinnyPlan pl{};
+  pl.strips = (p.N + CG * kColsPerWave - 1) / (CG * kColsPerWave);
+  const int64_t quads = (p.K + 3) / 4;
+  int64_t slices = target > 0 ? target
+                              : (kTargetWorkgroups + pl.strips - 1) / pl.strips;
+  const int64_t cap = quads / (4 * RG);
+  if (slices > cap) slices = cap;
+  if (slices < 1) slices = 1;
+  int64_t per = (quads + slices - 1) / slices;
+  if (per > Cfg::kMaxQuads) per = Cfg::kMaxQuads;
+  const int64_t splits = (quads + per - 1) / per;   // no empty slice
+  pl.splits = splits > 65536 ? 65536 : (int)splits;   // launch rejects > 65535
+  pl.kslice = (int)(per * 4);
+  pl.partial_floats = pl.splits > 1 ? (size_t)pl.splits * p.M * p.N : 0;
+  pl.lds_bytes = Cfg::kStageBytes > Cfg::kRedBytes ? Cfg::kStageBytes : Cfg::kRedBytes;
+  return pl;
+}
+
+template <int CG, int RG, int U, int MQ, bool TA>
+hipError_t launch_rows(const Problem& p, const SkinnyPlan& pl, float* partials, float alpha,
+                       float beta, hipStream_t s) {
+  using Cfg = RowsCfg<CG, RG, MQ>;
+  if (pl.strips <= 0 || pl.splits < 1 || pl.splits > 65535 || p.M > Cfg::kRows ||
+      p.N % 4 != 0 || p.ldb % 4 != 0 || (reinterpret_cast<uintptr_t>(p.B) & 15) != 0 ||
+      pl.lds_bytes > (size_t)kMaxLdsBytes)
+    return hipErrorInvalidConfiguration;
+  if (pl.splits > 1 && !partials) return hipErrorInvalidValue;
+  Problem pp = p;
+  int kslice = pl.kslice, slices = pl.splits;
+  float* part = partials;
+  float a = alpha, b = beta;
+  void* args[] = {&pp, &kslice, &slices, &part, &a, &b};
+  const hipError_t err = hipLaunchKernel(
+      reinterpret_cast<const void*>(&skinny_rows_kernel<CG, RG, U, MQ, TA>),
+      dim3(pl.strips, pl.splits), dim3(Cfg::kThreads), args, pl.lds_bytes, s);
+  if (err != hipSuccess || pl.splits == 1) return err;
+  return launch_combine(p, slices, partials, s, alpha, beta);
+}
+
+// Name: skinnyr_c<column groups of 256>_r<row groups>_u<quads in flight>_m<rows
+// of A>_s<K slices, 0 = from the shape>_<nn|tn>.
+#define GEMMF32_SKINNY_ROWS(CG, RG, U, MQ, S)                                               \
+  {"skinnyr_c" #CG "_r" #RG "_u" #U "_m" #MQ "x4_s" #S "_nn", 4 * MQ, CG * RG, U, false,    \
+   true, S, false, false, &plan_rows<CG, RG, MQ>, &launch_rows<CG, RG, U, MQ, false>, true}, \
+  {"skinnyr_c" #CG "_r" #RG "_u" #U "_m" #MQ "x4_s" #S "_tn", 4 * MQ, CG * RG, U, false,    \
+   true, S, true, false, &plan_rows<CG, RG, MQ>, &launch_rows<CG, RG, U, MQ, true>, true}
+
+const SkinnyVariant kRowsVariants[] = {
+    GEMMF32_SKINNY_ROWS(2, 4, 4, 2, 0),
+    GEMMF32_SKINNY_ROWS(2, 4, 2, 2, 0),
+    GEMMF32_SKINNY_ROWS(4, 2, 2, 2, 0),
+    GEMMF32_SKINNY_ROWS(4, 1, 4, 2, 0),
+    GEMMF32_SKINNY_ROWS(1, 8, 2, 2, 8),
+    GEMMF32_SKINNY_ROWS(4, 2, 2, 4, 0),
+    GEMMF32_SKINNY_ROWS(4, 2, 4, 1, 0),
+};
+
+}  // namespace
+
+int skinny_rows_variant_count() {
+  return (int)(sizeof(kRowsVariants) / sizeof(kRowsVariants[0]));
+}
+const SkinnyVariant& skinny_rows_variant(int i) { return kRowsVariants[i]; }
+
+}  // namespace gemmf32

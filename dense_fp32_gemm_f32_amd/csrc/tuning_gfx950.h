@@ -26,6 +26,9 @@ struct TuningRow {
 constexpr int64_t kAnyM = INT64_C(0x7fffffff);
 
 constexpr TuningRow kTuningGfx950[] = {
+    // wide skinny products (N above 20k): few K slices of 512-column strips
+    // streamed in KiB row runs (8 x 28672 x 4096: 81 us against 92 us)
+    {8, 160, "skinnyr_c2_r4_u4_m2x4_s0_nn"},
     {16, 0, "skinny_w8_c4_u4_s0_vec"},
     {kAnyM, 768, "mfma_128x256x16_w64x128_d6_vec"},
     {kAnyM, 768, "mfma_256x128x16_w128x64_p5_vec"},

@@ -103,6 +103,10 @@ def test_adjacent_but_not_overlapping_is_not_alias():
     (3, 8192, 8192, 8192, 8192, P16, Q16, "skinny_w8_c4"),
     (16, 4096, 4096, 4096, 4096, P16, Q16, "skinny_w8_c4"),
     (8, 3001, 1531, 1531, 3001, P16, Q16, "skinny_w8_c4"),
+    # wide N: KiB row runs, when B's rows are 16-byte aligned; else the tile kernel
+    (8, 28672, 4096, 4096, 28672, P16, Q16, "skinnyr_c2_r4"),
+    (8, 28672, 4096, 4096, 28673, P16, Q16, "skinny_w8_c4"),
+    (16, 28672, 4096, 4096, 28672, P16, Q16, "skinny_w8_c4"),
     (4096, 4096, 4096, 4096, 4096, P16, Q16, "mfma_128x256x16_w64x128_d6"),
     (2047, 3001, 1531, 1531, 3001, P16, Q16, "mfma_64x64x32_w32x32_p5"),
     (512, 512, 512, 512, 512, P16, Q16, "mfma_64x64x32_w32x32_d6_sk"),

@@ -75,6 +75,11 @@ def _kernel_case(name):
     suffix = name.rsplit("_", 1)[-1]
     vec_a = suffix in ("vec", "veca")
     vec_b = suffix in ("vec", "vecb")
+    if name.startswith("skinnyr_"):
+        # whole float4 row runs of B: N and ldb multiples of 4; M one short of
+        # the rows the kernel holds, N ending inside a wave's 256 columns, K
+        # ending inside a quad of rows
+        return _skinnyr_rows(name) - 1, 1004, 2057, 2058, 1008
     if name.startswith("skinny"):
         M, N, K = 13, 1000 + 3, 2050 + 7
     elif "_d6_" in name:
@@ -97,6 +102,12 @@ def _kernel_case(name):
     return M, N, K, lda, ldb
 
 
+def _skinnyr_rows(name):
+    """Rows of A a skinnyr_..._m<q>x4_... kernel holds (4 q)."""
+    tok = [t for t in name.split("_") if t.startswith("m") and t.endswith("x4")][0]
+    return 4 * int(tok[1:-2])
+
+
 def _all_kernel_names():
     """Every kernel of the table except those built for a transposed layout
     (and the extended-operation MFMA kernels), which test_gpu_ex.py covers."""
@@ -111,7 +122,11 @@ def _all_kernel_names():
 @pytest.mark.parametrize("kname", _all_kernel_names())
 def test_every_kernel_variant(gpu_lib, kname):
     M, N, K, lda, ldb = _kernel_case(kname)
-    for integer in (True, False):
+    cases = [(M, N, K, lda, ldb)]
+    if kname.startswith("skinnyr_"):
+        # K too short to split: one slice, written straight to C
+        cases.append((M, N, 21, 24, ldb))
+    for (M, N, K, lda, ldb), integer in [(c, i) for c in cases for i in (True, False)]:
         dist = "int2" if integer else "u11"
         A, B = inputs.make_ab(M, N, K, dist, dist, 3001 + integer, lda=lda, ldb=ldb)
         H.say(f"kernel {kname} M={M} N={N} K={K} lda={lda} ldb={ldb} int={integer}")
