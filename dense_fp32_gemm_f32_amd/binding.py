@@ -30,7 +30,8 @@ STATUS_NAMES = {
 EXPORTS = ["gemm_f32", "gemm_f32_ex", "gemm_f32_ref_gpu", "gemm_f32_status_string",
            "gemm_f32_selected_kernel", "gemm_f32_selected_kernel_ex", "gemm_f32_version",
            "gemm_f32_kernel_count", "gemm_f32_kernel_name", "gemm_f32_run_kernel",
-           "gemm_f32_run_kernel_ex", "gemm_f32_release_workspaces"]
+           "gemm_f32_run_kernel_ex", "gemm_f32_release_workspaces", "gemm_f32_batched",
+           "gemm_f32_selected_kernel_batched"]
 
 
 class GemmError(RuntimeError):
@@ -81,6 +82,12 @@ def load():
     lib.gemm_f32_kernel_name.restype = ctypes.c_char_p
     lib.gemm_f32_release_workspaces.argtypes = []
     lib.gemm_f32_release_workspaces.restype = ctypes.c_int
+    lib.gemm_f32_batched.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64,
+                                     i64, vp]
+    lib.gemm_f32_batched.restype = ctypes.c_int
+    lib.gemm_f32_selected_kernel_batched.argtypes = [i64, i64, i64, i64, i64, i64, i64, i64,
+                                                     i64, vp, vp]
+    lib.gemm_f32_selected_kernel_batched.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -106,6 +113,18 @@ def gemm_f32_selected_kernel_ex(transA, transB, M, N, K, lda, ldb, ldc, alpha=1.
                                 A=0, B=0, C=0) -> str:
     return load().gemm_f32_selected_kernel_ex(transA, transB, M, N, K, lda, ldb, ldc, alpha,
                                               beta, A, B, C).decode()
+
+
+def gemm_f32_batched(M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch,
+                     stream=0) -> int:
+    return load().gemm_f32_batched(M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC,
+                                   batch, stream)
+
+
+def gemm_f32_selected_kernel_batched(M, N, K, lda, strideA, ldb, strideB, ldc, batch, A=0,
+                                     B=0) -> str:
+    return load().gemm_f32_selected_kernel_batched(M, N, K, lda, strideA, ldb, strideB, ldc,
+                                                   batch, A, B).decode()
 
 
 def gemm_f32_ref_gpu(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
@@ -211,6 +230,48 @@ def run_kernel(index_or_name, A, B, C=None):
     if rc != GEMM_F32_OK:
         raise GemmError(rc, f"gemm_f32_run_kernel({index_or_name})")
     return C
+
+
+def _args_batched(A, B, C):
+    """Sizes, pointers, pitches and batch strides of 3-D tensors (batch, rows,
+    cols); a batch stride of 0 (an expanded tensor) shares one matrix."""
+    import torch
+    if A.dim() != 3 or B.dim() != 3:
+        raise TypeError("A and B must be 3-D (batch, rows, cols)")
+    batch, M, K = A.shape
+    batch2, K2, N = B.shape
+    if K != K2 or batch != batch2:
+        raise ValueError(f"shapes differ: A is {tuple(A.shape)}, B is {tuple(B.shape)}")
+    if C is None:
+        C = torch.empty((batch, M, N), dtype=torch.float32, device=A.device)
+    if tuple(C.shape) != (batch, M, N):
+        raise ValueError(f"C must be {batch}x{M}x{N}, got {tuple(C.shape)}")
+    if batch == 0:
+        lda, ldb, ldc = max(K, 1), max(N, 1), max(N, 1)
+    else:
+        lda, ldb, ldc = _pitch(A[0], "A"), _pitch(B[0], "B"), _pitch(C[0], "C")
+    sa, sb, sc = A.stride(0), B.stride(0), C.stride(0)
+    if not (A.device == B.device == C.device):
+        raise ValueError("A, B and C must be on one device")
+    stream = torch.cuda.current_stream(A.device).cuda_stream
+    return (M, N, K, A.data_ptr(), lda, sa, B.data_ptr(), ldb, sb, C.data_ptr(), ldc, sc,
+            batch, stream), C
+
+
+def gemm_batched(A, B, C=None):
+    """C[b] = A[b] @ B[b] for every b, in as few launches as possible (3-D
+    tensors; a stride of 0 along the batch shares one matrix).  Returns C."""
+    args, C = _args_batched(A, B, C)
+    with _device(A):
+        rc = gemm_f32_batched(*args)
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc, "gemm_f32_batched")
+    return C
+
+
+def selected_kernel_batched(A, B, C=None) -> str:
+    (M, N, K, a, lda, sa, b, ldb, sb, _c, ldc, _sc, batch, _s), _ = _args_batched(A, B, C)
+    return gemm_f32_selected_kernel_batched(M, N, K, lda, sa, ldb, sb, ldc, batch, a, b)
 
 
 def _args_ex(A, B, C, trans_a, trans_b):

@@ -200,6 +200,14 @@ int get_workspace(int dev, hipStream_t s, size_t partial_floats, float** partial
   if (!g_ws) g_ws = new std::map<std::pair<int, uintptr_t>, Workspace>();
   Workspace& w = (*g_ws)[{dev, (uintptr_t)s}];
   if (w.bytes < need) {
+    // a stream being captured into a graph can neither wait nor allocate:
+    // the workspace must have been grown by an earlier call on that stream
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
+      (void)hipGetLastError();
+      return GEMM_F32_ERR_WORKSPACE;
+    }
+    if (cap != hipStreamCaptureStatusNone) return GEMM_F32_ERR_WORKSPACE;
     if (w.ptr) {
       // the stream may still be using the old buffer
       if (hipStreamSynchronize(s) != hipSuccess || hipFree(w.ptr) != hipSuccess) {
@@ -408,6 +416,103 @@ const char* selected_impl(const Op& op, int64_t M, int64_t N, int64_t K, int64_t
   return idx < 0 ? "invalid" : entries()[idx].name.c_str();
 }
 
+// ---- strided batch ---------------------------------------------------------
+// Product b reads A + b*sa (M x K, pitch lda) and B + b*sb (K x N, pitch ldb)
+// and writes C + b*sc (M x N, pitch ldc).  Strides of A and B may be 0 (one
+// matrix shared by every product); C's windows must not overlap.
+struct Batch {
+  int64_t sa = 0, sb = 0, sc = 0, count = 1;
+};
+
+// Byte extent of a pitched matrix (rows x cols, pitch ld), 0 if empty.
+uint64_t extent_bytes(int64_t rows, int64_t cols, int64_t ld) {
+  return rows > 0 && cols > 0 ? (uint64_t)(((rows - 1) * ld + cols) * 4) : 0;
+}
+
+int check_batch(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+                int64_t ldb, const float* C, int64_t ldc, const Batch& bt) {
+  if (bt.count < 0 || bt.count > GEMM_F32_MAX_DIM) return GEMM_F32_ERR_INVALID_DIM;
+  // dimensions, pitches, NULL pointers and alignment of the first product
+  int rc = check_args(Op{}, M, N, K, A, lda, B, ldb, C, ldc);
+  if (rc != GEMM_F32_OK || bt.count <= 1) return rc;
+  if (bt.sa < 0 || bt.sb < 0 || bt.sc < 0) return GEMM_F32_ERR_INVALID_LD;
+  const int64_t kMaxElems = INT64_C(1) << 60;
+  const int64_t last = bt.count - 1;
+  if (bt.sa > kMaxElems / last || bt.sb > kMaxElems / last || bt.sc > kMaxElems / last)
+    return GEMM_F32_ERR_INVALID_LD;
+  const uint64_t ea = extent_bytes(M, K, lda), eb = extent_bytes(K, N, ldb),
+                 ec = extent_bytes(M, N, ldc);
+  if (ec == 0) return GEMM_F32_OK;   // nothing is written
+  // the products' C windows must not overlap one another ...
+  if ((uint64_t)bt.sc * 4 < ec) return GEMM_F32_ERR_ALIAS;
+  // ... nor any A or B of the batch (whole address ranges)
+  const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(last * bt.sc * 4) + ec;
+  if (ea) {
+    const uintptr_t a0 = (uintptr_t)A, a1 = a0 + (uintptr_t)(last * bt.sa * 4) + ea;
+    if (c0 < a1 && a0 < c1) return GEMM_F32_ERR_ALIAS;
+  }
+  if (eb) {
+    const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(last * bt.sb * 4) + eb;
+    if (c0 < b1 && b0 < c1) return GEMM_F32_ERR_ALIAS;
+  }
+  return GEMM_F32_OK;
+}
+
+// Kernel for a batch of more than one product: the first row of the plain
+// table whose kernel takes a whole batch (the whole-K MFMA kernels; no K
+// split, no skinny kernel) and these arguments, sized by all tiles of the
+// batch.  A direct-to-LDS kernel also needs every product 16-byte aligned.
+std::string select_name_batched(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                                const void* A, const void* B, const Batch& bt) {
+  if (bt.count <= 1) return select_name(Op{}, M, N, K, lda, ldb, A, B);
+  if (M == 0 || N == 0) return "empty";
+  if (K == 0) return "fill_zero_k0";
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128) * bt.count;
+  for (const auto& row : gemmf32::kTuningGfx950) {
+    if (M > row.max_m || tiles < row.min_tiles) continue;
+    const int idx = find_entry(row.kernel);
+    if (idx < 0 || entries()[idx].kind != Kind::Mfma) continue;
+    if (!accepts(entries()[idx], Op{}, M, N, K, lda, ldb, A, B)) continue;
+    if (gemmf32::mfma_variant(entries()[idx].sub).lds_dma && (bt.sa % 4 != 0 || bt.sb % 4 != 0))
+      continue;
+    return row.kernel;
+  }
+  // the rows above always end in a kernel that takes any operands
+  return "ref_naive";
+}
+
+int gemm_batched_impl(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                      const float* B, int64_t ldb, float* C, int64_t ldc, const Batch& bt,
+                      void* stream) {
+  int rc = check_batch(M, N, K, A, lda, B, ldb, C, ldc, bt);
+  if (rc != GEMM_F32_OK) return rc;
+  if (bt.count == 0 || M == 0 || N == 0) return GEMM_F32_OK;
+  if (bt.count == 1) return gemm_impl(Op{}, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  Prepared r = prepare(Op{}, M, N, K, A, lda, B, ldb, C, ldc);
+  if (r.status != GEMM_F32_OK) return r.status;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int idx = -1;
+  if (K > 0) {
+    idx = find_entry(select_name_batched(M, N, K, lda, ldb, A, B, bt));
+    if (idx < 0) return GEMM_F32_ERR_BAD_KERNEL;
+  }
+  // launches of at most kMaxLaunchBatch products (grid z)
+  for (int64_t b0 = 0; b0 < bt.count; b0 += gemmf32::kMaxLaunchBatch) {
+    Problem q = r.p;
+    q.A += b0 * bt.sa;
+    q.B += b0 * bt.sb;
+    q.C += b0 * bt.sc;
+    q.sa = bt.sa;
+    q.sb = bt.sb;
+    q.sc = bt.sc;
+    const int64_t n = bt.count - b0;
+    q.batch = (int)(n < gemmf32::kMaxLaunchBatch ? n : gemmf32::kMaxLaunchBatch);
+    rc = K == 0 ? run_k0(Op{}, q, s) : run_entry(entries()[idx], Op{}, q, r.dev, s);
+    if (rc != GEMM_F32_OK) return rc;
+  }
+  return GEMM_F32_OK;
+}
+
 Op make_op(int transA, int transB, float alpha, float beta) {
   Op op;
   op.ta = transA != 0;
@@ -431,6 +536,36 @@ int gemm_f32_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float a
                 int64_t ldc, void* stream) {
   return gemm_impl(make_op(transA, transB, alpha, beta), M, N, K, A, lda, B, ldb, C, ldc,
                    stream);
+}
+
+int gemm_f32_batched(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                     int64_t strideA, const float* B, int64_t ldb, int64_t strideB, float* C,
+                     int64_t ldc, int64_t strideC, int64_t batch, void* stream) {
+  Batch bt;
+  bt.sa = strideA;
+  bt.sb = strideB;
+  bt.sc = strideC;
+  bt.count = batch;
+  return gemm_batched_impl(M, N, K, A, lda, B, ldb, C, ldc, bt, stream);
+}
+
+const char* gemm_f32_selected_kernel_batched(int64_t M, int64_t N, int64_t K, int64_t lda,
+                                             int64_t strideA, int64_t ldb, int64_t strideB,
+                                             int64_t ldc, int64_t batch, const void* A,
+                                             const void* B) {
+  if (batch < 0 || batch > GEMM_F32_MAX_DIM || strideA < 0 || strideB < 0) return "invalid";
+  if (batch <= 1) return selected_impl(Op{}, M, N, K, lda, ldb, ldc, A, B);
+  const char* plain = selected_impl(Op{}, M, N, K, lda, ldb, ldc, A, B);
+  if (std::strcmp(plain, "invalid") == 0) return plain;
+  Batch bt;
+  bt.sa = strideA;
+  bt.sb = strideB;
+  bt.count = batch;
+  const std::string name = select_name_batched(M, N, K, lda, ldb, A, B, bt);
+  if (name == "empty") return "empty";
+  if (name == "fill_zero_k0") return "fill_zero_k0";
+  const int idx = find_entry(name);
+  return idx < 0 ? "invalid" : entries()[idx].name.c_str();
 }
 
 int gemm_f32_ref_gpu(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,

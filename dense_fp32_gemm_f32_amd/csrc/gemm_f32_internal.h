@@ -16,7 +16,26 @@ struct Problem {
   float* C;
   int64_t lda, ldb, ldc;
   int M, N, K;
+  // Strided batch: product b (0 <= b < batch, blockIdx.z) reads A + b*sa and
+  // B + b*sb and writes C + b*sc.  A single product has batch == 1.  Only the
+  // whole-K MFMA kernels, the reference kernel and the K == 0 fill take
+  // batch > 1; the others reject it at launch.
+  int64_t sa = 0, sb = 0, sc = 0;
+  int batch = 1;
 };
+
+#if defined(__HIP__)
+// Point p at product blockIdx.z of a strided batch.
+__device__ __forceinline__ void select_batch(Problem& p) {
+  const int64_t b = blockIdx.z;
+  p.A += b * p.sa;
+  p.B += b * p.sb;
+  p.C += b * p.sc;
+}
+#endif
+
+// Largest batch of one launch (grid z); larger batches are launched in chunks.
+constexpr int kMaxLaunchBatch = 65535;
 
 // ---- macro-tiled fp32 MFMA kernel --------------------------------------
 // slices == 1: one workgroup per output tile over all of K, writing C.

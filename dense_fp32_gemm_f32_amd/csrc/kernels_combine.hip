@@ -75,6 +75,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(Problem p, int slices
 hipError_t launch_combine(const Problem& p, int slices, const float* partials, hipStream_t s,
                           float alpha, float beta) {
   if (slices < 1 || !partials) return hipErrorInvalidValue;
+  if (p.batch != 1) return hipErrorInvalidConfiguration;
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   const unsigned bx = (unsigned)((p.N + kColsPerBlock - 1) / kColsPerBlock);
   const unsigned by = (unsigned)(p.M < kMaxGridY ? p.M : kMaxGridY);

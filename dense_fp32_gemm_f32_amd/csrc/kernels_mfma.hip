@@ -55,6 +55,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
   __shared__ __attribute__((aligned(16))) float lds_b[2][C_::kLdsB];
 
   const int tid = threadIdx.x;
+  select_batch(p);
 
   // Workgroup -> (K slice, tile).  Consecutive ids of one XCD stay within one
   // slice, so neighbouring tiles of a slice share that XCD's L2.
@@ -474,7 +475,9 @@ hipError_t launch(const Problem& p, int slices, int kchunk, float* partials, hip
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
-  if (slices < 1 || tiles * slices > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (slices < 1 || tiles * slices > 0x7fffffff || p.batch < 1 || p.batch > kMaxLaunchBatch ||
+      (slices > 1 && p.batch != 1))
+    return hipErrorInvalidConfiguration;
   if (slices > 1) {
     // every slice non-empty and whole K-tiles except the last
     if (!partials || kchunk <= 0 || kchunk % BK != 0 ||
@@ -488,7 +491,7 @@ hipError_t launch(const Problem& p, int slices, int kchunk, float* partials, hip
   const hipError_t err = hipLaunchKernel(
       reinterpret_cast<const void*>(
           &mfma_gemm_kernel<BM, BN, BK, WM, WN, VA, VB, kMinWaves, SCHED>),
-      dim3((unsigned)(tiles * slices)), dim3(C_::kThreads), args, 0, s);
+      dim3((unsigned)(tiles * slices), 1, (unsigned)p.batch), dim3(C_::kThreads), args, 0, s);
   if (err != hipSuccess || slices == 1) return err;
   return launch_combine(p, slices, partials, s);
 }

@@ -194,6 +194,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
+  select_batch(p);
 
   // workgroup -> (K slice, tile), as in the register-staged kernel
   const int tiles = tiles_m * tiles_n;
@@ -270,8 +271,11 @@ hipError_t launch_dma(const Problem& p, int slices, int kchunk, float* partials,
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
-  if (slices < 1 || tiles * slices > 0x7fffffff) return hipErrorInvalidConfiguration;
-  // direct-to-LDS preconditions
+  if (slices < 1 || tiles * slices > 0x7fffffff || p.batch < 1 || p.batch > kMaxLaunchBatch ||
+      (slices > 1 && p.batch != 1))
+    return hipErrorInvalidConfiguration;
+  // direct-to-LDS preconditions (every product of a batch: strides multiples of 4)
+  if (p.sa % 4 != 0 || p.sb % 4 != 0) return hipErrorInvalidValue;
   if (p.K % BK != 0 || p.lda % 4 != 0 || p.ldb % 4 != 0 || p.N % 4 != 0 ||
       (reinterpret_cast<uintptr_t>(p.A) & 15) != 0 || (reinterpret_cast<uintptr_t>(p.B) & 15) != 0)
     return hipErrorInvalidValue;
@@ -286,7 +290,7 @@ hipError_t launch_dma(const Problem& p, int slices, int kchunk, float* partials,
   void* args[] = {&pp, &tm, &tn, &kc, &part};
   const hipError_t err = hipLaunchKernel(
       reinterpret_cast<const void*>(&mfma_dma_kernel<BM, BN, BK, WM, WN, kMinWaves>),
-      dim3((unsigned)(tiles * slices)), dim3(C_::kThreads), args, 0, s);
+      dim3((unsigned)(tiles * slices), 1, (unsigned)p.batch), dim3(C_::kThreads), args, 0, s);
   if (err != hipSuccess || slices == 1) return err;
   return launch_combine(p, slices, partials, s);
 }

@@ -147,6 +147,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
   __shared__ __attribute__((aligned(16))) float lds_b[2][OpB::kLds];
 
   const int tid = threadIdx.x;
+  select_batch(p);
   const int M = p.M, N = p.N, K = p.K;
   int tm, tn;
   tile_coords(xcd_contiguous_id(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
@@ -357,14 +358,16 @@ hipError_t launch_ex(const Problem& p, float alpha, float beta, hipStream_t s) {
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
-  if (tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (tiles > 0x7fffffff || p.batch < 1 || p.batch > kMaxLaunchBatch)
+    return hipErrorInvalidConfiguration;
   Problem pp = p;
   float a = alpha, b = beta;
   int tm = tiles_m, tn = tiles_n;
   void* args[] = {&pp, &a, &b, &tm, &tn};
   return hipLaunchKernel(
       reinterpret_cast<const void*>(&mfma_ex_kernel<BM, BN, BK, WM, WN, A_KC, B_KC, kMinWaves>),
-      dim3((unsigned)tiles), dim3((BM / WM) * (BN / WN) * 64), args, 0, s);
+      dim3((unsigned)tiles, 1, (unsigned)p.batch), dim3((BM / WM) * (BN / WN) * 64), args, 0,
+      s);
 }
 
 // Name: mfmaex_<tile>_<layout>, layout = op(A) op(B) as n (stored as is) or t

@@ -16,6 +16,7 @@ constexpr int kRefTile = 16;
 constexpr int kMaxGridY = 65535;
 
 __global__ void __launch_bounds__(kRefTile * kRefTile) ref_gemm_kernel(Problem p) {
+  select_batch(p);
   const int col = blockIdx.x * kRefTile + threadIdx.x;
   if (col >= p.N) return;
   // grid-stride over rows when M needs more than kMaxGridY row tiles
@@ -31,6 +32,7 @@ __global__ void __launch_bounds__(kRefTile * kRefTile) ref_gemm_kernel(Problem p
 
 // An empty sum (K == 0): C = beta * C, or +0.0 without reading C when beta == 0.
 __global__ void __launch_bounds__(256) scale_kernel(Problem p, float beta) {
+  select_batch(p);
   const int col = blockIdx.x * 256 + threadIdx.x;
   if (col >= p.N) return;
   for (int64_t row = blockIdx.y; row < p.M; row += gridDim.y) {
@@ -42,16 +44,19 @@ __global__ void __launch_bounds__(256) scale_kernel(Problem p, float beta) {
 }  // namespace
 
 hipError_t launch_ref(const Problem& p, hipStream_t s) {
+  if (p.batch < 1 || p.batch > kMaxLaunchBatch) return hipErrorInvalidConfiguration;
   const int64_t gx = (p.N + kRefTile - 1) / kRefTile;
   int64_t gy = (p.M + kRefTile - 1) / kRefTile;
   if (gy > kMaxGridY) gy = kMaxGridY;
   Problem pp = p;
   void* args[] = {&pp};
   return hipLaunchKernel(reinterpret_cast<const void*>(&ref_gemm_kernel),
-                         dim3((unsigned)gx, (unsigned)gy), dim3(kRefTile, kRefTile), args, 0, s);
+                         dim3((unsigned)gx, (unsigned)gy, (unsigned)p.batch),
+                         dim3(kRefTile, kRefTile), args, 0, s);
 }
 
 hipError_t launch_scale(const Problem& p, float beta, hipStream_t s) {
+  if (p.batch < 1 || p.batch > kMaxLaunchBatch) return hipErrorInvalidConfiguration;
   const int64_t gx = (p.N + 255) / 256;
   int64_t gy = p.M;
   if (gy > kMaxGridY) gy = kMaxGridY;
@@ -59,7 +64,8 @@ hipError_t launch_scale(const Problem& p, float beta, hipStream_t s) {
   float b = beta;
   void* args[] = {&pp, &b};
   return hipLaunchKernel(reinterpret_cast<const void*>(&scale_kernel),
-                         dim3((unsigned)gx, (unsigned)gy), dim3(256), args, 0, s);
+                         dim3((unsigned)gx, (unsigned)gy, (unsigned)p.batch), dim3(256), args,
+                         0, s);
 }
 
 }  // namespace gemmf32

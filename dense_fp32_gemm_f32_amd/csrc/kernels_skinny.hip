@@ -255,7 +255,8 @@ SkinnyPlan plan_tile(const Problem& p, int target) {
 template <int NW, int CG, int U, bool VA, bool VB, bool TA>
 hipError_t launch_tile(const Problem& p, const SkinnyPlan& pl, float* partials, float alpha,
                        float beta, hipStream_t s) {
-  if (pl.strips <= 0 || pl.splits < 1 || pl.splits > 65535) return hipErrorInvalidConfiguration;
+  if (pl.strips <= 0 || pl.splits < 1 || pl.splits > 65535 || p.batch != 1)
+    return hipErrorInvalidConfiguration;
   if (pl.splits > 1 && !partials) return hipErrorInvalidValue;
   Problem pp = p;
   int per = pl.kslice, slices = pl.splits;

@@ -260,7 +260,7 @@ template <int CG, int RG, int U, int MQ, bool TA>
 hipError_t launch_rows(const Problem& p, const SkinnyPlan& pl, float* partials, float alpha,
                        float beta, hipStream_t s) {
   using Cfg = RowsCfg<CG, RG, MQ>;
-  if (pl.strips <= 0 || pl.splits < 1 || pl.splits > 65535 || p.M > Cfg::kRows ||
+  if (pl.strips <= 0 || pl.splits < 1 || pl.splits > 65535 || p.M > Cfg::kRows || p.batch != 1 ||
       p.N % 4 != 0 || p.ldb % 4 != 0 || (reinterpret_cast<uintptr_t>(p.B) & 15) != 0 ||
       pl.lds_bytes > (size_t)kMaxLdsBytes)
     return hipErrorInvalidConfiguration;

@@ -186,7 +186,7 @@ SkinnyPlan plan_t(const Problem& p, int target) {
 template <int MR, int JC, int U, bool TA>
 hipError_t launch_t(const Problem& p, const SkinnyPlan& pl, float* partials, float alpha,
                     float beta, hipStream_t s) {
-  if (pl.strips <= 0 || pl.splits < 1 || pl.splits > 65535 || p.M > MR)
+  if (pl.strips <= 0 || pl.splits < 1 || pl.splits > 65535 || p.M > MR || p.batch != 1)
     return hipErrorInvalidConfiguration;
   if (pl.splits > 1 && !partials) return hipErrorInvalidValue;
   Problem pp = p;

@@ -120,3 +120,10 @@ def int_matrix(rows: int, cols: int, seed: int, lo: int = -2, hi: int = 2) -> to
 def uniform_matrix(rows: int, cols: int, seed: int, lo: float = -1.0, hi: float = 1.0) -> torch.Tensor:
     g = torch.Generator(device="cpu").manual_seed(seed)
     return torch.empty(rows, cols).uniform_(lo, hi, generator=g)
+
+
+def draw_matrix(rows: int, cols: int, dist: str, seed: int) -> torch.Tensor:
+    """One rows x cols matrix of the named distribution from its own seed
+    (``u_inv_sqrt_k`` scales by the row length ``cols``)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return _draw(dist, rows, cols, g, cols)

@@ -33,6 +33,12 @@
  * freed by gemm_f32_release_workspaces or at unload).  C must not overlap A
  * or B.
  *
+ * Graph capture.  Every call may be captured into a HIP graph (no memset and
+ * no host synchronisation is enqueued).  A call that needs the workspace and
+ * would have to allocate or grow it on a stream that is being captured
+ * returns GEMM_F32_ERR_WORKSPACE instead: make the same call once on that
+ * stream before capturing.
+ *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
  * stream).  Work is enqueued on it and the call returns without waiting; the
  * caller synchronises.  Calls on one stream are ordered by the stream; calls
@@ -55,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GEMM_F32_VERSION 2
+#define GEMM_F32_VERSION 3
 
 /* Largest accepted M, N or K (2^31 - 2^16: tile arithmetic stays in int32). */
 #define GEMM_F32_MAX_DIM INT64_C(2147418112)
@@ -119,6 +125,32 @@ int gemm_f32_ex(int transA, int transB,
                 void *stream);
 
 /*
+ * gemm_f32_batched -- `batch` independent products C_b = A_b x B_b, 0 <= b <
+ * batch, in as few launches as possible: A_b = A + b * strideA, B_b = B + b *
+ * strideB, C_b = C + b * strideC (strides in elements), each matrix as for
+ * gemm_f32 (row-major with pitches lda, ldb, ldc).  strideA or strideB may be
+ * 0 (one matrix shared by every product); the C windows of the products must
+ * not overlap (strideC >= (M - 1) * ldc + N, else GEMM_F32_ERR_ALIAS) and no C
+ * may overlap any A or B of the batch (GEMM_F32_ERR_ALIAS).  Negative strides
+ * give GEMM_F32_ERR_INVALID_LD, a negative batch GEMM_F32_ERR_INVALID_DIM;
+ * batch == 0 is a successful no-op and batch == 1 is exactly gemm_f32.
+ *
+ * The pages time one product per dispatch and find the per-dispatch cost
+ * dominant for small sizes, gone when dispatches are batched ("GPU compute
+ * shaders", Performance); this is that batching for a run of small products:
+ * one launch covers every tile of every product (grid z = product), with the
+ * whole-K MFMA kernels chosen by the same table from the batch's total tile
+ * count.  Each product is summed as gemm_f32 sums a product of its class:
+ * exact on small integers, within fp32 summation error otherwise.  Other
+ * checks, errors, ownership and stream behaviour as gemm_f32.
+ */
+int gemm_f32_batched(int64_t M, int64_t N, int64_t K,
+                     const float *A, int64_t lda, int64_t strideA,
+                     const float *B, int64_t ldb, int64_t strideB,
+                     float *C, int64_t ldc, int64_t strideC,
+                     int64_t batch, void *stream);
+
+/*
  * gemm_f32_ref_gpu -- the same operation with the naive one-thread-per-output
  * kernel ("Optimizing a WebGPU Matmul Kernel using Subgroups", sections 1-3:
  * one invocation per element of C, adjacent threads on adjacent columns, k
@@ -151,6 +183,13 @@ const char *gemm_f32_selected_kernel_ex(int transA, int transB,
                                         int64_t lda, int64_t ldb, int64_t ldc,
                                         float alpha, float beta,
                                         const void *A, const void *B, const void *C);
+
+/* gemm_f32_selected_kernel for gemm_f32_batched's arguments (strides of A
+ * and B; the kernel is the same whatever C's stride). */
+const char *gemm_f32_selected_kernel_batched(int64_t M, int64_t N, int64_t K,
+                                             int64_t lda, int64_t strideA,
+                                             int64_t ldb, int64_t strideB, int64_t ldc,
+                                             int64_t batch, const void *A, const void *B);
 
 /* Library version (GEMM_F32_VERSION). */
 int gemm_f32_version(void);

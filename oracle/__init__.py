@@ -193,3 +193,28 @@ def gemm_ex(A: np.ndarray, B: np.ndarray, *, trans_a: bool = False, trans_b: boo
     if rc != 0:
         raise RuntimeError(f"oracle_gemm_ex_f64acc failed with status {rc}")
     return C, Cd, ABS
+
+
+def gemm_batched(A: np.ndarray, B: np.ndarray, *, want_f64: bool = True):
+    """Return ``(C, Cd, ABS)`` for the strided batch ``C[b] = A[b] @ B[b]``.
+
+    ``A`` (batch x M x K) and ``B`` (batch x K x N) are float32 arrays whose
+    matrices have contiguous rows; a batch stride of 0 (``np.broadcast_to``)
+    shares one matrix.  Each product is ``gemm`` of its two matrices: the
+    batch is a set of independent products (the batched dispatch the "GPU
+    compute shaders" page times), with nothing shared between them.
+    """
+    if A.ndim != 3 or B.ndim != 3 or A.shape[0] != B.shape[0]:
+        raise ValueError("A and B must be 3-D with equal batch sizes")
+    batch, M, _ = A.shape
+    N = B.shape[2]
+    C = np.zeros((batch, M, N), dtype=np.float32)
+    Cd = np.zeros((batch, M, N), dtype=np.float64) if want_f64 else None
+    ABS = np.zeros((batch, M, N), dtype=np.float64) if want_f64 else None
+    for b in range(batch):
+        c, cd, ab = gemm(A[b], B[b], want_f64=want_f64)
+        C[b] = c
+        if want_f64:
+            Cd[b] = cd
+            ABS[b] = ab
+    return C, Cd, ABS

@@ -346,3 +346,54 @@ def run_all_ex(fn_ex):
     for p in EX_PINS:
         errs += p(fn_ex)
     return errs
+
+
+# --- strided batch (gemm_batched contract: fn_b(A3, B3) -> (C, Cd, ABS)) ---------
+
+def _ints3(batch, rows, cols, seed):
+    return np.stack([_ints(rows, cols, seed + b) for b in range(batch)])
+
+
+def pin_batched_integer_einsum(fn_b):
+    """Integer batches against an int64 einsum (a library routine, exact):
+    C, the binary64 sums and sum|a||b| all equal it exactly, for distinct
+    matrices and for one A or one B shared by the batch (stride 0)."""
+    errs = []
+    for (bt, m, n, k, seed) in [(5, 7, 9, 11, 900), (3, 1, 33, 70, 910), (4, 16, 5, 1, 920)]:
+        A, B = _ints3(bt, m, k, seed), _ints3(bt, k, n, seed + 50)
+        cases = [("distinct", A, B),
+                 ("shared A", np.broadcast_to(A[0], A.shape), B),
+                 ("shared B", A, np.broadcast_to(B[0], B.shape))]
+        for what, Aa, Bb in cases:
+            want = np.einsum("bik,bkj->bij", Aa.astype(np.int64), Bb.astype(np.int64))
+            mag = np.einsum("bik,bkj->bij", np.abs(Aa).astype(np.int64),
+                            np.abs(Bb).astype(np.int64))
+            C, Cd, ABS = fn_b(Aa, Bb)
+            if C.shape != want.shape or not np.array_equal(C, want.astype(np.float32)):
+                errs += _fail("batched-int", f"{what} {bt}x{m}x{n}x{k}: C != int64 einsum")
+            elif not (np.array_equal(Cd, want.astype(np.float64)) and
+                      np.array_equal(ABS, mag.astype(np.float64))):
+                errs += _fail("batched-int", f"{what} {bt}x{m}x{n}x{k}: Cd or ABS inexact")
+    return errs
+
+
+def pin_batched_products_independent(fn_b):
+    """A NaN in one product's A reaches only that product's rows; the others
+    keep their exact values (products share nothing)."""
+    A, B = _ints3(4, 6, 8, 940).astype(np.float32), _ints3(4, 8, 5, 950).astype(np.float32)
+    A = A.copy()
+    A[2, 3, 4] = np.nan
+    C, _, _ = fn_b(A, B)
+    want = np.einsum("bik,bkj->bij", A.astype(np.float64), B.astype(np.float64))
+    bad = np.isnan(C)
+    expect_bad = np.zeros_like(bad)
+    expect_bad[2, 3, :] = True
+    if not np.array_equal(bad, expect_bad):
+        return _fail("batched-independent", "NaN spread beyond its product's row")
+    ok = ~expect_bad
+    if not np.array_equal(C[ok], want[ok].astype(np.float32)):
+        return _fail("batched-independent", "products other than the NaN one changed")
+    return []
+
+
+BATCHED_PINS = [pin_batched_integer_einsum, pin_batched_products_independent]

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert binding.gemm_f32_version() == 2
+    assert binding.gemm_f32_version() == 3
 
 
 def test_status_strings():
@@ -231,3 +231,55 @@ def test_ex_alias_uses_the_stored_extent():
 def test_kernel_names_are_unique():
     names = binding.kernel_names()
     assert len(names) == len(set(names)), [n for n in names if names.count(n) > 1][:5]
+
+
+# ---- strided batch (gemm_f32_batched) -------------------------------------------
+
+def _batched(M, N, K, A, lda, sa, B, ldb, sb, C, ldc, sc, batch):
+    return binding.gemm_f32_batched(M, N, K, A, lda, sa, B, ldb, sb, C, ldc, sc, batch, 0)
+
+
+def test_batched_argument_errors_before_any_device_call():
+    big = 1 << 28
+    # negative batch; negative strides
+    assert _batched(4, 4, 4, P16, 4, 16, Q16, 4, 16, R16, 4, 16, -1) == 1
+    assert _batched(4, 4, 4, P16, 4, -16, Q16, 4, 16, R16, 4, 16, 2) == 2
+    assert _batched(4, 4, 4, P16, 4, 16, Q16, 4, -16, R16, 4, 16, 2) == 2
+    assert _batched(4, 4, 4, P16, 4, 16, Q16, 4, 16, R16, 4, -16, 2) == 2
+    # the per-product checks still apply
+    assert _batched(4, 4, 4, P16, 3, 16, Q16, 4, 16, R16, 4, 16, 2) == 2
+    assert _batched(4, 4, 4, 0, 4, 16, Q16, 4, 16, R16, 4, 16, 2) == 3
+    # C windows of two products overlap (stride shorter than one window)
+    assert _batched(4, 4, 4, P16, 4, 16, Q16, 4, 16, R16, 4, 15, 2) == 4
+    # the second product's C runs into the batch of A (A stride 0 is fine)
+    assert _batched(4, 4, 4, P16, 4, 16, Q16, 4, 0, P16 + 4 * 16 * 4, 4, 16, 8) == 4
+    # strides too large for 64-bit extents
+    assert _batched(4, 4, 4, P16, 4, big * big, Q16, 4, 16, R16, 4, 16, 1 << 20) == 2
+
+
+def test_batched_empty_and_single():
+    # batch 0, M or N 0: successful no-ops with no device
+    assert _batched(4, 4, 4, P16, 4, 16, Q16, 4, 16, R16, 4, 16, 0) == 0
+    assert _batched(0, 4, 4, P16, 4, 16, Q16, 4, 16, R16, 4, 16, 3) == 0
+    assert _batched(4, 0, 4, P16, 4, 16, Q16, 1, 16, R16, 1, 16, 3) == 0
+
+
+def test_batched_selection():
+    sel = binding.gemm_f32_selected_kernel_batched
+    names = binding.kernel_names()
+    # batch 1 is gemm_f32
+    for (M, N, K) in [(4096, 4096, 4096), (8, 8192, 8192), (512, 512, 512)]:
+        assert sel(M, N, K, K, M * K, N, K * N, N, 1, P16, Q16) == \
+            binding.gemm_f32_selected_kernel(M, N, K, K, N, N, P16, Q16, R16)
+    # a batch: whole-K MFMA kernels only (no K split, no skinny kernel), sized
+    # by the tiles of the whole batch
+    for (M, N, K, bt) in [(512, 512, 512, 64), (8, 8192, 8192, 4), (64, 64, 64, 1000),
+                          (1000, 999, 777, 3), (256, 256, 256, 100000)]:
+        name = sel(M, N, K, K, M * K, N, K * N, N, bt, P16, Q16)
+        assert name in names and name.startswith("mfma_") and "_sk_" not in name, name
+    # direct-to-LDS kernels need every product 16-byte aligned: strides % 4
+    assert "_d6_" in sel(512, 512, 512, 512, 512 * 512, 512, 512 * 512, 512, 64, P16, Q16)
+    odd = sel(512, 512, 512, 512, 512 * 512 + 1, 512, 512 * 512, 512, 64, P16, Q16)
+    assert odd.startswith("mfma_") and "_d6_" not in odd, odd
+    assert sel(4, 4, 4, 4, -1, 4, 16, 4, 2, P16, Q16) == "invalid"
+    assert sel(4, 4, 4, 4, 16, 4, 16, 4, -2, P16, Q16) == "invalid"

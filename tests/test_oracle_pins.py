@@ -205,3 +205,43 @@ def test_ex_correct_variant_passes_all_pins():
 def test_ex_pins_catch_planted_mistake(mistake):
     errs = pins.run_all_ex(_ex_variant(mistake))
     assert errs, f"no pin caught the planted mistake {mistake!r}"
+
+
+# ---- strided batch ------------------------------------------------------------
+
+def oracle_batched_fn(A, B):
+    return oracle.gemm_batched(A, B)
+
+
+@pytest.mark.parametrize("pin", pins.BATCHED_PINS, ids=lambda p: p.__name__)
+def test_oracle_batched_passes_pin(pin):
+    errs = pin(oracle_batched_fn)
+    assert not errs, "\n".join(errs)
+
+
+def _batched_variant(mistake):
+    """Batched oracle-like function with one planted mistake."""
+    def fn(A, B):
+        bt = A.shape[0]
+        out = [oracle.gemm(A[0] if mistake == "first_a_only" else A[b],
+                           B[min(b + 1, bt - 1)] if mistake == "shifted_b" else B[b])
+               for b in range(bt)]
+        C = np.stack([o[0] for o in out])
+        Cd = np.stack([o[1] for o in out])
+        ABS = np.stack([o[2] for o in out])
+        if mistake == "running_sum":
+            C, Cd, ABS = (np.cumsum(C, axis=0, dtype=np.float32), np.cumsum(Cd, axis=0),
+                          np.cumsum(ABS, axis=0))
+        return C, Cd, ABS
+    return fn
+
+
+BATCHED_MISTAKES = ["first_a_only", "shifted_b", "running_sum"]
+
+
+@pytest.mark.parametrize("mistake", BATCHED_MISTAKES)
+def test_batched_pins_catch_planted_mistake(mistake):
+    errs = []
+    for pin in pins.BATCHED_PINS:
+        errs += pin(_batched_variant(mistake))
+    assert errs, f"no batched pin caught the planted mistake {mistake!r}"
