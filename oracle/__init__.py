@@ -1,4 +1,5 @@
-"""CPU oracle for dense row-major fp32 ``C = A x B`` (binary64 accumulation).
+"""CPU oracle for dense row-major fp32 ``C = A x B`` and for the sum of an
+fp32 array (binary64 accumulation).
 
 TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only ``tests/``,
 ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
@@ -64,6 +65,9 @@ def _load():
                                           f32p, i64, f32p, i64, f32, f32p, i64,
                                           f32p, i64, f64p, i64, f64p, i64]
     lib.oracle_gemm_ex_f64acc.restype = ctypes.c_int
+    lib.oracle_sum_f64acc.argtypes = [i64, f32p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    lib.oracle_sum_f64acc.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_version.restype = ctypes.c_int
@@ -218,3 +222,20 @@ def gemm_batched(A: np.ndarray, B: np.ndarray, *, want_f64: bool = True):
             Cd[b] = cd
             ABS[b] = ab
     return C, Cd, ABS
+
+
+def sum_f32(x: np.ndarray):
+    """Return ``(s, sd, abs)`` for the sum of a 1-D float32 array: the binary32
+    rounding of the ascending-order binary64 sum, that sum, and sum |x[i]|.
+    Definition: ``oracle_sum_f64acc`` in ``gemm_oracle.c``."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim != 1:
+        raise ValueError("x must be 1-D")
+    s = ctypes.c_float(0.0)
+    sd = ctypes.c_double(0.0)
+    ab = ctypes.c_double(0.0)
+    rc = _load().oracle_sum_f64acc(x.size, x.ctypes.data if x.size else None,
+                                   ctypes.byref(s), ctypes.byref(sd), ctypes.byref(ab))
+    if rc != 0:
+        raise RuntimeError(f"oracle_sum_f64acc failed with status {rc}")
+    return np.float32(s.value), sd.value, ab.value

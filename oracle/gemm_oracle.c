@@ -1,5 +1,6 @@
 /*
- * gemm_oracle.c -- the CPU oracle for dense row-major fp32 C = A x B.
+ * gemm_oracle.c -- the CPU oracle for dense row-major fp32 C = A x B (and
+ * for the sum of an fp32 array, at the end of this file).
  *
  * TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only the test suite,
  * the smoke check and the benchmark's CPU-baseline leg may load this
@@ -236,4 +237,31 @@ int oracle_gemm_ex_f64acc(int transA, int transB, int64_t M, int64_t N, int64_t 
     free(mag);
   }
   return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/*
+ * oracle_sum_f64acc -- the sum of n binary32 values.
+ *
+ * The reduction of "GPU compute shaders" (How it works: one partial sum per
+ * group, then the partials combined) computes the plain sum of the array; a
+ * rerun gives the same bits only when the group count and the order are
+ * fixed (its Pitfalls).  Here the definition itself, written out: x[0] +
+ * x[1] + ... + x[n-1] in ascending index order in binary64, rounded once to
+ * binary32.  *sum_f64 is the binary64 sum before rounding, *abs_f64 the sum
+ * of |x[i]| (the tolerance scale).  n = 0 gives +0.0.  Serial, so the result
+ * is one fixed order.
+ */
+int oracle_sum_f64acc(int64_t n, const float *x, float *sum_f32, double *sum_f64,
+                      double *abs_f64) {
+  if (n < 0 || (n > 0 && !x) || !sum_f32) return ORACLE_BAD_ARG;
+  double s = 0.0, a = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    const double v = (double)x[i];
+    s += v;
+    a += fabs(v);
+  }
+  *sum_f32 = (float)s;
+  if (sum_f64) *sum_f64 = s;
+  if (abs_f64) *abs_f64 = a;
+  return ORACLE_OK;
 }

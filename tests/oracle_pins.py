@@ -397,3 +397,76 @@ def pin_batched_products_independent(fn_b):
 
 
 BATCHED_PINS = [pin_batched_integer_einsum, pin_batched_products_independent]
+
+
+# --- sum of an fp32 array (sum contract: fn_s(x) -> (s_f32, s_f64, abs_f64)) ------
+
+def pin_sum_closed_forms(fn_s):
+    """Sums with a closed form, exact in binary64 and in the binary32 result:
+    0 + 1 + ... + (n-1) = n(n-1)/2, n ones = n, the empty sum = +0.0, and the
+    cancellation 1e8 + 1 - 1e8 = 1 (lost by a binary32 running sum)."""
+    errs = []
+    for n in (1, 2, 7, 1000, 4097):
+        s, sd, ab = fn_s(np.arange(n, dtype=np.float32))
+        if sd != n * (n - 1) / 2 or s != np.float32(n * (n - 1) / 2) or ab != sd:
+            errs += _fail("sum-arange", f"n={n}: got {sd}")
+        s, sd, _ = fn_s(np.ones(n, dtype=np.float32))
+        if sd != n or s != n:
+            errs += _fail("sum-ones", f"n={n}: got {sd}")
+    s, sd, ab = fn_s(np.zeros(0, dtype=np.float32))
+    if not (s == 0 and not np.signbit(s) and sd == 0 and ab == 0):
+        errs += _fail("sum-empty", f"got {s}")
+    s, sd, _ = fn_s(np.array([1e8, 1.0, -1e8], dtype=np.float32))
+    if sd != 1.0 or s != 1.0:
+        errs += _fail("sum-cancel", f"1e8 + 1 - 1e8 gave {sd}")
+    return errs
+
+
+def pin_sum_integer_int64(fn_s):
+    """Integer arrays against an int64 sum (a library routine, exact)."""
+    errs = []
+    for n, seed in [(1, 960), (3, 961), (1000, 962), (2 ** 20 + 3, 963)]:
+        x = _ints(1, n, seed).reshape(-1)
+        want = int(x.astype(np.int64).sum())
+        s, sd, ab = fn_s(x)
+        if sd != want or s != np.float32(want) or ab != float(np.abs(x).astype(np.int64).sum()):
+            errs += _fail("sum-int", f"n={n}: got {sd}, want {want}")
+    return errs
+
+
+def pin_sum_fsum(fn_s):
+    """Float arrays against math.fsum (the correctly rounded exact sum, a
+    library routine): the binary64 sum within n 2^-53 sum|x| of it, and the
+    binary32 result its rounding (within half an ulp plus that bound)."""
+    import math
+    errs = []
+    for n, seed in [(10, 970), (12345, 971), (2 ** 18, 972)]:
+        x = _np(inputs.draw_matrix(1, n, "normal", seed)).reshape(-1)
+        exact = math.fsum(x.astype(np.float64))
+        s, sd, ab = fn_s(x)
+        if abs(sd - exact) > n * 2.0 ** -53 * ab:
+            errs += _fail("sum-fsum", f"n={n}: binary64 sum {sd} vs fsum {exact}")
+        if abs(float(s) - exact) > 2.0 ** -24 * abs(exact) + n * 2.0 ** -53 * ab:
+            errs += _fail("sum-fsum", f"n={n}: binary32 result {s} vs fsum {exact}")
+        if abs(ab - math.fsum(np.abs(x).astype(np.float64))) > n * 2.0 ** -53 * ab:
+            errs += _fail("sum-fsum", f"n={n}: sum |x| wrong")
+    return errs
+
+
+def pin_sum_special_values(fn_s):
+    """IEEE propagation: one NaN makes the sum NaN, Inf stays Inf, Inf - Inf is NaN."""
+    x = _np(inputs.draw_matrix(1, 100, "u11", 980)).reshape(-1).copy()
+    errs = []
+    y = x.copy(); y[57] = np.nan
+    if not np.isnan(fn_s(y)[0]):
+        errs += _fail("sum-nan", "NaN did not propagate")
+    y = x.copy(); y[3] = np.inf
+    if fn_s(y)[0] != np.inf:
+        errs += _fail("sum-inf", "Inf lost")
+    y[90] = -np.inf
+    if not np.isnan(fn_s(y)[0]):
+        errs += _fail("sum-inf", "Inf - Inf is not NaN")
+    return errs
+
+
+SUM_PINS = [pin_sum_closed_forms, pin_sum_integer_int64, pin_sum_fsum, pin_sum_special_values]

@@ -245,3 +245,44 @@ def test_batched_pins_catch_planted_mistake(mistake):
     for pin in pins.BATCHED_PINS:
         errs += pin(_batched_variant(mistake))
     assert errs, f"no batched pin caught the planted mistake {mistake!r}"
+
+
+# ---- sum of an fp32 array -------------------------------------------------------
+
+@pytest.mark.parametrize("pin", pins.SUM_PINS, ids=lambda p: p.__name__)
+def test_oracle_sum_passes_pin(pin):
+    errs = pin(oracle.sum_f32)
+    assert not errs, "\n".join(errs)
+
+
+def _sum_variant(mistake):
+    """Sum-oracle-like function with one planted mistake."""
+    def fn(x):
+        x = np.asarray(x, dtype=np.float32)
+        if mistake == "drop_last":
+            x = x[:-1]
+        if mistake == "skip_first":
+            x = x[1:]
+        if mistake == "fp32_accumulate":
+            acc = np.float32(0.0)
+            for v in x:
+                acc = np.float32(acc + v)
+            sd = float(acc)
+        else:
+            sd = float(np.sum(x.astype(np.float64)))
+        ab = abs(sd) if mistake == "abs_of_sum" else float(np.sum(np.abs(x).astype(np.float64)))
+        if mistake == "double_first" and x.size:
+            sd += float(x[0])
+        return np.float32(sd), sd, ab
+    return fn
+
+
+SUM_MISTAKES = ["drop_last", "skip_first", "fp32_accumulate", "abs_of_sum", "double_first"]
+
+
+@pytest.mark.parametrize("mistake", SUM_MISTAKES)
+def test_sum_pins_catch_planted_mistake(mistake):
+    errs = []
+    for pin in pins.SUM_PINS:
+        errs += pin(_sum_variant(mistake))
+    assert errs, f"no sum pin caught the planted mistake {mistake!r}"
