@@ -87,6 +87,63 @@ def traffic_for(kernel_name: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def launch_amortisation(stream, steps, warmup, batch=64, n=512):
+    """Many small products (batch x 512^3, the pages' N = 512 size): per-product
+    time for separate gemm_f32 calls, one gemm_f32_batched call, and a HIP
+    graph replaying the separate calls.  Event-timed on the launch stream."""
+    import torch
+    from dense_fp32_gemm_f32_amd import binding, inputs
+    A = torch.stack([inputs.draw_matrix(n, n, "u11", 1100 + b) for b in range(batch)]).cuda()
+    B = torch.stack([inputs.draw_matrix(n, n, "u11", 1200 + b) for b in range(batch)]).cuda()
+    C = torch.empty((batch, n, n), device="cuda")
+    flops = 2.0 * n * n * n * batch
+
+    def separate(_i):
+        for b in range(batch):
+            binding.gemm(A[b], B[b], C[b])
+
+    def batched(_i):
+        binding.gemm_batched(A, B, C)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        separate(0)   # the split-K workspace of the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        separate(0)
+    torch.cuda.synchronize()
+
+    out = {"products": batch, "M": n, "N": n, "K": n,
+           "kernel_separate": binding.selected_kernel(A[0], B[0]),
+           "kernel_batched": binding.selected_kernel_batched(A, B, C)}
+    for name, fn in (("separate_calls", separate), ("one_batched_call", batched),
+                     ("graph_of_separate_calls", lambda _i: g.replay())):
+        _, per = time_launches(fn, steps, warmup, stream)
+        mean_ms = sum(per) / len(per)
+        out[name] = {"us_per_product": round(mean_ms * 1e3 / batch, 3),
+                     "TFLOP/s": round(flops / (mean_ms * 1e-3) / 1e12, 2)}
+    return out
+
+
+def sum_bandwidth(stream, steps, warmup, n=2 ** 26, copies=4):
+    """reduce_sum_f32 on 2^26 floats (the pages' reduction size), rotating 4
+    copies (1 GiB > the 256 MB last-level cache) so it streams from HBM."""
+    import torch
+    from dense_fp32_gemm_f32_amd import binding, inputs
+    xs = [inputs.draw_matrix(1, n, "u11", 1300 + c).reshape(-1).cuda() for c in range(copies)]
+    out = torch.empty(1, device="cuda")
+    _, per = time_launches(lambda i: binding.reduce_sum(xs[i % copies], out), steps, warmup,
+                           stream)
+    mean_ms = sum(per) / len(per)
+    gbs = 4.0 * n / (mean_ms * 1e-3) / 1e9
+    return {"n": n, "launch_us_mean": round(mean_ms * 1e3, 2),
+            "launch_us_min": round(min(per) * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
 def cpu_baseline(w, target_s):
     """The oracle on the first R rows of A; R sized from a short probe."""
     import numpy as np
@@ -267,6 +324,12 @@ def main():
                          "traffic": traffic_for(sk)}}}
         del As, Bs, Cs
         torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        result.setdefault("secondary", {})["batched_64x512"] = launch_amortisation(
+            stream, max(args.steps, 20), args.warmup)
+        result["secondary"]["sum_2^26"] = sum_bandwidth(stream, max(args.steps, 20),
+                                                        args.warmup)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

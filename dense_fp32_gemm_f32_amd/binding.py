@@ -31,7 +31,7 @@ EXPORTS = ["gemm_f32", "gemm_f32_ex", "gemm_f32_ref_gpu", "gemm_f32_status_strin
            "gemm_f32_selected_kernel", "gemm_f32_selected_kernel_ex", "gemm_f32_version",
            "gemm_f32_kernel_count", "gemm_f32_kernel_name", "gemm_f32_run_kernel",
            "gemm_f32_run_kernel_ex", "gemm_f32_release_workspaces", "gemm_f32_batched",
-           "gemm_f32_selected_kernel_batched"]
+           "gemm_f32_selected_kernel_batched", "reduce_sum_f32"]
 
 
 class GemmError(RuntimeError):
@@ -82,6 +82,8 @@ def load():
     lib.gemm_f32_kernel_name.restype = ctypes.c_char_p
     lib.gemm_f32_release_workspaces.argtypes = []
     lib.gemm_f32_release_workspaces.restype = ctypes.c_int
+    lib.reduce_sum_f32.argtypes = [i64, vp, vp, vp]
+    lib.reduce_sum_f32.restype = ctypes.c_int
     lib.gemm_f32_batched.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64,
                                      i64, vp]
     lib.gemm_f32_batched.restype = ctypes.c_int
@@ -125,6 +127,10 @@ def gemm_f32_selected_kernel_batched(M, N, K, lda, strideA, ldb, strideB, ldc, b
                                      B=0) -> str:
     return load().gemm_f32_selected_kernel_batched(M, N, K, lda, strideA, ldb, strideB, ldc,
                                                    batch, A, B).decode()
+
+
+def reduce_sum_f32(n, x, out, stream=0) -> int:
+    return load().reduce_sum_f32(n, x, out, stream)
 
 
 def gemm_f32_ref_gpu(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
@@ -272,6 +278,24 @@ def gemm_batched(A, B, C=None):
 def selected_kernel_batched(A, B, C=None) -> str:
     (M, N, K, a, lda, sa, b, ldb, sb, _c, ldc, _sc, batch, _s), _ = _args_batched(A, B, C)
     return gemm_f32_selected_kernel_batched(M, N, K, lda, sa, ldb, sb, ldc, batch, a, b)
+
+
+def reduce_sum(x, out=None):
+    """Sum of a 1-D contiguous float32 GPU tensor into a 1-element tensor
+    (returned), in an order fixed by the length."""
+    import torch
+    if x.dtype != torch.float32 or x.dim() != 1 or (x.numel() > 1 and x.stride(0) != 1):
+        raise TypeError("x must be a contiguous 1-D float32 tensor")
+    if x.device.type != "cuda":
+        raise TypeError(f"x must be on a GPU (got {x.device})")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    with _device(x):
+        rc = reduce_sum_f32(x.numel(), x.data_ptr(), out.data_ptr(), stream)
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc, "reduce_sum_f32")
+    return out
 
 
 def _args_ex(A, B, C, trans_a, trans_b):

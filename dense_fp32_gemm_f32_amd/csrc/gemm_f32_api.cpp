@@ -568,6 +568,31 @@ const char* gemm_f32_selected_kernel_batched(int64_t M, int64_t N, int64_t K, in
   return idx < 0 ? "invalid" : entries()[idx].name.c_str();
 }
 
+int reduce_sum_f32(int64_t n, const float* x, float* out, void* stream) {
+  if (n < 0 || n > (INT64_C(1) << 60)) return GEMM_F32_ERR_INVALID_DIM;
+  if ((n > 0 && !x) || !out) return GEMM_F32_ERR_NULL_PTR;
+  if ((n > 0 && !aligned4(x)) || !aligned4(out)) return GEMM_F32_ERR_POINTER;
+  if (n > 0) {
+    const uintptr_t x0 = (uintptr_t)x, x1 = x0 + (uintptr_t)(n * 4), o = (uintptr_t)out;
+    if (o + 4 > x0 && o < x1) return GEMM_F32_ERR_ALIAS;
+  }
+  int dev = -1;
+  int rc = check_device(&dev);
+  if (rc != GEMM_F32_OK) return rc;
+  if (n > 0 && (rc = check_pointer(x, dev)) != GEMM_F32_OK) return rc;
+  if ((rc = check_pointer(out, dev)) != GEMM_F32_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const gemmf32::ReducePlan pl = gemmf32::plan_reduce(n);
+  float* part = nullptr;
+  if (pl.groups > 0 && (rc = get_workspace(dev, s, (size_t)pl.groups, &part)) != GEMM_F32_OK)
+    return rc;
+  if (gemmf32::launch_reduce_sum(n, x, out, part, s) != hipSuccess) {
+    (void)hipGetLastError();
+    return GEMM_F32_ERR_LAUNCH;
+  }
+  return GEMM_F32_OK;
+}
+
 int gemm_f32_ref_gpu(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                      const float* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
   const Op op;

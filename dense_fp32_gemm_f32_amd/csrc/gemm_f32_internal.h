@@ -110,6 +110,16 @@ const SkinnyVariant& skinny_rows_variant(int i);
 hipError_t launch_combine(const Problem& p, int slices, const float* partials, hipStream_t s,
                           float alpha = 1.f, float beta = 0.f);
 
+// ---- deterministic sum of an fp32 array ------------------------------------
+// Pass 1: `groups` workgroups, group g sums x[g*chunk, min(n, (g+1)*chunk))
+// into part[g]; pass 2 adds the partials into *out.  Both depend on n only.
+struct ReducePlan {
+  int groups = 0;      // 0 for n == 0 (pass 2 alone writes +0.0)
+  int64_t chunk = 0;   // elements per group, a multiple of 4
+};
+ReducePlan plan_reduce(int64_t n);
+hipError_t launch_reduce_sum(int64_t n, const float* x, float* out, float* part, hipStream_t s);
+
 // ---- naive reference and the K == 0 fill ----------------------------------
 hipError_t launch_ref(const Problem& p, hipStream_t s);
 // C = beta * C over the M x N window (C = +0.0 when beta == 0; C not read then)

@@ -163,6 +163,32 @@ int gemm_f32_ref_gpu(int64_t M, int64_t N, int64_t K,
                      float *C, int64_t ldc,
                      void *stream);
 
+/*
+ * reduce_sum_f32 -- *out = x[0] + x[1] + ... + x[n-1] for n fp32 values in
+ * device memory, summed in fp32 in an order that depends on n only, so the
+ * same array gives bitwise the same result on every run and at any address.
+ *
+ * The reduction of "GPU compute shaders" (How it works: one partial sum per
+ * workgroup from a grid-stride loop and a shared-memory tree, then the
+ * partials combined; the Pitfalls section's fixed group count and order for
+ * a reproducible result), measured there on 2^26 values.  Two launches: up to
+ * 256 workgroups each sum a contiguous chunk into the workspace, then one
+ * workgroup adds those partials and writes *out.  The error is at most about
+ * d 2^-24 sum|x[i]|, with d the depth of the summation tree (276 for n =
+ * 2^26; d grows as n / 2^18 beyond that); exact when every partial sum is
+ * an integer below 2^24 in magnitude.  n == 0 writes +0.0.  NaN and Inf
+ * propagate as IEEE addition does.
+ *
+ * x: n floats (4-byte aligned; 16-byte aligned reads at full width); out: one
+ * float, not inside x.  Both device memory of the current device, caller
+ * owned.  Errors: n < 0 GEMM_F32_ERR_INVALID_DIM; NULL x (n > 0) or out
+ * GEMM_F32_ERR_NULL_PTR; misaligned or unreachable pointers
+ * GEMM_F32_ERR_POINTER; out inside x GEMM_F32_ERR_ALIAS; then the device and
+ * workspace checks of gemm_f32 (it shares the per-stream workspace).
+ * Asynchronous on `stream` like gemm_f32.
+ */
+int reduce_sum_f32(int64_t n, const float *x, float *out, void *stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *gemm_f32_status_string(int status);
 

@@ -16,7 +16,7 @@ HEADER = ROOT / "include" / "gemm_f32.h"
 def declared_functions():
     text = HEADER.read_text()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gemm_f32\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:gemm|reduce_sum)_f32\w*)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -283,3 +283,17 @@ def test_batched_selection():
     assert odd.startswith("mfma_") and "_d6_" not in odd, odd
     assert sel(4, 4, 4, 4, -1, 4, 16, 4, 2, P16, Q16) == "invalid"
     assert sel(4, 4, 4, 4, 16, 4, 16, 4, -2, P16, Q16) == "invalid"
+
+
+# ---- deterministic sum (reduce_sum_f32) ------------------------------------------
+
+def test_reduce_sum_argument_errors_before_any_device_call():
+    f = binding.reduce_sum_f32
+    assert f(-1, P16, R16, 0) == 1
+    assert f(10, 0, R16, 0) == 3
+    assert f(10, P16, 0, 0) == 3
+    assert f(0, 0, 0, 0) == 3            # out is always written
+    assert f(10, P16 + 2, R16, 0) == 9
+    assert f(10, P16, R16 + 1, 0) == 9
+    assert f(10, P16, P16 + 36, 0) == 4  # out is the last element of x
+    assert f(10, P16, P16 + 40, 0) != 4  # right after x: not an alias
