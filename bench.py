@@ -39,8 +39,8 @@ PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -82,7 +82,7 @@ def traffic_for(kernel_name: str):
     except ValueError:
         return None
     from dense_fp32_gemm_f32_amd.prof_summary import source_hash
-    if not rec or rec.get("source_sha256") != source_hash():
+    if not rec or rec.get("source_sha256") != source_hash(kernel_name):
         return None
     return rec.get("hbm_bytes_per_launch")
 

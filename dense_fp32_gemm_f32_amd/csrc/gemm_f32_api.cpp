@@ -319,6 +319,15 @@ int run_entry(const Entry& e, const Op& op, const Problem& p, int dev, hipStream
 }
 
 // ---- the dispatcher ---------------------------------------------------------
+// Do the workgroups of an MFMA entry (over `batch` products) fill whole waves
+// of the CUs, or at least four waves?
+bool fills_whole_waves(const Entry& e, int64_t M, int64_t N, int64_t batch) {
+  if (e.kind != Kind::Mfma && e.kind != Kind::MfmaSplitK) return true;
+  const auto& v = gemmf32::mfma_variant(e.sub);
+  const int64_t wgs = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn) * batch;
+  return wgs % gemmf32::kNumCus == 0 || wgs >= 4 * gemmf32::kNumCus;
+}
+
 std::string select_name(const Op& op, int64_t M, int64_t N, int64_t K, int64_t lda,
                         int64_t ldb, const void* A, const void* B) {
   if (M == 0 || N == 0) return "empty";
@@ -340,7 +349,9 @@ std::string select_name(const Op& op, int64_t M, int64_t N, int64_t K, int64_t l
     if (M > row.max_m || tiles < row.min_tiles) continue;
     // a row whose kernel cannot take these arguments defers to the next one
     const int idx = find_entry(row.kernel);
-    if (idx >= 0 && accepts(entries()[idx], op, M, N, K, lda, ldb, A, B)) return row.kernel;
+    if (idx < 0 || !accepts(entries()[idx], op, M, N, K, lda, ldb, A, B)) continue;
+    if (row.whole_waves && !fills_whole_waves(entries()[idx], M, N, 1)) continue;
+    return row.kernel;
   }
   return "ref_naive";
 }
@@ -475,6 +486,7 @@ std::string select_name_batched(int64_t M, int64_t N, int64_t K, int64_t lda, in
     if (!accepts(entries()[idx], Op{}, M, N, K, lda, ldb, A, B)) continue;
     if (gemmf32::mfma_variant(entries()[idx].sub).lds_dma && (bt.sa % 4 != 0 || bt.sb % 4 != 0))
       continue;
+    if (row.whole_waves && !fills_whole_waves(entries()[idx], M, N, bt.count)) continue;
     return row.kernel;
   }
   // the rows above always end in a kernel that takes any operands

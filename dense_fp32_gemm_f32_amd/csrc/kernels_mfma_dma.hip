@@ -310,6 +310,10 @@ const MfmaVariant kDmaVariants[] = {
     GEMMF32_MFMA_DMA(128, 64, 64, 64, 32, 2),
     GEMMF32_MFMA_DMA(64, 64, 32, 32, 32, 4),
     GEMMF32_MFMA_DMA(64, 64, 64, 32, 32, 2),
+    GEMMF32_MFMA_DMA(256, 256, 16, 128, 64, 1),
+    GEMMF32_MFMA_DMA(256, 256, 16, 64, 128, 1),
+    GEMMF32_MFMA_DMA(256, 256, 32, 128, 64, 1),
+    GEMMF32_MFMA_DMA(256, 256, 32, 64, 128, 1),
 };
 
 }  // namespace

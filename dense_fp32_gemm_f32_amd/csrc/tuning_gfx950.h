@@ -8,19 +8,25 @@
 // dense_fp32_gemm_f32_amd/tune.py.
 //
 // Columns:
-//   max_m       the row applies when M <= max_m
-//   min_tiles   ... and the grid of 128 x 128 tiles has at least this many tiles
-//   kernel      a name in the kernel table
+//   max_m        the row applies when M <= max_m
+//   min_tiles    ... and the grid of 128 x 128 tiles has at least this many tiles
+//   kernel       a name in the kernel table
+//   whole_waves  ... and (if set) the kernel's own workgroups fill whole waves of
+//                the 256 CUs (a multiple of 256, or at least 4 waves), so a
+//                large tile leaves no part-empty last wave
 #pragma once
 
 #include <cstdint>
 
 namespace gemmf32 {
 
+constexpr int64_t kNumCus = 256;   // MI355X
+
 struct TuningRow {
   int64_t max_m;
   int64_t min_tiles;
   const char* kernel;
+  bool whole_waves = false;
 };
 
 constexpr int64_t kAnyM = INT64_C(0x7fffffff);
@@ -30,6 +36,8 @@ constexpr TuningRow kTuningGfx950[] = {
     // streamed in KiB row runs (8 x 28672 x 4096: 81 us against 92 us)
     {8, 160, "skinnyr_c2_r4_u4_m2x4_s0_nn"},
     {16, 0, "skinny_w8_c4_u4_s0_vec"},
+    // 256 x 256 tiles, 8 waves of 64 x 128 (4096^3: 939 us against 958 us)
+    {kAnyM, 768, "mfma_256x256x32_w64x128_d6_vec", true},
     {kAnyM, 768, "mfma_128x256x16_w64x128_d6_vec"},
     {kAnyM, 768, "mfma_256x128x16_w128x64_p5_vec"},
     {kAnyM, 192, "mfma_128x128x16_w64x64_d6_vec"},

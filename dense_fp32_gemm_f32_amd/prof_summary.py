@@ -28,11 +28,42 @@ ROOT = Path(__file__).resolve().parent.parent
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
-def source_hash() -> str:
+def kernel_sources(kernel: str | None = None) -> list[str]:
+    """The source files a table kernel is compiled from (every source when
+    the name is unknown or None)."""
+    csrc = ROOT / "dense_fp32_gemm_f32_amd" / "csrc"
+    every = sorted(p.name for p in csrc.glob("*"))
+    if not kernel:
+        return every
+    files = ["gemm_f32_internal.h"]
+    if kernel.startswith("mfmaex_"):
+        files += ["kernels_mfma_ex.hip", "mfma_common.h"]
+    elif kernel.startswith("mfma_"):
+        files += ["kernels_mfma_dma.hip" if "_d6_" in kernel else "kernels_mfma.hip",
+                  "mfma_common.h"]
+        if "_sk_" in kernel:
+            files.append("kernels_combine.hip")
+    elif kernel.startswith("skinnyr_"):
+        files += ["kernels_skinny_rows.hip", "kernels_combine.hip"]
+    elif kernel.startswith("skinnyt_"):
+        files += ["kernels_skinny_t.hip", "kernels_combine.hip", "mfma_common.h"]
+    elif kernel.startswith("skinny_"):
+        files += ["kernels_skinny.hip", "kernels_combine.hip"]
+    elif kernel.startswith("reduce_"):
+        files += ["kernels_reduce.hip"]
+    else:
+        return every
+    return sorted(files)
+
+
+def source_hash(kernel: str | None = None) -> str:
+    """Hash of the sources a kernel is built from: profiles record it, and a
+    recorded traffic figure is used only while the kernel's sources match."""
     h = hashlib.sha256()
-    for p in sorted((ROOT / "dense_fp32_gemm_f32_amd" / "csrc").glob("*")):
-        h.update(p.name.encode())
-        h.update(p.read_bytes())
+    csrc = ROOT / "dense_fp32_gemm_f32_amd" / "csrc"
+    for name in kernel_sources(kernel):
+        h.update(name.encode())
+        h.update((csrc / name).read_bytes())
     return h.hexdigest()
 
 
@@ -78,25 +109,65 @@ def mean(v):
     return sum(v) / len(v)
 
 
+def by_launch_shape(d: Path):
+    """Per (kernel, grid) dispatch durations of a --kernel-trace run: one kernel
+    template launched on several shapes (a 4096^3 product and a batch of
+    512^3 products, say) gets one row per grid."""
+    per = defaultdict(list)
+    with open(_find(d, "kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], f'{r["Grid_Size_X"]}x{r["Grid_Size_Y"]}x{r["Grid_Size_Z"]}',
+                   f'{r["Workgroup_Size_X"]}x{r["Workgroup_Size_Y"]}x{r["Workgroup_Size_Z"]}')
+            per[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return per
+
+
+def bench_summary(trace: Path, commands, out: Path):
+    """Markdown table of a bench.py kernel trace, split by launch shape."""
+    lines = ["# bench.py kernel trace (rocprofv3 --kernel-trace --stats)", "",
+             "Command (from the repository root on the MI355X box):", ""]
+    lines += [f"    {c}" for c in commands] + [""]
+    lines += ["Every dispatch of the run, warm-up included, grouped by kernel and grid "
+              "(grid sizes in threads).", "",
+              "| kernel | grid | workgroup | calls | avg us | min us | max us |",
+              "|---|---|---|---|---|---|---|"]
+    rows = sorted(by_launch_shape(trace).items(), key=lambda kv: -sum(kv[1]))
+    for (name, grid, wg), ds in rows:
+        if "gemmf32" not in name:
+            continue
+        short = name.replace("gemmf32::(anonymous namespace)::", "").replace("void ", "")
+        short = short.split("(")[0]
+        lines.append(f"| `{short}` | {grid} | {wg} | {len(ds)} | {sum(ds) / len(ds) / 1e3:.2f} "
+                     f"| {min(ds) / 1e3:.2f} | {max(ds) / 1e3:.2f} |")
+    Path(out).write_text("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("--workload", required=True)
-    ap.add_argument("--kernel", required=True, help="table name of the kernel")
-    ap.add_argument("--match", required=True, help="substring of the rocprof kernel name(s)")
-    ap.add_argument("--trace", required=True)
+    ap.add_argument("--bench-trace", help="summarise a bench.py --kernel-trace run instead")
+    ap.add_argument("--workload")
+    ap.add_argument("--kernel", help="table name of the kernel")
+    ap.add_argument("--match", help="substring of the rocprof kernel name(s)")
+    ap.add_argument("--trace")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--sq")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--skip", type=int, default=0,
                     help="leave out the first SKIP dispatches of each kernel from the durations")
-    ap.add_argument("--algo-bytes", type=float, required=True)
-    ap.add_argument("--flops", type=float, required=True)
+    ap.add_argument("--algo-bytes", type=float, default=0.0)
+    ap.add_argument("--flops", type=float, default=0.0)
     ap.add_argument("--mfma-cycles", type=int, default=0,
                     help="cycles one MFMA of the kernel occupies the pipe (32x32x2 f32: 64)")
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--out", required=True)
     args = ap.parse_args(argv)
+    if args.bench_trace:
+        bench_summary(Path(args.bench_trace), args.command, Path(args.out))
+        return
+    if not (args.workload and args.kernel and args.match and args.trace):
+        ap.error("--workload, --kernel, --match and --trace are required")
 
     lines = [f"# {args.kernel} on {args.workload}", ""]
     lines += ["Commands (from the repository root on the MI355X box):", ""]
@@ -172,7 +243,8 @@ def main(argv=None):
         tf = ROOT / "profiles" / "traffic.json"
         rec = json.loads(tf.read_text()) if tf.exists() else {}
         rec[args.kernel] = {"workload": args.workload, "hbm_bytes_per_launch": round(traffic),
-                            "algo_bytes": args.algo_bytes, "source_sha256": source_hash(),
+                            "algo_bytes": args.algo_bytes,
+                            "source_sha256": source_hash(args.kernel),
                             "summary": str(Path(args.out).name)}
         tf.write_text(json.dumps(rec, indent=1, sort_keys=True) + "\n")
     print("\n".join(lines))

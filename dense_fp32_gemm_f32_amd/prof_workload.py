@@ -25,6 +25,8 @@ def main(argv=None):
     ap.add_argument("--copies", type=int, default=0,
                     help="rotate this many input copies (0: 4 when B exceeds 128 MiB)")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--reduce", type=int, default=0,
+                    help="run reduce_sum_f32 on this many floats (4 copies) instead of a GEMM")
     args = ap.parse_args(argv)
 
     import torch
@@ -32,6 +34,17 @@ def main(argv=None):
 
     binding.load()
     dev = torch.device("cuda:0")
+    if args.reduce:
+        xs = [inputs.draw_matrix(1, args.reduce, "u11", 1300 + c).reshape(-1).to(dev)
+              for c in range(4)]
+        out = torch.empty(1, device=dev)
+        print(f"reduce_sum_f32 on {args.reduce} floats, {args.reps} launches over 4 copies",
+              flush=True)
+        for i in range(args.reps):
+            binding.reduce_sum(xs[i % 4], out)
+        torch.cuda.synchronize()
+        _calibration_copy(dev, args.copy_mib)
+        return 0
     w = inputs.WORKLOADS[args.workload]
     copies = args.copies or (4 if 4 * w.K * w.N > 128 * 2 ** 20 else 1)
     As, Bs, Cs = [], [], []
@@ -46,16 +59,19 @@ def main(argv=None):
     for i in range(args.reps):
         binding.run_kernel(name, As[i % copies], Bs[i % copies], Cs[i % copies])
     torch.cuda.synchronize()
+    _calibration_copy(dev, args.copy_mib)
+    return 0
 
-    n = args.copy_mib * 2 ** 20 // 4
+
+def _calibration_copy(dev, mib):
+    import torch
+    n = mib * 2 ** 20 // 4
     src = torch.ones(n, device=dev)
     dst = torch.empty(n, device=dev)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(f"calibration copy: 3 x {args.copy_mib} MiB read + {args.copy_mib} MiB written",
-          flush=True)
-    return 0
+    print(f"calibration copy: 3 x {mib} MiB read + {mib} MiB written", flush=True)
 
 
 if __name__ == "__main__":

@@ -107,7 +107,11 @@ def test_adjacent_but_not_overlapping_is_not_alias():
     (8, 28672, 4096, 4096, 28672, P16, Q16, "skinnyr_c2_r4"),
     (8, 28672, 4096, 4096, 28673, P16, Q16, "skinny_w8_c4"),
     (16, 28672, 4096, 4096, 28672, P16, Q16, "skinny_w8_c4"),
-    (4096, 4096, 4096, 4096, 4096, P16, Q16, "mfma_128x256x16_w64x128_d6"),
+    (4096, 4096, 4096, 4096, 4096, P16, Q16, "mfma_256x256x32_w64x128_d6"),
+    # 256 x 256 tiles only where they fill whole waves of the 256 CUs
+    (8192, 8192, 4096, 4096, 8192, P16, Q16, "mfma_256x256x32_w64x128_d6"),
+    (6144, 6144, 4096, 4096, 6144, P16, Q16, "mfma_128x256x16_w64x128_d6"),
+    (4096, 4097, 4096, 4096, 4097, P16, Q16, "mfma_256x128x16_w128x64_p5"),
     (2047, 3001, 1531, 1531, 3001, P16, Q16, "mfma_64x64x32_w32x32_p5"),
     (512, 512, 512, 512, 512, P16, Q16, "mfma_64x64x32_w32x32_d6_sk"),
     (1024, 1024, 1024, 1024, 1024, P16, Q16, "mfma_64x64x32_w32x32_d6"),
