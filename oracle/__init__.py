@@ -65,6 +65,11 @@ def _load():
                                           f32p, i64, f32p, i64, f32, f32p, i64,
                                           f32p, i64, f64p, i64, f64p, i64]
     lib.oracle_gemm_ex_f64acc.restype = ctypes.c_int
+    lib.oracle_gemm_fused_f64acc.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, f32,
+                                             f32p, i64, f32p, i64, f32, f32p, i64,
+                                             f32p, ctypes.c_int,
+                                             f32p, i64, f64p, i64, f64p, i64]
+    lib.oracle_gemm_fused_f64acc.restype = ctypes.c_int
     lib.oracle_sum_f64acc.argtypes = [i64, f32p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p]
     lib.oracle_sum_f64acc.restype = ctypes.c_int
@@ -239,3 +244,50 @@ def sum_f32(x: np.ndarray):
     if rc != 0:
         raise RuntimeError(f"oracle_sum_f64acc failed with status {rc}")
     return np.float32(s.value), sd.value, ab.value
+
+
+def gemm_fused(A: np.ndarray, B: np.ndarray, *, trans_a: bool = False, trans_b: bool = False,
+               alpha: float = 1.0, beta: float = 0.0, C_in: np.ndarray | None = None,
+               bias: np.ndarray | None = None, act: int = 0):
+    """Return ``(C, Cd, ABS)`` for ``act(alpha * op(A) @ op(B) + beta * C_in +
+    bias)``: ``gemm_ex`` plus a bias row vector (length N, added to every row)
+    and an activation (0: none, 1: ReLU).  Definition:
+    ``oracle_gemm_fused_f64acc`` in ``gemm_oracle.c``."""
+    if trans_a:
+        K, M = A.shape
+    else:
+        M, K = A.shape
+    if trans_b:
+        N, K2 = B.shape
+    else:
+        K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner sizes differ: {K} vs {K2}")
+    lda, ldb = _ld(A, "A"), _ld(B, "B")
+    alpha32, beta32 = float(np.float32(alpha)), float(np.float32(beta))
+    C = np.zeros((M, N), dtype=np.float32)
+    Cd = np.zeros((M, N), dtype=np.float64)
+    ABS = np.zeros((M, N), dtype=np.float64)
+    if M == 0 or N == 0:
+        return C, Cd, ABS
+    cin_ptr, ldcin = None, max(1, N)
+    if beta32 != 0.0:
+        if C_in is None or C_in.shape != (M, N):
+            raise ValueError("C_in (M x N) is needed when beta != 0")
+        ldcin = _ld(C_in, "C_in")
+        cin_ptr = C_in.ctypes.data
+    bias_ptr = None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        if bias.shape != (N,):
+            raise ValueError("bias must have N elements")
+        bias_ptr = bias.ctypes.data
+    rc = _load().oracle_gemm_fused_f64acc(
+        int(bool(trans_a)), int(bool(trans_b)), M, N, K, alpha32,
+        A.ctypes.data if A.size else None, max(lda, M if trans_a else K),
+        B.ctypes.data if B.size else None, max(ldb, K if trans_b else N),
+        beta32, cin_ptr, max(ldcin, N), bias_ptr, int(act),
+        C.ctypes.data, N, Cd.ctypes.data, N, ABS.ctypes.data, N)
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_fused_f64acc failed with status {rc}")
+    return C, Cd, ABS

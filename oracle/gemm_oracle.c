@@ -178,14 +178,29 @@ int oracle_gemm_elems(int64_t M, int64_t N, int64_t K,
  *
  *   Cin, ldcin     the input C (read only when beta != 0; may alias C)
  * Pitches: lda >= (transA ? M : K), ldb >= (transB ? K : N).
+ *
+ * oracle_gemm_fused_f64acc adds the rest of a fused epilogue ("fuse kernels:
+ * one memory pass fewer", "GPU compute shaders", Performance): a bias row
+ * vector broadcast down the columns and an elementwise activation.  Readings:
+ * bias[j] is added to every row's column j (NULL: no bias); act 0 is the
+ * identity and act 1 is ReLU, relu(x) = (x < 0 ? +0 : x), which keeps NaN.
+ *
+ *   Cd[i][j] = act(alpha * S[i][j] + beta * Cin[i][j] + bias[j])   (binary64)
+ *   C[i][j]  = (float)Cd[i][j]
+ *   ABS[i][j]= |alpha| * sum of |products| + |beta * Cin[i][j]| + |bias[j]|
+ *
+ * (ReLU commutes with the rounding to binary32, so where it is applied does
+ * not change C.)  oracle_gemm_ex_f64acc is the case bias = NULL, act = 0.
  */
-int oracle_gemm_ex_f64acc(int transA, int transB, int64_t M, int64_t N, int64_t K,
-                          float alpha, const float *A, int64_t lda,
-                          const float *B, int64_t ldb, float beta,
-                          const float *Cin, int64_t ldcin,
-                          float *C, int64_t ldc,
-                          double *Cd, int64_t ldcd,
-                          double *ABS, int64_t ldabs) {
+int oracle_gemm_fused_f64acc(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                             float alpha, const float *A, int64_t lda,
+                             const float *B, int64_t ldb, float beta,
+                             const float *Cin, int64_t ldcin,
+                             const float *bias, int act,
+                             float *C, int64_t ldc,
+                             double *Cd, int64_t ldcd,
+                             double *ABS, int64_t ldabs) {
+  if (act != 0 && act != 1) return ORACLE_BAD_ARG;
   if (M < 0 || N < 0 || K < 0) return ORACLE_BAD_ARG;
   if (M == 0 || N == 0) return ORACLE_OK;
   if (lda < (transA ? M : K) || ldb < (transB ? K : N)) return ORACLE_BAD_ARG;
@@ -228,6 +243,11 @@ int oracle_gemm_ex_f64acc(int transA, int transB, int64_t M, int64_t N, int64_t 
           v += c;
           m += fabs(c);
         }
+        if (bias) {
+          v += (double)bias[j];
+          m += fabs((double)bias[j]);
+        }
+        if (act == 1 && v < 0.0) v = 0.0;
         if (C) C[i * ldc + j] = (float)v;
         if (Cd) Cd[i * ldcd + j] = v;
         if (ABS) ABS[i * ldabs + j] = m;
@@ -237,6 +257,17 @@ int oracle_gemm_ex_f64acc(int transA, int transB, int64_t M, int64_t N, int64_t 
     free(mag);
   }
   return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+int oracle_gemm_ex_f64acc(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                          float alpha, const float *A, int64_t lda,
+                          const float *B, int64_t ldb, float beta,
+                          const float *Cin, int64_t ldcin,
+                          float *C, int64_t ldc,
+                          double *Cd, int64_t ldcd,
+                          double *ABS, int64_t ldabs) {
+  return oracle_gemm_fused_f64acc(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, Cin,
+                                  ldcin, 0, 0, C, ldc, Cd, ldcd, ABS, ldabs);
 }
 
 /*

@@ -470,3 +470,90 @@ def pin_sum_special_values(fn_s):
 
 
 SUM_PINS = [pin_sum_closed_forms, pin_sum_integer_int64, pin_sum_fsum, pin_sum_special_values]
+
+
+# --- fused epilogue: act(alpha * op(A) op(B) + beta * C + bias) ----------------------
+#
+# ``fn_f(A, B, ta, tb, alpha, beta, C_in, bias, act) -> (C, Cd, ABS)`` with the
+# contract of ``oracle.gemm_fused``.
+
+def _relu64(x):
+    return np.where(x < 0, 0, x)
+
+
+def pin_fused_integer_bruteforce(fn_f):
+    """Small integers, integer alpha, beta and bias, every layout, with and
+    without ReLU: C equals the int64 computation exactly."""
+    errs = []
+    for (m, n, k, seed) in [(13, 9, 21, 1401), (5, 17, 3, 1402), (1, 6, 8, 1403)]:
+        A, B = _ints(m, k, seed), _ints(k, n, seed + 10)
+        Cin = _ints(m, n, seed + 20, -5, 5)
+        bias = _ints(1, n, seed + 30, -9, 9).reshape(-1)
+        for (ta, tb) in TRANS:
+            for (alpha, beta, act) in [(1, 0, 1), (2, -1, 0), (-3, 2, 1), (0, 1, 1)]:
+                C, _, _ = fn_f(_stored(A, ta), _stored(B, tb), ta, tb, float(alpha), float(beta),
+                               Cin, bias, act)
+                want = (alpha * _exact_int(A, B) + beta * Cin.astype(np.int64)
+                        + bias.astype(np.int64)[None, :])
+                if act == 1:
+                    want = _relu64(want)
+                if not np.array_equal(C.astype(np.int64), want):
+                    errs += _fail("fused-integer", f"{m}x{n}x{k} trans={ta},{tb} "
+                                                   f"alpha={alpha} beta={beta} act={act}")
+    return errs
+
+
+def pin_fused_bias_is_a_row_vector(fn_f):
+    """With A = 0 the product vanishes: every row of C is act(bias) (M != N, so
+    a bias indexed by row would not fit or would differ)."""
+    errs = []
+    m, n, k = 6, 10, 4
+    A = np.zeros((m, k), np.float32)
+    B = _np(inputs.uniform_matrix(k, n, 1411))
+    bias = _np(inputs.uniform_matrix(1, n, 1412)).reshape(-1)
+    for act in (0, 1):
+        C, _, ABS = fn_f(A, B, False, False, 1.0, 0.0, None, bias, act)
+        want = np.maximum(bias, 0) if act else bias
+        if not np.array_equal(C, np.broadcast_to(want, (m, n))):
+            errs += _fail("fused-bias", f"act={act}: rows are not act(bias)")
+        if not np.array_equal(ABS, np.broadcast_to(np.abs(bias).astype(np.float64), (m, n))):
+            errs += _fail("fused-bias", "ABS is not |bias|")
+    return errs
+
+
+def pin_fused_relu_of_identity(fn_f):
+    """ReLU is applied last and keeps NaN: the ReLU result equals ReLU of the
+    identity-activation result, element by element and bit for bit."""
+    A, B = inputs.make_ab(12, 15, 40, "normal", "normal", 1421)
+    A, B = _np(A).copy(), _np(B)
+    A[3, 7] = np.nan
+    bias = _np(inputs.uniform_matrix(1, 15, 1422)).reshape(-1)
+    C0, _, _ = fn_f(A, B, False, False, 0.5, 0.0, None, bias, 0)
+    C1, _, _ = fn_f(A, B, False, False, 0.5, 0.0, None, bias, 1)
+    want = np.where(C0 < 0, np.float32(0), C0)
+    same = (C1 == want) | (np.isnan(C1) & np.isnan(want))
+    if not same.all():
+        return _fail("fused-relu", "ReLU result != ReLU of the plain result (or NaN lost)")
+    if not np.isnan(C1[3]).all():
+        return _fail("fused-relu", "NaN row did not survive ReLU")
+    return []
+
+
+def pin_fused_reduces_to_ex(fn_f):
+    """No bias, no activation: exactly gemm_ex (C, Cd and ABS), which the
+    extended-operation pins fix."""
+    import oracle
+    A, B = inputs.make_ab(10, 9, 33, "u11", "normal", 1431)
+    Cin = _np(inputs.uniform_matrix(10, 9, 1432))
+    errs = []
+    for (ta, tb) in TRANS:
+        As, Bs = _stored(_np(A), ta), _stored(_np(B), tb)
+        want = oracle.gemm_ex(As, Bs, trans_a=ta, trans_b=tb, alpha=1.5, beta=-0.5, C_in=Cin)
+        got = fn_f(As, Bs, ta, tb, 1.5, -0.5, Cin, None, 0)
+        if not all(np.array_equal(g, w) for g, w in zip(got, want)):
+            errs += _fail("fused-ex", f"trans={ta},{tb}: differs from gemm_ex")
+    return errs
+
+
+FUSED_PINS = [pin_fused_integer_bruteforce, pin_fused_bias_is_a_row_vector,
+              pin_fused_relu_of_identity, pin_fused_reduces_to_ex]

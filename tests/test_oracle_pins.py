@@ -286,3 +286,61 @@ def test_sum_pins_catch_planted_mistake(mistake):
     for pin in pins.SUM_PINS:
         errs += pin(_sum_variant(mistake))
     assert errs, f"no sum pin caught the planted mistake {mistake!r}"
+
+
+# ---- fused epilogue: bias and activation ----------------------------------------
+
+def oracle_fused_fn(A, B, ta, tb, alpha, beta, C_in, bias, act):
+    return oracle.gemm_fused(A, B, trans_a=ta, trans_b=tb, alpha=alpha, beta=beta, C_in=C_in,
+                             bias=bias, act=act)
+
+
+@pytest.mark.parametrize("pin", pins.FUSED_PINS, ids=lambda p: p.__name__)
+def test_oracle_fused_passes_pin(pin):
+    errs = pin(oracle_fused_fn)
+    assert not errs, "\n".join(errs)
+
+
+def _fused_variant(mistake):
+    """gemm_fused-like function with one planted mistake, built on gemm_ex."""
+    def fn(A, B, ta, tb, alpha, beta, C_in, bias, act):
+        _, Cd, ABS = oracle.gemm_ex(A, B, trans_a=ta, trans_b=tb, alpha=alpha, beta=beta,
+                                    C_in=C_in)
+        Cd, ABS = Cd.copy(), ABS.copy()
+        relu = (lambda x: np.abs(x)) if mistake == "relu_is_abs" else \
+            (lambda x: np.where(x > 0, x, 0.0)) if mistake == "relu_drops_nan" else \
+            (lambda x: np.where(x < 0, 0.0, x))
+        if act == 1 and mistake == "relu_before_bias":
+            Cd = relu(Cd)
+        if bias is not None:
+            b = bias.astype(np.float64)
+            if mistake == "bias_by_row":
+                m = Cd.shape[0]
+                bb = np.resize(b, m)[:, None]
+                Cd = Cd + bb
+            else:
+                Cd = Cd + b[None, :] * (2 if mistake == "bias_twice" else 1)
+            ABS = ABS + np.abs(b)[None, :]
+        if act == 1 and mistake != "relu_before_bias":
+            Cd = relu(Cd)
+        return Cd.astype(np.float32), Cd, ABS
+    return fn
+
+
+FUSED_MISTAKES = ["relu_is_abs", "relu_drops_nan", "relu_before_bias", "bias_by_row",
+                  "bias_twice"]
+
+
+def test_fused_correct_variant_passes_all_pins():
+    errs = []
+    for pin in pins.FUSED_PINS:
+        errs += pin(_fused_variant("none"))
+    assert not errs, "\n".join(errs)
+
+
+@pytest.mark.parametrize("mistake", FUSED_MISTAKES)
+def test_fused_pins_catch_planted_mistake(mistake):
+    errs = []
+    for pin in pins.FUSED_PINS:
+        errs += pin(_fused_variant(mistake))
+    assert errs, f"no fused pin caught the planted mistake {mistake!r}"
