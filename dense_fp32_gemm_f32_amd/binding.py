@@ -25,13 +25,15 @@ STATUS_NAMES = {
     0: "GEMM_F32_OK", 1: "GEMM_F32_ERR_INVALID_DIM", 2: "GEMM_F32_ERR_INVALID_LD",
     3: "GEMM_F32_ERR_NULL_PTR", 4: "GEMM_F32_ERR_ALIAS", 5: "GEMM_F32_ERR_DEVICE",
     6: "GEMM_F32_ERR_WORKSPACE", 7: "GEMM_F32_ERR_LAUNCH", 8: "GEMM_F32_ERR_BAD_KERNEL",
-    9: "GEMM_F32_ERR_POINTER",
+    9: "GEMM_F32_ERR_POINTER", 10: "GEMM_F32_ERR_INVALID_ARG",
 }
+ACT_NONE, ACT_RELU = 0, 1
 EXPORTS = ["gemm_f32", "gemm_f32_ex", "gemm_f32_ref_gpu", "gemm_f32_status_string",
            "gemm_f32_selected_kernel", "gemm_f32_selected_kernel_ex", "gemm_f32_version",
            "gemm_f32_kernel_count", "gemm_f32_kernel_name", "gemm_f32_run_kernel",
            "gemm_f32_run_kernel_ex", "gemm_f32_release_workspaces", "gemm_f32_batched",
-           "gemm_f32_selected_kernel_batched", "reduce_sum_f32"]
+           "gemm_f32_selected_kernel_batched", "reduce_sum_f32", "gemm_f32_fused",
+           "gemm_f32_run_kernel_fused"]
 
 
 class GemmError(RuntimeError):
@@ -67,6 +69,11 @@ def load():
     lib.gemm_f32_ex.restype = ctypes.c_int
     lib.gemm_f32_run_kernel_ex.argtypes = [ci, *ex_args]
     lib.gemm_f32_run_kernel_ex.restype = ctypes.c_int
+    fused_args = [ci, ci, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, vp, ci, vp]
+    lib.gemm_f32_fused.argtypes = fused_args
+    lib.gemm_f32_fused.restype = ctypes.c_int
+    lib.gemm_f32_run_kernel_fused.argtypes = [ci, *fused_args]
+    lib.gemm_f32_run_kernel_fused.restype = ctypes.c_int
     lib.gemm_f32_selected_kernel_ex.argtypes = [ci, ci, i64, i64, i64, i64, i64, i64, f32, f32,
                                                 vp, vp, vp]
     lib.gemm_f32_selected_kernel_ex.restype = ctypes.c_char_p
@@ -103,6 +110,18 @@ def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
 def gemm_f32_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
     return load().gemm_f32_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                               stream)
+
+
+def gemm_f32_fused(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, bias, act,
+                   stream=0) -> int:
+    return load().gemm_f32_fused(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                 bias, act, stream)
+
+
+def gemm_f32_run_kernel_fused(index, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                              ldc, bias, act, stream=0) -> int:
+    return load().gemm_f32_run_kernel_fused(index, transA, transB, M, N, K, alpha, A, lda, B,
+                                            ldb, beta, C, ldc, bias, act, stream)
 
 
 def gemm_f32_run_kernel_ex(index, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
@@ -331,6 +350,32 @@ def gemm_ex(A, B, C=None, *, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, 
                                         ldc, stream)
     if rc != GEMM_F32_OK:
         raise GemmError(rc, "gemm_f32_ex" if kernel is None else f"gemm_f32_run_kernel_ex({kernel})")
+    return C
+
+
+def gemm_fused(A, B, C=None, *, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, bias=None,
+               act=ACT_NONE, kernel=None):
+    """C = act(alpha * op(A) @ op(B) + beta * C + bias) on the GPU; ``bias`` a
+    1-D contiguous tensor of N floats (or None), ``act`` ACT_NONE or ACT_RELU.
+    ``kernel`` runs one named (or indexed) kernel of the table.  Returns C."""
+    (M, N, K, a, lda, b, ldb, c, ldc, stream), C = _args_ex(A, B, C, trans_a, trans_b)
+    bptr = 0
+    if bias is not None:
+        if bias.dim() != 1 or bias.numel() != N or (N > 1 and bias.stride(0) != 1):
+            raise ValueError(f"bias must be a contiguous vector of {N} floats")
+        bptr = bias.data_ptr()
+    ta, tb = int(bool(trans_a)), int(bool(trans_b))
+    with _device(A):
+        if kernel is None:
+            rc = gemm_f32_fused(ta, tb, M, N, K, alpha, a, lda, b, ldb, beta, c, ldc, bptr,
+                                int(act), stream)
+        else:
+            index = kernel_index(kernel) if isinstance(kernel, str) else int(kernel)
+            rc = gemm_f32_run_kernel_fused(index, ta, tb, M, N, K, alpha, a, lda, b, ldb, beta,
+                                           c, ldc, bptr, int(act), stream)
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc, "gemm_f32_fused" if kernel is None else
+                        f"gemm_f32_run_kernel_fused({kernel})")
     return C
 
 

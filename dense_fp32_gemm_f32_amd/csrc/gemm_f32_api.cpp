@@ -89,12 +89,25 @@ MfmaPlan plan_mfma(const gemmf32::MfmaVariant& v, const Problem& p, bool split) 
 
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
-// The operation around the product: C = alpha * op(A) op(B) + beta * C, with
-// op(A) = A^T when ta (A stored K x M) and op(B) = B^T when tb (B stored N x K).
+// The operation around the product: C = act(alpha * op(A) op(B) + beta * C +
+// bias), with op(A) = A^T when ta (A stored K x M) and op(B) = B^T when tb (B
+// stored N x K); bias a row of N values or NULL; act 0 identity, 1 ReLU.
 struct Op {
   bool ta = false, tb = false;
   float alpha = 1.f, beta = 0.f;
-  bool plain() const { return !ta && !tb && alpha == 1.f && beta == 0.f; }
+  const float* bias = nullptr;
+  int act = 0;
+  bool plain() const {
+    return !ta && !tb && alpha == 1.f && beta == 0.f && !bias && act == 0;
+  }
+  gemmf32::Epilogue epilogue() const {
+    gemmf32::Epilogue e;
+    e.alpha = alpha;
+    e.beta = beta;
+    e.bias = bias;
+    e.act = act;
+    return e;
+  }
 };
 
 // ---- argument checks (host only, nothing enqueued) -------------------------
@@ -128,6 +141,14 @@ int check_args(const Op& op, int64_t M, int64_t N, int64_t K, const float* A, in
       const uintptr_t b0 = (uintptr_t)B, b1 = b0 + (uintptr_t)(((b_rows - 1) * ldb + b_cols) * 4);
       if (c0 < b1 && b0 < c1) return GEMM_F32_ERR_ALIAS;
     }
+  }
+  // the epilogue: a known activation; a bias row that is aligned and not in C
+  if (op.act != 0 && op.act != 1) return GEMM_F32_ERR_INVALID_ARG;
+  if (op.bias && has_c) {
+    if (!aligned4(op.bias)) return GEMM_F32_ERR_POINTER;
+    const uintptr_t c0 = (uintptr_t)C, c1 = c0 + (uintptr_t)(((M - 1) * ldc + N) * 4);
+    const uintptr_t b0 = (uintptr_t)op.bias, b1 = b0 + (uintptr_t)(N * 4);
+    if (c0 < b1 && b0 < c1) return GEMM_F32_ERR_ALIAS;
   }
   return GEMM_F32_OK;
 }
@@ -301,11 +322,11 @@ int run_entry(const Entry& e, const Op& op, const Problem& p, int dev, hipStream
         const int rc = get_workspace(dev, s, pl.partial_floats, &partials);
         if (rc != GEMM_F32_OK) return rc;
       }
-      err = v.launch(p, pl, partials, op.alpha, op.beta, s);
+      err = v.launch(p, pl, partials, op.epilogue(), s);
       break;
     }
     case Kind::MfmaEx:
-      err = gemmf32::mfma_ex_variant(e.sub).launch(p, op.alpha, op.beta, s);
+      err = gemmf32::mfma_ex_variant(e.sub).launch(p, op.epilogue(), s);
       break;
     case Kind::Ref:
       err = gemmf32::launch_ref(p, s);
@@ -376,12 +397,14 @@ Prepared prepare(const Op& op, int64_t M, int64_t N, int64_t K, const float* A, 
     if ((r.status = check_pointer(B, r.dev)) != GEMM_F32_OK) return r;
   }
   r.status = check_pointer(C, r.dev);
+  if (r.status == GEMM_F32_OK && op.bias) r.status = check_pointer(op.bias, r.dev);
   return r;
 }
 
-// K == 0: C = beta * C (an empty sum), or +0.0 when beta == 0.
+// K == 0: the epilogue of an empty sum, C = act(alpha * 0 + beta * C + bias)
+// (+0.0 for the plain product).
 int run_k0(const Op& op, const Problem& p, hipStream_t s) {
-  if (gemmf32::launch_scale(p, op.beta, s) != hipSuccess) {
+  if (gemmf32::launch_scale(p, op.epilogue(), s) != hipSuccess) {
     (void)hipGetLastError();
     return GEMM_F32_ERR_LAUNCH;
   }
@@ -525,12 +548,15 @@ int gemm_batched_impl(int64_t M, int64_t N, int64_t K, const float* A, int64_t l
   return GEMM_F32_OK;
 }
 
-Op make_op(int transA, int transB, float alpha, float beta) {
+Op make_op(int transA, int transB, float alpha, float beta, const float* bias = nullptr,
+           int act = 0) {
   Op op;
   op.ta = transA != 0;
   op.tb = transB != 0;
   op.alpha = alpha;
   op.beta = beta;
+  op.bias = bias;
+  op.act = act;
   return op;
 }
 
@@ -548,6 +574,21 @@ int gemm_f32_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float a
                 int64_t ldc, void* stream) {
   return gemm_impl(make_op(transA, transB, alpha, beta), M, N, K, A, lda, B, ldb, C, ldc,
                    stream);
+}
+
+int gemm_f32_fused(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                   const float* A, int64_t lda, const float* B, int64_t ldb, float beta,
+                   float* C, int64_t ldc, const float* bias, int activation, void* stream) {
+  return gemm_impl(make_op(transA, transB, alpha, beta, bias, activation), M, N, K, A, lda, B,
+                   ldb, C, ldc, stream);
+}
+
+int gemm_f32_run_kernel_fused(int index, int transA, int transB, int64_t M, int64_t N,
+                              int64_t K, float alpha, const float* A, int64_t lda,
+                              const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
+                              const float* bias, int activation, void* stream) {
+  return run_kernel_impl(index, make_op(transA, transB, alpha, beta, bias, activation), M, N, K,
+                         A, lda, B, ldb, C, ldc, stream);
 }
 
 int gemm_f32_batched(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
@@ -612,7 +653,7 @@ int gemm_f32_ref_gpu(int64_t M, int64_t N, int64_t K, const float* A, int64_t ld
   if (r.status != GEMM_F32_OK || M == 0 || N == 0) return r.status;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t err =
-      K == 0 ? gemmf32::launch_scale(r.p, 0.f, s) : gemmf32::launch_ref(r.p, s);
+      K == 0 ? gemmf32::launch_scale(r.p, gemmf32::Epilogue{}, s) : gemmf32::launch_ref(r.p, s);
   if (err != hipSuccess) {
     (void)hipGetLastError();
     return GEMM_F32_ERR_LAUNCH;
@@ -645,6 +686,7 @@ const char* gemm_f32_status_string(int status) {
     case GEMM_F32_ERR_LAUNCH: return "kernel launch failed";
     case GEMM_F32_ERR_BAD_KERNEL: return "kernel index unknown or unable to run these arguments";
     case GEMM_F32_ERR_POINTER: return "pointer is not device memory the current device can access";
+    case GEMM_F32_ERR_INVALID_ARG: return "unknown activation";
     default: return "unknown status";
   }
 }

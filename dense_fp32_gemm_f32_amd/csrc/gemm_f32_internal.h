@@ -24,7 +24,27 @@ struct Problem {
   int batch = 1;
 };
 
+// The update written to each element of C, given its fp32 sum s and column j:
+//   C = act(alpha * s + beta * C + bias[j])
+// C is not read when beta == 0; bias may be NULL; act 0 is the identity and 1
+// is ReLU, relu(x) = (x < 0 ? +0 : x), which keeps NaN.  The plain product is
+// alpha = 1, beta = 0, no bias, identity.
+struct Epilogue {
+  float alpha = 1.f, beta = 0.f;
+  const float* bias = nullptr;
+  int act = 0;
+};
+
 #if defined(__HIP__)
+__device__ __forceinline__ float epilogue_apply(const Epilogue& e, float s, const float* c,
+                                                int64_t j) {
+  float v = e.alpha * s;
+  if (e.beta != 0.f) v = v + e.beta * *c;
+  if (e.bias) v = v + e.bias[j];
+  if (e.act == 1 && v < 0.f) v = 0.f;
+  return v;
+}
+
 // Point p at product blockIdx.z of a strided batch.
 __device__ __forceinline__ void select_batch(Problem& p) {
   const int64_t b = blockIdx.z;
@@ -64,7 +84,7 @@ struct MfmaExVariant {
   const char* name;
   int bm, bn, bk;
   bool trans_a, trans_b;
-  hipError_t (*launch)(const Problem&, float alpha, float beta, hipStream_t);
+  hipError_t (*launch)(const Problem&, const Epilogue&, hipStream_t);
 };
 int mfma_ex_variant_count();
 const MfmaExVariant& mfma_ex_variant(int i);
@@ -93,8 +113,8 @@ struct SkinnyVariant {
   int target_splits;   // K slices (0 = choose from the shape)
   bool trans_a, trans_b;
   SkinnyPlan (*plan)(const Problem&, int target_splits);
-  hipError_t (*launch)(const Problem&, const SkinnyPlan&, float* partials, float alpha,
-                       float beta, hipStream_t);
+  hipError_t (*launch)(const Problem&, const SkinnyPlan&, float* partials, const Epilogue&,
+                       hipStream_t);
   // needs B 16-byte aligned with N and ldb multiples of 4 (whole float4 row runs)
   bool b16 = false;
 };
@@ -108,7 +128,7 @@ const SkinnyVariant& skinny_rows_variant(int i);
 // ---- sum of K-slice partials: C = part[0] + part[1] + ... (slice order) ---
 // With alpha and beta: C = alpha * (sum of slices) + beta * C (C not read when beta == 0).
 hipError_t launch_combine(const Problem& p, int slices, const float* partials, hipStream_t s,
-                          float alpha = 1.f, float beta = 0.f);
+                          const Epilogue& e = Epilogue{});
 
 // ---- deterministic sum of an fp32 array ------------------------------------
 // Pass 1: `groups` workgroups, group g sums x[g*chunk, min(n, (g+1)*chunk))
@@ -123,6 +143,6 @@ hipError_t launch_reduce_sum(int64_t n, const float* x, float* out, float* part,
 // ---- naive reference and the K == 0 fill ----------------------------------
 hipError_t launch_ref(const Problem& p, hipStream_t s);
 // C = beta * C over the M x N window (C = +0.0 when beta == 0; C not read then)
-hipError_t launch_scale(const Problem& p, float beta, hipStream_t s);
+hipError_t launch_scale(const Problem& p, const Epilogue& e, hipStream_t s);
 
 }  // namespace gemmf32

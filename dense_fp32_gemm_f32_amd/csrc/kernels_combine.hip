@@ -24,7 +24,7 @@ constexpr int kMaxGridY = 65535;
 // multiple of 4 (then every row of every slice starts 16-byte aligned).
 __global__ void __launch_bounds__(kThreads) combine_kernel(Problem p, int slices,
                                                           const float* __restrict__ part,
-                                                          float alpha, float beta) {
+                                                          Epilogue e) {
   const int N = p.N;
   const int n0 = blockIdx.x * kColsPerBlock + kPerThread * threadIdx.x;
   if (n0 >= N) return;
@@ -63,8 +63,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(Problem p, int slices
 #pragma unroll
     for (int q = 0; q < kPerThread; ++q) {
       if (n0 + q < N) {
-        const float v = alpha * s[q];
-        dst[q] = beta == 0.f ? v : v + beta * dst[q];
+        dst[q] = epilogue_apply(e, s[q], dst + q, (int64_t)n0 + q);
       }
     }
   }
@@ -73,7 +72,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(Problem p, int slices
 }  // namespace
 
 hipError_t launch_combine(const Problem& p, int slices, const float* partials, hipStream_t s,
-                          float alpha, float beta) {
+                          const Epilogue& e) {
   if (slices < 1 || !partials) return hipErrorInvalidValue;
   if (p.batch != 1) return hipErrorInvalidConfiguration;
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
@@ -82,8 +81,8 @@ hipError_t launch_combine(const Problem& p, int slices, const float* partials, h
   Problem pp = p;
   int sl = slices;
   const float* part = partials;
-  float a = alpha, b = beta;
-  void* args[] = {&pp, &sl, &part, &a, &b};
+  Epilogue ee = e;
+  void* args[] = {&pp, &sl, &part, &ee};
   return hipLaunchKernel(reinterpret_cast<const void*>(&combine_kernel), dim3(bx, by),
                          dim3(kThreads), args, 0, s);
 }

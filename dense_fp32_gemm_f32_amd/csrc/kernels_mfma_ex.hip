@@ -136,7 +136,7 @@ struct Frag {
 template <int BM, int BN, int BK, int WM, int WN, bool A_KC, bool B_KC, int kMinWaves>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     __attribute__((amdgpu_waves_per_eu(kMinWaves)))
-    mfma_ex_kernel(Problem p, float alpha, float beta, int tiles_m, int tiles_n) {
+    mfma_ex_kernel(Problem p, Epilogue e, int tiles_m, int tiles_n) {
   constexpr int kWavesM = BM / WM, kWavesN = BN / WN;
   constexpr int kThreads = kWavesM * kWavesN * 64;
   constexpr int kFragM = WM / 32, kFragN = WN / 32;
@@ -331,7 +331,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
   }
   for (; t < ktiles; ++t) step(t, std::false_type{}, std::false_type{}, std::false_type{});
 
-  // ---- epilogue: C = alpha * acc + beta * C (C not read when beta == 0) ----
+  // ---- epilogue: C = act(alpha * acc + beta * C + bias) (C not read when beta == 0)
 #pragma unroll
   for (int i = 0; i < kFragM; ++i) {
 #pragma unroll
@@ -344,8 +344,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
           const int row = rbase + 8 * (r >> 2) + (r & 3);
           if (row < M) {
             float* c = p.C + (int64_t)row * p.ldc + col;
-            const float v = alpha * acc[i][j][r];
-            *c = beta == 0.f ? v : v + beta * *c;
+            *c = epilogue_apply(e, acc[i][j][r], c, col);
           }
         }
       }
@@ -354,16 +353,16 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool A_KC, bool B_KC, int kMinWaves>
-hipError_t launch_ex(const Problem& p, float alpha, float beta, hipStream_t s) {
+hipError_t launch_ex(const Problem& p, const Epilogue& e, hipStream_t s) {
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + BN - 1) / BN;
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
   if (tiles > 0x7fffffff || p.batch < 1 || p.batch > kMaxLaunchBatch)
     return hipErrorInvalidConfiguration;
   Problem pp = p;
-  float a = alpha, b = beta;
+  Epilogue ee = e;
   int tm = tiles_m, tn = tiles_n;
-  void* args[] = {&pp, &a, &b, &tm, &tn};
+  void* args[] = {&pp, &ee, &tm, &tn};
   return hipLaunchKernel(
       reinterpret_cast<const void*>(&mfma_ex_kernel<BM, BN, BK, WM, WN, A_KC, B_KC, kMinWaves>),
       dim3((unsigned)tiles, 1, (unsigned)p.batch), dim3((BM / WM) * (BN / WN) * 64), args, 0,

@@ -31,13 +31,13 @@ __global__ void __launch_bounds__(kRefTile * kRefTile) ref_gemm_kernel(Problem p
 }
 
 // An empty sum (K == 0): C = beta * C, or +0.0 without reading C when beta == 0.
-__global__ void __launch_bounds__(256) scale_kernel(Problem p, float beta) {
+__global__ void __launch_bounds__(256) scale_kernel(Problem p, Epilogue e) {
   select_batch(p);
   const int col = blockIdx.x * 256 + threadIdx.x;
   if (col >= p.N) return;
   for (int64_t row = blockIdx.y; row < p.M; row += gridDim.y) {
     float* c = p.C + row * p.ldc + col;
-    *c = beta == 0.f ? 0.f : beta * *c;
+    *c = epilogue_apply(e, 0.f, c, col);
   }
 }
 
@@ -55,14 +55,14 @@ hipError_t launch_ref(const Problem& p, hipStream_t s) {
                          dim3(kRefTile, kRefTile), args, 0, s);
 }
 
-hipError_t launch_scale(const Problem& p, float beta, hipStream_t s) {
+hipError_t launch_scale(const Problem& p, const Epilogue& e, hipStream_t s) {
   if (p.batch < 1 || p.batch > kMaxLaunchBatch) return hipErrorInvalidConfiguration;
   const int64_t gx = (p.N + 255) / 256;
   int64_t gy = p.M;
   if (gy > kMaxGridY) gy = kMaxGridY;
   Problem pp = p;
-  float b = beta;
-  void* args[] = {&pp, &b};
+  Epilogue ee = e;
+  void* args[] = {&pp, &ee};
   return hipLaunchKernel(reinterpret_cast<const void*>(&scale_kernel),
                          dim3((unsigned)gx, (unsigned)gy, (unsigned)p.batch), dim3(256), args,
                          0, s);

@@ -171,7 +171,7 @@ __device__ __forceinline__ void stream_tile(const Problem& p, int lane, int n0, 
 template <int NW, int CG, int U, bool VA, bool VB, bool TA>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 16 ? 4 : 2)))
     skinny_tile_kernel(Problem p, int sb_per_slice, int slices, float* __restrict__ part,
-                       float alpha, float beta) {
+                       Epilogue ep) {
   constexpr int NRG = NW / CG;
   static_assert(NW % CG == 0, "whole row groups");
   __shared__ __attribute__((aligned(16))) float red[NW][2][4][64];
@@ -224,9 +224,7 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW
       for (int w = 1; w < NRG; ++w) s += red[w * CG + g][c][r][l];
       float* d = dst + (int64_t)m * ld + n;
       if (slices == 1) {
-        // C = alpha * sum + beta * C (C not read when beta == 0)
-        const float v = alpha * s;
-        *d = beta == 0.f ? v : v + beta * *d;
+        *d = epilogue_apply(ep, s, d, n);
       } else {
         *d = s;
       }
@@ -253,21 +251,21 @@ SkinnyPlan plan_tile(const Problem& p, int target) {
 }
 
 template <int NW, int CG, int U, bool VA, bool VB, bool TA>
-hipError_t launch_tile(const Problem& p, const SkinnyPlan& pl, float* partials, float alpha,
-                       float beta, hipStream_t s) {
+hipError_t launch_tile(const Problem& p, const SkinnyPlan& pl, float* partials,
+                       const Epilogue& e, hipStream_t s) {
   if (pl.strips <= 0 || pl.splits < 1 || pl.splits > 65535 || p.batch != 1)
     return hipErrorInvalidConfiguration;
   if (pl.splits > 1 && !partials) return hipErrorInvalidValue;
   Problem pp = p;
   int per = pl.kslice, slices = pl.splits;
   float* part = partials;
-  float a = alpha, b = beta;
-  void* args[] = {&pp, &per, &slices, &part, &a, &b};
+  Epilogue ee = e;
+  void* args[] = {&pp, &per, &slices, &part, &ee};
   hipError_t err = hipLaunchKernel(
       reinterpret_cast<const void*>(&skinny_tile_kernel<NW, CG, U, VA, VB, TA>),
       dim3(pl.strips, pl.splits), dim3(NW * 64), args, 0, s);
   if (err != hipSuccess || pl.splits == 1) return err;
-  return launch_combine(p, slices, partials, s, alpha, beta);
+  return launch_combine(p, slices, partials, s, e);
 }
 
 #define GEMMF32_SKINNY_TILE(NW, CG, U, S)                                                   \

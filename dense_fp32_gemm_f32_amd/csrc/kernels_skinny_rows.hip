@@ -57,8 +57,7 @@ struct RowsCfg {
 
 template <int CG, int RG, int U, int MQ, bool TA>
 __global__ void __launch_bounds__(CG * RG * 64)
-    skinny_rows_kernel(Problem p, int kslice, int slices, float* __restrict__ part, float alpha,
-                       float beta) {
+    skinny_rows_kernel(Problem p, int kslice, int slices, float* __restrict__ part, Epilogue ep) {
   using Cfg = RowsCfg<CG, RG, MQ>;
   constexpr int MR = Cfg::kRows;
   extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -217,13 +216,10 @@ __global__ void __launch_bounds__(CG * RG * 64)
       const int n = nb + 4 * r;
       if (n >= N) continue;   // N % 4 == 0: the four columns are all in or all out
       if (slices == 1) {
-        // C = alpha * sum + beta * C (C not read when beta == 0)
+        // C = act(alpha * sum + beta * C + bias) (C not read when beta == 0)
         float* d = p.C + (int64_t)m * p.ldc + n;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float v = alpha * acc[h][c][r];
-          d[c] = beta == 0.f ? v : v + beta * d[c];
-        }
+        for (int c = 0; c < 4; ++c) d[c] = epilogue_apply(ep, acc[h][c][r], d + c, n + c);
       } else {
         float* d = part + ((size_t)slice * M + m) * N + n;   // 16-byte aligned: N % 4 == 0
         *reinterpret_cast<floatx4*>(d) =
@@ -257,8 +253,8 @@ SkinnyPlan plan_rows(const Problem& p, int target) {
 }
 
 template <int CG, int RG, int U, int MQ, bool TA>
-hipError_t launch_rows(const Problem& p, const SkinnyPlan& pl, float* partials, float alpha,
-                       float beta, hipStream_t s) {
+hipError_t launch_rows(const Problem& p, const SkinnyPlan& pl, float* partials,
+                       const Epilogue& e, hipStream_t s) {
   using Cfg = RowsCfg<CG, RG, MQ>;
   if (pl.strips <= 0 || pl.splits < 1 || pl.splits > 65535 || p.M > Cfg::kRows || p.batch != 1 ||
       p.N % 4 != 0 || p.ldb % 4 != 0 || (reinterpret_cast<uintptr_t>(p.B) & 15) != 0 ||
@@ -268,13 +264,13 @@ hipError_t launch_rows(const Problem& p, const SkinnyPlan& pl, float* partials, 
   Problem pp = p;
   int kslice = pl.kslice, slices = pl.splits;
   float* part = partials;
-  float a = alpha, b = beta;
-  void* args[] = {&pp, &kslice, &slices, &part, &a, &b};
+  Epilogue ee = e;
+  void* args[] = {&pp, &kslice, &slices, &part, &ee};
   const hipError_t err = hipLaunchKernel(
       reinterpret_cast<const void*>(&skinny_rows_kernel<CG, RG, U, MQ, TA>),
       dim3(pl.strips, pl.splits), dim3(Cfg::kThreads), args, pl.lds_bytes, s);
   if (err != hipSuccess || pl.splits == 1) return err;
-  return launch_combine(p, slices, partials, s, alpha, beta);
+  return launch_combine(p, slices, partials, s, e);
 }
 
 // Name: skinnyr_c<column groups of 256>_r<row groups>_u<quads in flight>_m<rows

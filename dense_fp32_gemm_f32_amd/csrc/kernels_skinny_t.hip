@@ -41,8 +41,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 template <int MR, int JC, int U, bool TA>
 __global__ void __launch_bounds__(kWavesPerGroup * 64)
-    skinny_t_kernel(Problem p, int kslice, int slices, float* __restrict__ part, float alpha,
-                    float beta) {
+    skinny_t_kernel(Problem p, int kslice, int slices, float* __restrict__ part, Epilogue e) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int M = p.M, N = p.N, K = p.K;
@@ -153,8 +152,7 @@ __global__ void __launch_bounds__(kWavesPerGroup * 64)
       if (lane == ((m * JC + c) & 63) && m < M && j < N) {
         if (slices == 1) {
           float* d = p.C + (int64_t)m * p.ldc + j;
-          const float v = alpha * s;
-          *d = beta == 0.f ? v : v + beta * *d;
+          *d = epilogue_apply(e, s, d, j);
         } else {
           part[((size_t)slice * M + m) * N + j] = s;
         }
@@ -184,21 +182,21 @@ SkinnyPlan plan_t(const Problem& p, int target) {
 }
 
 template <int MR, int JC, int U, bool TA>
-hipError_t launch_t(const Problem& p, const SkinnyPlan& pl, float* partials, float alpha,
-                    float beta, hipStream_t s) {
+hipError_t launch_t(const Problem& p, const SkinnyPlan& pl, float* partials,
+                    const Epilogue& e, hipStream_t s) {
   if (pl.strips <= 0 || pl.splits < 1 || pl.splits > 65535 || p.M > MR || p.batch != 1)
     return hipErrorInvalidConfiguration;
   if (pl.splits > 1 && !partials) return hipErrorInvalidValue;
   Problem pp = p;
   int kslice = pl.kslice, slices = pl.splits;
   float* part = partials;
-  float a = alpha, b = beta;
-  void* args[] = {&pp, &kslice, &slices, &part, &a, &b};
+  Epilogue ee = e;
+  void* args[] = {&pp, &kslice, &slices, &part, &ee};
   const hipError_t err = hipLaunchKernel(
       reinterpret_cast<const void*>(&skinny_t_kernel<MR, JC, U, TA>),
       dim3(pl.strips, pl.splits), dim3(kWavesPerGroup * 64), args, 0, s);
   if (err != hipSuccess || pl.splits == 1) return err;
-  return launch_combine(p, slices, partials, s, alpha, beta);
+  return launch_combine(p, slices, partials, s, e);
 }
 
 // Name: skinnyt_m<rows>_j<columns per wave>_u<chunks in flight>_<nt|tt>.

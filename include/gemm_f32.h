@@ -61,7 +61,11 @@
 extern "C" {
 #endif
 
-#define GEMM_F32_VERSION 3
+#define GEMM_F32_VERSION 4
+
+/* Activations of gemm_f32_fused. */
+#define GEMM_F32_ACT_NONE 0
+#define GEMM_F32_ACT_RELU 1   /* relu(x) = (x < 0 ? +0 : x): NaN stays NaN */
 
 /* Largest accepted M, N or K (2^31 - 2^16: tile arithmetic stays in int32). */
 #define GEMM_F32_MAX_DIM INT64_C(2147418112)
@@ -76,7 +80,8 @@ enum gemm_f32_status {
   GEMM_F32_ERR_WORKSPACE = 6,     /* scratch workspace could not be allocated */
   GEMM_F32_ERR_LAUNCH = 7,        /* the kernel launch reported an error */
   GEMM_F32_ERR_BAD_KERNEL = 8,    /* unknown kernel index, or one that cannot run these arguments */
-  GEMM_F32_ERR_POINTER = 9        /* A, B or C not 4-byte aligned, or not memory the current device can access */
+  GEMM_F32_ERR_POINTER = 9,       /* A, B or C not 4-byte aligned, or not memory the current device can access */
+  GEMM_F32_ERR_INVALID_ARG = 10   /* an activation other than GEMM_F32_ACT_NONE / _RELU */
 };
 
 /*
@@ -123,6 +128,31 @@ int gemm_f32_ex(int transA, int transB,
                 float beta,
                 float *C, int64_t ldc,
                 void *stream);
+
+/*
+ * gemm_f32_fused -- C = act(alpha * op(A) op(B) + beta * C + bias) in one
+ * pass: gemm_f32_ex with a bias row vector and an activation applied in the
+ * kernel's epilogue, so the product never makes a second trip through HBM
+ * ("GPU compute shaders", Performance: fuse kernels, one memory pass fewer).
+ * bias: N floats, device memory, bias[j] added to every row's column j (NULL
+ * for none; 4-byte aligned, not inside C's window, else GEMM_F32_ERR_POINTER /
+ * GEMM_F32_ERR_ALIAS).  activation: GEMM_F32_ACT_NONE or GEMM_F32_ACT_RELU
+ * (else GEMM_F32_ERR_INVALID_ARG), applied last.  The fp32 update per element
+ * is v = alpha * s; v += beta * C (only when beta != 0); v += bias[j]; then
+ * act(v).  K == 0 gives act(alpha * 0 + beta * C + bias).  Runs the
+ * extended-operation kernels (or, for M <= 16, the skinny kernels); with no
+ * bias and no activation it is exactly gemm_f32_ex.  Other arguments, checks
+ * and errors as gemm_f32_ex.
+ */
+int gemm_f32_fused(int transA, int transB,
+                   int64_t M, int64_t N, int64_t K,
+                   float alpha,
+                   const float *A, int64_t lda,
+                   const float *B, int64_t ldb,
+                   float beta,
+                   float *C, int64_t ldc,
+                   const float *bias, int activation,
+                   void *stream);
 
 /*
  * gemm_f32_batched -- `batch` independent products C_b = A_b x B_b, 0 <= b <
@@ -254,6 +284,20 @@ int gemm_f32_run_kernel_ex(int index, int transA, int transB,
                            float beta,
                            float *C, int64_t ldc,
                            void *stream);
+
+/*
+ * gemm_f32_run_kernel_fused -- gemm_f32_run_kernel_ex with gemm_f32_fused's
+ * bias and activation (the same kernels take them).
+ */
+int gemm_f32_run_kernel_fused(int index, int transA, int transB,
+                              int64_t M, int64_t N, int64_t K,
+                              float alpha,
+                              const float *A, int64_t lda,
+                              const float *B, int64_t ldb,
+                              float beta,
+                              float *C, int64_t ldc,
+                              const float *bias, int activation,
+                              void *stream);
 
 /*
  * gemm_f32_release_workspaces -- free every scratch workspace the library

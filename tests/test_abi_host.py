@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert binding.gemm_f32_version() == 3
+    assert binding.gemm_f32_version() == 4
 
 
 def test_status_strings():
@@ -301,3 +301,31 @@ def test_reduce_sum_argument_errors_before_any_device_call():
     assert f(10, P16, R16 + 1, 0) == 9
     assert f(10, P16, P16 + 36, 0) == 4  # out is the last element of x
     assert f(10, P16, P16 + 40, 0) != 4  # right after x: not an alias
+
+
+# ---- fused epilogue (gemm_f32_fused) ---------------------------------------------
+
+def test_fused_argument_errors_before_any_device_call():
+    f = binding.gemm_f32_fused
+    # unknown activation
+    assert f(0, 0, 4, 4, 4, 1.0, P16, 4, Q16, 4, 0.0, R16, 4, 0, 2, 0) == 10
+    assert f(0, 0, 4, 4, 4, 1.0, P16, 4, Q16, 4, 0.0, R16, 4, 0, -1, 0) == 10
+    # misaligned bias; bias inside C's window
+    assert f(0, 0, 4, 4, 4, 1.0, P16, 4, Q16, 4, 0.0, R16, 4, R16 + 0x100002, 1, 0) == 9
+    assert f(0, 0, 4, 4, 4, 1.0, P16, 4, Q16, 4, 0.0, R16, 4, R16 + 16, 1, 0) == 4
+    # the checks of gemm_f32_ex come first
+    assert f(0, 0, -1, 4, 4, 1.0, P16, 4, Q16, 4, 0.0, R16, 4, 0, 7, 0) == 1
+    # empty products succeed without a device
+    assert f(0, 0, 0, 4, 4, 1.0, P16, 4, Q16, 4, 0.0, R16, 4, 0, 1, 0) == 0
+
+
+def test_fused_selects_the_extended_kernels():
+    """With a bias or an activation the product is not plain: gemm_f32_fused
+    runs what gemm_f32_ex runs for alpha, beta other than 1, 0 (the kernel
+    choice does not depend on the bias or activation)."""
+    names = binding.kernel_names()
+    assert any(n.startswith("mfmaex_") for n in names)
+    # run_kernel_fused refuses the plain-only kernels for a fused update
+    plain = names.index("mfma_64x64x32_w32x32_p5_vec")
+    assert binding.gemm_f32_run_kernel_fused(plain, 0, 0, 4, 4, 4, 1.0, P16, 4, Q16, 4, 0.0,
+                                             R16, 4, 0, 1, 0) in (5, 8)
