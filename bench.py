@@ -144,6 +144,34 @@ def sum_bandwidth(stream, steps, warmup, n=2 ** 26, copies=4):
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def fused_epilogue(stream, steps, warmup):
+    """4096^3 with a bias row and ReLU: gemm_f32_fused (applied as C is stored)
+    against gemm_f32 followed by a separate bias + ReLU pass over C (torch
+    elementwise ops, one more read and write of the 64 MiB C)."""
+    import torch
+    from dense_fp32_gemm_f32_amd import binding, inputs
+    w = inputs.WORKLOADS[inputs.HEADLINE]
+    A_cpu, B_cpu = inputs.workload_inputs(w)
+    A, B = A_cpu.cuda(), B_cpu.cuda()
+    C = torch.empty((w.M, w.N), device="cuda")
+    bias = inputs.uniform_matrix(1, w.N, 1400).reshape(-1).cuda()
+
+    def fused(_i):
+        binding.gemm_fused(A, B, C, bias=bias, act=binding.ACT_RELU)
+
+    def separate(_i):
+        binding.gemm(A, B, C)
+        torch.relu_(C.add_(bias))
+
+    out = {"kernel": binding.selected_kernel_ex(A, B, C, alpha=1.0, beta=0.0)}
+    for name, fn in (("fused", fused), ("gemm_then_bias_relu", separate)):
+        _, per = time_launches(fn, steps, warmup, stream)
+        mean_ms = sum(per) / len(per)
+        out[name] = {"ms": round(mean_ms, 4),
+                     "TFLOP/s": round(w.flops / (mean_ms * 1e-3) / 1e12, 2)}
+    return out
+
+
 def cpu_baseline(w, target_s):
     """The oracle on the first R rows of A; R sized from a short probe."""
     import numpy as np
@@ -330,6 +358,8 @@ def main():
             stream, max(args.steps, 20), args.warmup)
         result["secondary"]["sum_2^26"] = sum_bandwidth(stream, max(args.steps, 20),
                                                         args.warmup)
+        result["secondary"]["fused_bias_relu_4096"] = fused_epilogue(stream, args.steps,
+                                                                     args.warmup)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

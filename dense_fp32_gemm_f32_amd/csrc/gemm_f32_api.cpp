@@ -281,15 +281,16 @@ bool accepts(const Entry& e, const Op& op, int64_t M, int64_t N, int64_t K, int6
     }
     return true;
   }
-  // every other kernel computes the plain product C = A B
-  if (!op.plain()) return false;
   if (e.kind == Kind::Mfma || e.kind == Kind::MfmaSplitK) {
+    // A and B as stored; any epilogue
+    if (op.ta || op.tb) return false;
     const auto& v = gemmf32::mfma_variant(e.sub);
     if (!v.lds_dma) return true;
     return K % v.bk == 0 && lda % 4 == 0 && ldb % 4 == 0 && N % 4 == 0 && aligned16(A) &&
            aligned16(B);
   }
-  return true;
+  // the reference kernel computes the plain product only
+  return op.plain();
 }
 bool entry_accepts(const Entry& e, const Op& op, const Problem& p) {
   return accepts(e, op, p.M, p.N, p.K, p.lda, p.ldb, p.A, p.B);
@@ -311,7 +312,7 @@ int run_entry(const Entry& e, const Op& op, const Problem& p, int dev, hipStream
         const int rc = get_workspace(dev, s, (size_t)pl.slices * p.M * p.N, &partials);
         if (rc != GEMM_F32_OK) return rc;
       }
-      err = v.launch(p, pl.slices, pl.kchunk, partials, s);
+      err = v.launch(p, pl.slices, pl.kchunk, partials, op.epilogue(), s);
       break;
     }
     case Kind::Skinny: {
@@ -360,10 +361,14 @@ std::string select_name(const Op& op, int64_t M, int64_t N, int64_t K, int64_t l
       const int idx = find_entry(row.kernel);
       if (idx >= 0 && accepts(entries()[idx], op, M, N, K, lda, ldb, A, B)) return row.kernel;
     }
+    // a transposed operand: the extended-operation tiles; A and B as stored
+    // (an epilogue only): the plain table below, whose kernels take it
     static const char* const kLayout[2][2] = {{"_nn", "_nt"}, {"_tn", "_tt"}};
-    for (const auto& row : gemmf32::kTuningGfx950Ex) {
-      if (tiles < row.min_tiles) continue;
-      return std::string(row.kernel) + kLayout[op.ta][op.tb];
+    if (op.ta || op.tb) {
+      for (const auto& row : gemmf32::kTuningGfx950Ex) {
+        if (tiles < row.min_tiles) continue;
+        return std::string(row.kernel) + kLayout[op.ta][op.tb];
+      }
     }
   }
   for (const auto& row : gemmf32::kTuningGfx950) {

@@ -70,7 +70,9 @@ struct MfmaVariant {
   // Direct global -> LDS loads.  These need A and B 16-byte aligned, lda, ldb
   // and N multiples of 4 and K a multiple of bk.
   bool lds_dma;
-  hipError_t (*launch)(const Problem&, int slices, int kchunk, float* partials, hipStream_t);
+  // e: the update written to C (applied by the combine when K is split)
+  hipError_t (*launch)(const Problem&, int slices, int kchunk, float* partials, const Epilogue& e,
+                       hipStream_t);
 };
 int mfma_variant_count();          // both kinds below
 const MfmaVariant& mfma_variant(int i);

@@ -49,7 +49,7 @@ using namespace mfma;
 template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB, int kMinWaves, int SCHED>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     __attribute__((amdgpu_waves_per_eu(kMinWaves)))
-    mfma_gemm_kernel(Problem p, int tiles_m, int tiles_n, int kchunk, float* part) {
+    mfma_gemm_kernel(Problem p, int tiles_m, int tiles_n, int kchunk, float* part, Epilogue ep) {
   using C_ = Cfg<BM, BN, BK, WM, WN>;
   __shared__ __attribute__((aligned(16))) float lds_a[2][C_::kLdsA];
   __shared__ __attribute__((aligned(16))) float lds_b[2][C_::kLdsB];
@@ -462,7 +462,11 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = rbase + 8 * (r >> 2) + (r & 3);
-          if (row < M) p.C[(int64_t)row * p.ldc + col] = acc[i][j][r];
+          if (row < M) {
+            // a K slice writes its raw partial sum; the combine applies the update
+            float* c = p.C + (int64_t)row * p.ldc + col;
+            *c = part ? acc[i][j][r] : epilogue_apply(ep, acc[i][j][r], c, col);
+          }
         }
       }
     }
@@ -470,7 +474,8 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool VA, bool VB, int kMinWaves, int SCHED>
-hipError_t launch(const Problem& p, int slices, int kchunk, float* partials, hipStream_t s) {
+hipError_t launch(const Problem& p, int slices, int kchunk, float* partials, const Epilogue& e,
+                      hipStream_t s) {
   using C_ = Cfg<BM, BN, BK, WM, WN>;
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + BN - 1) / BN;
@@ -487,13 +492,14 @@ hipError_t launch(const Problem& p, int slices, int kchunk, float* partials, hip
   Problem pp = p;
   int tm = tiles_m, tn = tiles_n, kc = kchunk;
   float* part = slices > 1 ? partials : nullptr;
-  void* args[] = {&pp, &tm, &tn, &kc, &part};
+  Epilogue ee = e;
+  void* args[] = {&pp, &tm, &tn, &kc, &part, &ee};
   const hipError_t err = hipLaunchKernel(
       reinterpret_cast<const void*>(
           &mfma_gemm_kernel<BM, BN, BK, WM, WN, VA, VB, kMinWaves, SCHED>),
       dim3((unsigned)(tiles * slices), 1, (unsigned)p.batch), dim3(C_::kThreads), args, 0, s);
   if (err != hipSuccess || slices == 1) return err;
-  return launch_combine(p, slices, partials, s);
+  return launch_combine(p, slices, partials, s, e);
 }
 
 #define GEMMF32_MFMA_S(BM, BN, BK, WM, WN, MW, SC, TAG)                                      \

@@ -183,7 +183,7 @@ __device__ __forceinline__ void dma_k_loop(float* lds_a0, float* lds_b0, float* 
 template <int BM, int BN, int BK, int WM, int WN, int kMinWaves>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     __attribute__((amdgpu_waves_per_eu(kMinWaves)))
-    mfma_dma_kernel(Problem p, int tiles_m, int tiles_n, int kchunk, float* part) {
+    mfma_dma_kernel(Problem p, int tiles_m, int tiles_n, int kchunk, float* part, Epilogue ep) {
   using C_ = Cfg<BM, BN, BK, WM, WN>;
   constexpr int kWaves = C_::kThreads / 64;
   __shared__ __attribute__((aligned(16))) float lds_a0[C_::kLdsA];
@@ -258,7 +258,11 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = rbase + 8 * (r >> 2) + (r & 3);
-          if (row < M) p.C[(int64_t)row * p.ldc + col] = acc[i][j][r];
+          if (row < M) {
+            // a K slice writes its raw partial sum; the combine applies the update
+            float* c = p.C + (int64_t)row * p.ldc + col;
+            *c = part ? acc[i][j][r] : epilogue_apply(ep, acc[i][j][r], c, col);
+          }
         }
       }
     }
@@ -266,7 +270,8 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int kMinWaves>
-hipError_t launch_dma(const Problem& p, int slices, int kchunk, float* partials, hipStream_t s) {
+hipError_t launch_dma(const Problem& p, int slices, int kchunk, float* partials, const Epilogue& e,
+                      hipStream_t s) {
   using C_ = Cfg<BM, BN, BK, WM, WN>;
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + BN - 1) / BN;
@@ -287,12 +292,13 @@ hipError_t launch_dma(const Problem& p, int slices, int kchunk, float* partials,
   Problem pp = p;
   int tm = tiles_m, tn = tiles_n, kc = kchunk;
   float* part = slices > 1 ? partials : nullptr;
-  void* args[] = {&pp, &tm, &tn, &kc, &part};
+  Epilogue ee = e;
+  void* args[] = {&pp, &tm, &tn, &kc, &part, &ee};
   const hipError_t err = hipLaunchKernel(
       reinterpret_cast<const void*>(&mfma_dma_kernel<BM, BN, BK, WM, WN, kMinWaves>),
       dim3((unsigned)(tiles * slices), 1, (unsigned)p.batch), dim3(C_::kThreads), args, 0, s);
   if (err != hipSuccess || slices == 1) return err;
-  return launch_combine(p, slices, partials, s);
+  return launch_combine(p, slices, partials, s, e);
 }
 
 #define GEMMF32_MFMA_DMA(BM, BN, BK, WM, WN, MW)                                          \

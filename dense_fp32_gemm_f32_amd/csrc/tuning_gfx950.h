@@ -48,9 +48,10 @@ constexpr TuningRow kTuningGfx950[] = {
     {kAnyM, 0, "mfma_64x64x16_w32x32_sk_veca"},
 };
 
-// C = alpha * op(A) op(B) + beta * C with a transposed operand or alpha, beta
-// other than 1, 0: the first row with at least min_tiles tiles of 128 x 128
-// names the tile; the layout suffix (_nn, _nt, _tn, _tt) comes from the call.
+// A transposed operand (any epilogue): the first row with at least min_tiles
+// tiles of 128 x 128 names the tile; the layout suffix (_nt, _tn, _tt) comes
+// from the call.  A and B as stored with an epilogue (alpha, beta, bias,
+// activation) use the plain table above: its kernels apply the epilogue.
 struct TuningRowEx {
   int64_t min_tiles;
   const char* kernel;
@@ -61,8 +62,8 @@ constexpr TuningRowEx kTuningGfx950Ex[] = {
     {0, "mfmaex_64x64x32_w32x32"},
 };
 
-// M <= 16 with a transposed operand or alpha, beta other than 1, 0: the first
-// row whose max_m and layout match (ta: A stored K x M, tb: B stored N x K).
+// M <= 16 with a transposed operand or an epilogue: the first row whose max_m
+// and layout match (ta: A stored K x M, tb: B stored N x K).
 struct TuningRowSkinny {
   int64_t max_m;
   bool ta, tb;

@@ -115,10 +115,11 @@ int gemm_f32(int64_t M, int64_t N, int64_t K,
  * The pages define only C = A x B; the transposed operands follow the
  * pre-transposed B of "Optimizing a WebGPU Matmul Kernel using Subgroups"
  * (section 7) and the BLAS convention, alpha and beta a fused epilogue (one
- * memory pass fewer, "GPU compute shaders", Performance section).  The plain
- * case (transA = transB = 0, alpha = 1, beta = 0) runs exactly what gemm_f32
- * runs.  Same checks and errors as gemm_f32, with the pitches checked against
- * the stored shapes.
+ * memory pass fewer, "GPU compute shaders", Performance section).  With A and
+ * B as stored it runs the kernels gemm_f32 picks for the shape, which apply
+ * alpha and beta as they store C (exactly gemm_f32 when alpha = 1, beta = 0);
+ * a transposed operand runs the extended-operation kernels.  Same checks and
+ * errors as gemm_f32, with the pitches checked against the stored shapes.
  */
 int gemm_f32_ex(int transA, int transB,
                 int64_t M, int64_t N, int64_t K,
@@ -139,10 +140,11 @@ int gemm_f32_ex(int transA, int transB,
  * GEMM_F32_ERR_ALIAS).  activation: GEMM_F32_ACT_NONE or GEMM_F32_ACT_RELU
  * (else GEMM_F32_ERR_INVALID_ARG), applied last.  The fp32 update per element
  * is v = alpha * s; v += beta * C (only when beta != 0); v += bias[j]; then
- * act(v).  K == 0 gives act(alpha * 0 + beta * C + bias).  Runs the
- * extended-operation kernels (or, for M <= 16, the skinny kernels); with no
- * bias and no activation it is exactly gemm_f32_ex.  Other arguments, checks
- * and errors as gemm_f32_ex.
+ * act(v).  K == 0 gives act(alpha * 0 + beta * C + bias).  A and B as stored
+ * run the kernels gemm_f32 picks (the epilogue is part of every tile
+ * kernel's store, and of the combine when K is split); a transposed operand
+ * runs the extended-operation kernels.  With no bias and no activation it is
+ * exactly gemm_f32_ex.  Other arguments, checks and errors as gemm_f32_ex.
  */
 int gemm_f32_fused(int transA, int transB,
                    int64_t M, int64_t N, int64_t K,

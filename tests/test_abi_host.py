@@ -198,6 +198,10 @@ def test_ex_dispatcher_picks_the_layout_kernel(ta, tb):
             assert name.startswith("skinny"), name
             if (ta, tb) != (0, 0):
                 assert name.endswith(LAYOUTS[(ta, tb)]), name
+        elif (ta, tb) == (0, 0):
+            # A and B as stored: the plain table's kernel, which applies the epilogue
+            assert name == binding.gemm_f32_selected_kernel(M, N, K, lda, ldb, N, P16, Q16,
+                                                            R16), name
         else:
             assert name.startswith("mfmaex_") and name.endswith(LAYOUTS[(ta, tb)]), name
 
@@ -207,11 +211,11 @@ def test_ex_plain_case_runs_what_gemm_f32_runs():
         plain = binding.gemm_f32_selected_kernel(M, N, K, K, N, N, P16, Q16, R16)
         ex = binding.gemm_f32_selected_kernel_ex(0, 0, M, N, K, K, N, N, 1.0, 0.0, P16, Q16, R16)
         assert plain == ex
-        # alpha or beta other than 1, 0: the extended MFMA kernel, or for M <= 16
-        # the skinny kernel (whose epilogue takes alpha and beta)
-        name = binding.gemm_f32_selected_kernel_ex(0, 0, M, N, K, K, N, N, 2.0, 0.0, P16, Q16,
+        # alpha or beta other than 1, 0 with A and B as stored: the same kernel,
+        # whose store applies the epilogue
+        name = binding.gemm_f32_selected_kernel_ex(0, 0, M, N, K, K, N, N, 2.0, 0.5, P16, Q16,
                                                    R16)
-        assert name.startswith("skinny_" if M <= 16 else "mfmaex_"), name
+        assert name == plain, (name, plain)
 
 
 def test_ex_pitches_are_checked_against_the_stored_shapes():

@@ -161,3 +161,41 @@ def test_fused_full_size(gpu_lib):
                                       C_in=Cin.numpy(), bias=bias.numpy(), act=RELU)
     ratio = H.assert_within_tol(C.cpu().numpy(), C_ref, ABS, "fused 4096^3")
     print(f"fused 4096^3: max |dC| / scale = {ratio:.3e}")
+
+
+def _plain_kernels():
+    """The tile kernels of the plain table (A and B as stored), whose store
+    applies the epilogue (and, when K is split, the combine)."""
+    try:
+        from dense_fp32_gemm_f32_amd import binding
+        return [n for n in binding.kernel_names() if n.startswith("mfma_")]
+    except Exception:  # library not built: the fixture fails the test loudly
+        return ["<library missing>"]
+
+
+@pytest.mark.parametrize("kname", _plain_kernels())
+def test_every_plain_kernel_with_epilogue(gpu_lib, kname):
+    from tests.test_gpu_parity import _kernel_case
+    M, N, K, lda, ldb = _kernel_case(kname)
+    for integer, (alpha, beta, act, seed) in [(True, (2.0, -1.0, RELU, 7611)),
+                                              (False, (1.5, 0.5, RELU, 7613))]:
+        dist = "int2" if integer else "u11"
+        A, B = inputs.make_ab(M, N, K, dist, dist, seed, lda=lda, ldb=ldb)
+        ldc = N + 5
+        Cd, flat = H.sentinel_output(M, N, ldc)
+        Cin = (inputs.int_matrix(M, N, seed + 7, -5, 5) if integer
+               else inputs.uniform_matrix(M, N, seed + 7))
+        Cd.copy_(Cin.to("cuda"))
+        bias = (inputs.int_matrix(1, N, seed + 11, -9, 9) if integer
+                else inputs.uniform_matrix(1, N, seed + 11)).reshape(-1)
+        H.say(f"fused plain kernel {kname} M={M} N={N} K={K} int={integer}")
+        gpu_lib.gemm_fused(H.to_device(A), H.to_device(B), Cd, alpha=alpha, beta=beta,
+                           bias=bias.cuda(), act=act, kernel=kname)
+        torch.cuda.synchronize()
+        C_ref, _, ABS = oracle.gemm_fused(A.numpy(), B.numpy(), alpha=alpha, beta=beta,
+                                          C_in=Cin.numpy(), bias=bias.numpy(), act=act)
+        if integer:
+            H.assert_bitexact(Cd.cpu().numpy(), C_ref, kname)
+        else:
+            H.assert_within_tol(Cd.cpu().numpy(), C_ref, ABS, kname)
+        H.check_outside_untouched(flat, M, N, ldc)
