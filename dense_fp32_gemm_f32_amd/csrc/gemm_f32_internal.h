@@ -74,10 +74,12 @@ struct MfmaVariant {
   hipError_t (*launch)(const Problem&, int slices, int kchunk, float* partials, const Epilogue& e,
                        hipStream_t);
 };
-int mfma_variant_count();          // both kinds below
+int mfma_variant_count();          // all three kinds below
 const MfmaVariant& mfma_variant(int i);
 int mfma_dma_variant_count();      // the direct-to-LDS kernels
 const MfmaVariant& mfma_dma_variant(int i);
+int mfma_small_variant_count();    // fragments from global memory, K split over waves
+const MfmaVariant& mfma_small_variant(int i);
 
 // ---- MFMA kernel for C = alpha * op(A) op(B) + beta * C ------------------
 // trans_a: A stored K x M (op(A) = A^T); trans_b: B stored N x K.  The

@@ -555,11 +555,15 @@ const MfmaVariant kVariants[] = {
 }  // namespace
 
 int mfma_variant_count() {
-  return (int)(sizeof(kVariants) / sizeof(kVariants[0])) + mfma_dma_variant_count();
+  return (int)(sizeof(kVariants) / sizeof(kVariants[0])) + mfma_dma_variant_count() +
+         mfma_small_variant_count();
 }
 const MfmaVariant& mfma_variant(int i) {
   const int n = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
-  return i < n ? kVariants[i] : mfma_dma_variant(i - n);
+  if (i < n) return kVariants[i];
+  i -= n;
+  if (i < mfma_dma_variant_count()) return mfma_dma_variant(i);
+  return mfma_small_variant(i - mfma_dma_variant_count());
 }
 
 }  // namespace gemmf32

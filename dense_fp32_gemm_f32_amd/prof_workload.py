@@ -25,6 +25,8 @@ def main(argv=None):
     ap.add_argument("--copies", type=int, default=0,
                     help="rotate this many input copies (0: 4 when B exceeds 128 MiB)")
     ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--torch", action="store_true",
+                    help="run torch.matmul in fp32 (the vendor library, for comparison) instead")
     ap.add_argument("--reduce", type=int, default=0,
                     help="run reduce_sum_f32 on this many floats (4 copies) instead of a GEMM")
     args = ap.parse_args(argv)
@@ -53,6 +55,14 @@ def main(argv=None):
         As.append(a.contiguous().to(dev))
         Bs.append(b.contiguous().to(dev))
         Cs.append(torch.empty((w.M, w.N), device=dev))
+    if args.torch:
+        torch.backends.cuda.matmul.allow_tf32 = False
+        print(f"workload {w.name}: torch.matmul, {args.reps} launches", flush=True)
+        for i in range(args.reps):
+            torch.matmul(As[i % copies], Bs[i % copies], out=Cs[i % copies])
+        torch.cuda.synchronize()
+        _calibration_copy(dev, args.copy_mib)
+        return 0
     name = args.kernel or binding.selected_kernel(As[0], Bs[0], Cs[0])
     print(f"workload {w.name}: kernel {name}, {args.reps} launches over {copies} input copies",
           flush=True)

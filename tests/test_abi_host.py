@@ -113,7 +113,8 @@ def test_adjacent_but_not_overlapping_is_not_alias():
     (6144, 6144, 4096, 4096, 6144, P16, Q16, "mfma_128x256x16_w64x128_d6"),
     (4096, 4097, 4096, 4096, 4097, P16, Q16, "mfma_256x128x16_w128x64_p5"),
     (2047, 3001, 1531, 1531, 3001, P16, Q16, "mfma_64x64x32_w32x32_p5"),
-    (512, 512, 512, 512, 512, P16, Q16, "mfma_64x64x32_w32x32_d6_sk"),
+    (512, 512, 512, 512, 512, P16, Q16, "mfma_32x32x8_k4_g4_small"),
+    (768, 768, 768, 768, 768, P16, Q16, "mfma_64x64x32_w32x32_d6"),
     (1024, 1024, 1024, 1024, 1024, P16, Q16, "mfma_64x64x32_w32x32_d6"),
 ])
 def test_dispatcher_families(M, N, K, lda, ldb, A, B, expect):
@@ -146,7 +147,7 @@ def test_direct_to_lds_kernels_only_for_aligned_operands():
     sel = binding.gemm_f32_selected_kernel
     assert "_d6_" in sel(4096, 4096, 4096, 4096, 4096, 4096, P16, Q16, R16)
     assert "_d6_" in sel(1024, 1024, 1024, 1024, 1024, 1024, P16, Q16, R16)
-    assert "_d6_" in sel(512, 512, 512, 512, 512, 512, P16, Q16, R16)
+    assert "_d6_" in sel(768, 768, 768, 768, 768, 768, P16, Q16, R16)
     for args in [(4096, 4096, 4096, 4097, 4096, 4096, P16, Q16),      # lda % 4
                  (4096, 4096, 4096, 4096, 4098, 4096, P16, Q16),      # ldb % 4
                  (4096, 4095, 4096, 4096, 4096, 4096, P16, Q16),      # N % 4
