@@ -9,7 +9,7 @@
 //  pass 1: G groups (G and the chunk length depend on n only), group g owns
 //          the contiguous chunk [g c, min(n, (g + 1) c)) (c a multiple of 4).
 //          Thread t keeps four running sums, one per float4 component, over
-//          the float4s t, t + 256, ... of the chunk (8 loads in flight,
+//          the float4s t, t + 256, ... of the chunk (16 loads in flight,
 //          non-temporal); then (s0 + s1) + (s2 + s3), a butterfly across the
 //          wave (xor 32, 16, ..., 1: fp addition commutes, so every lane ends
 //          with the same value), and the four waves in LDS in wave order.
@@ -31,7 +31,7 @@ namespace {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;             // 4 waves
-constexpr int kUnroll = 8;                // float4 loads in flight per thread
+constexpr int kUnroll = 16;               // float4 loads in flight per thread (16 KiB per wave)
 constexpr int kMaxGroups = 256;           // one per CU of MI355X
 constexpr int64_t kMinPerGroup = 16384;   // elements; smaller arrays use fewer groups
 
