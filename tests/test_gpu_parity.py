@@ -140,7 +140,10 @@ def test_every_kernel_variant(gpu_lib, kname):
 
 
 @pytest.mark.parametrize("shape", [(33, 129, 2000), (512, 512, 512), (1, 64, 4096),
-                                   (200, 70, 1031), (1024, 1024, 1024)])
+                                   (200, 70, 1031), (1024, 1024, 1024),
+                                   # very deep K, and one-column / one-row products
+                                   (40, 50, 300000), (64, 64, 262144), (1000, 1, 1000),
+                                   (1, 1000, 5000), (17, 1, 70000)])
 def test_split_k_through_dispatcher(gpu_lib, shape):
     """Grids too small to fill the GPU take the K-split MFMA path; its slice
     partials are summed in a fixed order, so reruns are bitwise identical."""
