@@ -341,13 +341,16 @@ int run_entry(const Entry& e, const Op& op, const Problem& p, int dev, hipStream
 }
 
 // ---- the dispatcher ---------------------------------------------------------
-// Do the workgroups of an MFMA entry (over `batch` products) fill whole waves
-// of the CUs, or at least four waves?
-bool fills_whole_waves(const Entry& e, int64_t M, int64_t N, int64_t batch) {
+// Do the workgroups of an MFMA entry (over `batch` products), `slots` of them
+// resident per CU, leave the last wave at least 90 % full, or make four waves
+// or more?  (w waves of work take ceil(w) waves of time.)
+bool fills_waves(const Entry& e, int64_t M, int64_t N, int64_t batch, int slots) {
   if (e.kind != Kind::Mfma && e.kind != Kind::MfmaSplitK) return true;
   const auto& v = gemmf32::mfma_variant(e.sub);
   const int64_t wgs = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn) * batch;
-  return wgs % gemmf32::kNumCus == 0 || wgs >= 4 * gemmf32::kNumCus;
+  const int64_t per_wave = gemmf32::kNumCus * slots;
+  const int64_t waves = (wgs + per_wave - 1) / per_wave;
+  return waves >= 4 || 10 * wgs >= 9 * waves * per_wave;
 }
 
 std::string select_name(const Op& op, int64_t M, int64_t N, int64_t K, int64_t lda,
@@ -376,7 +379,7 @@ std::string select_name(const Op& op, int64_t M, int64_t N, int64_t K, int64_t l
     // a row whose kernel cannot take these arguments defers to the next one
     const int idx = find_entry(row.kernel);
     if (idx < 0 || !accepts(entries()[idx], op, M, N, K, lda, ldb, A, B)) continue;
-    if (row.whole_waves && !fills_whole_waves(entries()[idx], M, N, 1)) continue;
+    if (row.wave_slots > 0 && !fills_waves(entries()[idx], M, N, 1, row.wave_slots)) continue;
     return row.kernel;
   }
   return "ref_naive";
@@ -514,7 +517,8 @@ std::string select_name_batched(int64_t M, int64_t N, int64_t K, int64_t lda, in
     if (!accepts(entries()[idx], Op{}, M, N, K, lda, ldb, A, B)) continue;
     if (gemmf32::mfma_variant(entries()[idx].sub).lds_dma && (bt.sa % 4 != 0 || bt.sb % 4 != 0))
       continue;
-    if (row.whole_waves && !fills_whole_waves(entries()[idx], M, N, bt.count)) continue;
+    if (row.wave_slots > 0 && !fills_waves(entries()[idx], M, N, bt.count, row.wave_slots))
+      continue;
     return row.kernel;
   }
   // the rows above always end in a kernel that takes any operands

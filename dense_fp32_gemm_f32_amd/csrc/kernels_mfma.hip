@@ -550,6 +550,12 @@ const MfmaVariant kVariants[] = {
     GEMMF32_MFMA_S(128, 64, 64, 64, 32, 1, 5, "_p5"),
     GEMMF32_MFMA_S(64, 64, 64, 32, 32, 2, 5, "_p5"),
     GEMMF32_MFMA_S(64, 64, 32, 32, 32, 4, 5, "_p5"),
+    GEMMF32_MFMA_S(128, 192, 16, 64, 96, 1, 5, "_p5"),
+    GEMMF32_MFMA_S(128, 192, 32, 64, 96, 1, 5, "_p5"),
+    GEMMF32_MFMA_S(128, 192, 32, 32, 96, 2, 5, "_p5"),
+    GEMMF32_MFMA_S(256, 192, 16, 128, 96, 1, 5, "_p5"),
+    GEMMF32_MFMA_S(192, 128, 32, 96, 32, 2, 5, "_p5"),
+    GEMMF32_MFMA_S(128, 192, 32, 32, 96, 2, 3, "_p3"),
 };
 
 }  // namespace

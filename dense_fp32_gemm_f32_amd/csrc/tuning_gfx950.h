@@ -1,9 +1,9 @@
 // Tuning table for gfx950 (MI355X): which kernel gemm_f32 runs for a shape.
 //
 // The first row whose bounds hold and whose kernel can take the arguments
-// wins.  Rows come in pairs: the kernel with direct-to-LDS loads (needs
-// 16-byte aligned A and B, lda, ldb and N multiples of 4 and K a multiple of
-// its K-tile), then the register-staged kernel that takes any 4-byte aligned
+// wins.  At each size the kernels with direct-to-LDS loads (16-byte aligned A
+// and B, lda, ldb and N multiples of 4, K a multiple of the K-tile) come
+// first, then the register-staged kernels that take any 4-byte aligned
 // operands.  The choices are the fastest measured per shape class with
 // dense_fp32_gemm_f32_amd/tune.py.
 //
@@ -11,9 +11,10 @@
 //   max_m        the row applies when M <= max_m
 //   min_tiles    ... and the grid of 128 x 128 tiles has at least this many tiles
 //   kernel       a name in the kernel table
-//   whole_waves  ... and (if set) the kernel's own workgroups fill whole waves of
-//                the 256 CUs (a multiple of 256, or at least 4 waves), so a
-//                large tile leaves no part-empty last wave
+//   wave_slots   ... and (if not 0) the kernel's own workgroups, wave_slots of
+//                them resident per CU, fill their last wave of the 256 CUs to
+//                at least 90 % or make 4 waves or more: a large tile is taken
+//                only where it leaves no part-empty last wave
 #pragma once
 
 #include <cstdint>
@@ -26,7 +27,7 @@ struct TuningRow {
   int64_t max_m;
   int64_t min_tiles;
   const char* kernel;
-  bool whole_waves = false;
+  int wave_slots = 0;
 };
 
 constexpr int64_t kAnyM = INT64_C(0x7fffffff);
@@ -37,10 +38,17 @@ constexpr TuningRow kTuningGfx950[] = {
     {8, 160, "skinnyr_c2_r4_u4_m2x4_s0_nn"},
     {16, 0, "skinny_w8_c4_u4_s0_vec"},
     // 256 x 256 tiles, 8 waves of 64 x 128 (4096^3: 939 us against 958 us)
-    {kAnyM, 768, "mfma_256x256x32_w64x128_d6_vec", true},
+    {kAnyM, 768, "mfma_256x256x32_w64x128_d6_vec", 1},
     {kAnyM, 768, "mfma_128x256x16_w64x128_d6_vec"},
-    {kAnyM, 768, "mfma_256x128x16_w128x64_p5_vec"},
+    // operands the direct loads cannot take: the tile whose grid fills its
+    // waves (8191^2 x 2001: 128 x 128, 2126 us; 4096 x 4097 x 4096: 128 x 192,
+    // 1187 us, against 1217 us for 64 x 64 tiles)
+    {kAnyM, 768, "mfma_128x128x32_w64x64_p5_vec", 2},
     {kAnyM, 192, "mfma_128x128x16_w64x64_d6_vec"},
+    // 128 x 192 or 192 x 128 tiles of 8 waves where they make whole waves
+    // (2047 x 3001 x 1531: 256 tiles, 170 us against 185 us for 64 x 64)
+    {kAnyM, 192, "mfma_128x192x32_w32x96_p5_vec", 1},
+    {kAnyM, 192, "mfma_192x128x32_w96x32_p5_vec", 1},
     {kAnyM, 192, "mfma_64x64x32_w32x32_p5_vec"},
     {kAnyM, 24, "mfma_64x64x32_w32x32_d6_vec"},
     {kAnyM, 24, "mfma_64x64x32_w32x32_p5_vec"},

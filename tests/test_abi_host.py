@@ -111,8 +111,15 @@ def test_adjacent_but_not_overlapping_is_not_alias():
     # 256 x 256 tiles only where they fill whole waves of the 256 CUs
     (8192, 8192, 4096, 4096, 8192, P16, Q16, "mfma_256x256x32_w64x128_d6"),
     (6144, 6144, 4096, 4096, 6144, P16, Q16, "mfma_128x256x16_w64x128_d6"),
-    (4096, 4097, 4096, 4096, 4097, P16, Q16, "mfma_256x128x16_w128x64_p5"),
-    (2047, 3001, 1531, 1531, 3001, P16, Q16, "mfma_64x64x32_w32x32_p5"),
+    # operands the direct loads cannot take: the register-staged tile whose
+    # grid leaves its last wave at least 90 % full (or makes 4+ waves)
+    (4096, 4097, 4096, 4096, 4097, P16, Q16, "mfma_128x192x32_w32x96_p5"),   # 704 of 768
+    (8191, 8191, 2001, 2001, 8191, P16, Q16, "mfma_128x128x32_w64x64_p5"),   # 8 waves of 512
+    (6001, 6001, 999, 999, 6001, P16, Q16, "mfma_128x128x32_w64x64_p5"),     # 4.3 waves
+    (2047, 3001, 1531, 1531, 3001, P16, Q16, "mfma_128x192x32_w32x96_p5"),   # 256 tiles
+    (3001, 2047, 1531, 1531, 2047, P16, Q16, "mfma_192x128x32_w96x32_p5"),   # 256 tiles
+    (2049, 2049, 2049, 2049, 2049, P16, Q16, "mfma_64x64x32_w32x32_p5"),     # 187 of 256
+    (7936, 7936, 4096, 4096, 7936, P16, Q16, "mfma_256x256x32_w64x128_d6"),  # 961 of 1024
     (512, 512, 512, 512, 512, P16, Q16, "mfma_32x32x8_k4_g4_small"),
     (768, 768, 768, 768, 768, P16, Q16, "mfma_64x64x32_w32x32_d6"),
     (1024, 1024, 1024, 1024, 1024, P16, Q16, "mfma_64x64x32_w32x32_d6"),
