@@ -11,7 +11,10 @@ Kernel time is measured with HIP events recorded on the stream the library
 launches on (torch's current stream), one pair per launch; the roofline
 fraction uses the mean launch duration.  The skinny 8 x 8192 x 8192 workload
 is timed the same way (with rotating copies of B so it streams from HBM, not
-from the 256 MB last-level cache) and reported under "secondary".
+from the 256 MB last-level cache) and reported under "secondary"; each
+secondary measurement first runs its own call untimed for 300 ms, so that
+short kernels are not timed at the idle clocks the host-side work before
+them leaves.
 
 cpu_baseline: the CPU oracle (binary64 triple loop) timed on a bounded sample
 of the same workload (the first R rows of A), scaled to GFLOP/s.
@@ -51,10 +54,28 @@ def parse():
     return ap.parse_args()
 
 
-def time_launches(fn, steps, warmup, stream):
-    """Run fn() warmup times, then steps times with an event pair around each
-    launch on `stream`.  Returns (wall ms per step, list of per-launch ms)."""
+def settle(fn, seconds=0.3):
+    """Untimed: keep calling fn for `seconds`, so that the GPU clocks have left
+    the idle state that host-side work (input generation, oracle checks) puts
+    them in; a few dozen warm-up launches of a 50 us kernel take 2 ms, too
+    short for that."""
     import torch
+    t_end, i = time.perf_counter() + seconds, 0
+    while time.perf_counter() < t_end:
+        fn(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def time_launches(fn, steps, warmup, stream, settle_s=0.3):
+    """Settle the clocks (settle_s seconds of untimed calls), run fn() warmup
+    times, then steps times with an event pair around each launch on
+    `stream`.  Returns (wall ms per step, list of per-launch ms)."""
+    import torch
+    if settle_s > 0:
+        settle(fn, settle_s)
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
@@ -237,13 +258,7 @@ def per_config(args):
             Cs.append(torch.empty((w.M, w.N), device=dev))
         kname = binding.selected_kernel(As[0], Bs[0], Cs[0])
         call = lambda i: binding.gemm(As[i % copies], Bs[i % copies], Cs[i % copies])  # noqa: E731
-        # settle the clock: about 200 ms of calls before the 5 warm-up and 20 timed ones
-        t_end, i = time.perf_counter() + 0.2, 0
-        while time.perf_counter() < t_end:
-            call(i)
-            i += 1
-            if i % 16 == 0:
-                torch.cuda.synchronize()
+        # 300 ms of calls to settle the clocks, then 5 warm-up and 20 timed ones
         _, per = time_launches(call, 20, 5, stream)
         per = sorted(per)
         t_med, t_min = per[len(per) // 2], per[0]
@@ -299,8 +314,9 @@ def main():
     A, B = A_cpu.to(dev), B_cpu.to(dev)
     C = torch.empty((w.M, w.N), device=dev)
     kname = binding.selected_kernel(A, B, C)
+    # exactly W warm-up steps before the K timed ones (no extra settle)
     wall_ms, per = time_launches(lambda i: binding.gemm(A, B, C), args.steps, args.warmup,
-                                 stream)
+                                 stream, settle_s=0)
     mean_launch_ms = sum(per) / len(per)
     flops = w.flops
     value = flops / (wall_ms * 1e-3) / 1e9

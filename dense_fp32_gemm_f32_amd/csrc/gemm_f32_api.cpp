@@ -251,6 +251,51 @@ int get_workspace(int dev, hipStream_t s, size_t partial_floats, float** partial
   return GEMM_F32_OK;
 }
 
+// ---- exchange slots of the in-kernel K-slice sum, one set per (device, stream)
+// The kernels that use them find every slot zero and leave it zero, so a new
+// or grown buffer is cleared once, on the stream, before its first use.  Kept
+// for the life of the process (or until gemm_f32_release_workspaces).
+std::map<std::pair<int, uintptr_t>, Workspace>* g_xs = nullptr;
+
+int get_exchange_slots(int dev, hipStream_t s, size_t words, unsigned long long** slots) {
+  const size_t need = words * 8;
+  if (std::getenv("GEMM_F32_TEST_FAIL_WORKSPACE")) return GEMM_F32_ERR_WORKSPACE;
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  if (!g_xs) g_xs = new std::map<std::pair<int, uintptr_t>, Workspace>();
+  Workspace& w = (*g_xs)[{dev, (uintptr_t)s}];
+  if (w.bytes < need) {
+    // neither allocating nor clearing may be captured into a graph
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
+      (void)hipGetLastError();
+      return GEMM_F32_ERR_WORKSPACE;
+    }
+    if (cap != hipStreamCaptureStatusNone) return GEMM_F32_ERR_WORKSPACE;
+    if (w.ptr) {
+      if (hipStreamSynchronize(s) != hipSuccess || hipFree(w.ptr) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_F32_ERR_WORKSPACE;
+      }
+      w = Workspace{};
+    }
+    const size_t bytes = round_up(need + need / 2, 1 << 20);
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return GEMM_F32_ERR_WORKSPACE;
+    }
+    if (hipMemsetAsync(p, 0, bytes, s) != hipSuccess) {
+      (void)hipGetLastError();
+      (void)hipFree(p);
+      return GEMM_F32_ERR_WORKSPACE;
+    }
+    w.ptr = p;
+    w.bytes = bytes;
+  }
+  *slots = static_cast<unsigned long long*>(w.ptr);
+  return GEMM_F32_OK;
+}
+
 bool log_enabled() {
   static const bool on = [] {
     const char* v = std::getenv("GEMM_F32_LOG");
@@ -317,10 +362,14 @@ int run_entry(const Entry& e, const Op& op, const Problem& p, int dev, hipStream
     }
     case Kind::Skinny: {
       const auto& v = gemmf32::skinny_variant(e.sub);
-      const gemmf32::SkinnyPlan pl = v.plan(p, v.target_splits);
+      gemmf32::SkinnyPlan pl = v.plan(p, v.target_splits);
       float* partials = nullptr;
-      if (pl.splits > 1) {
+      if (pl.partial_floats > 0) {
         const int rc = get_workspace(dev, s, pl.partial_floats, &partials);
+        if (rc != GEMM_F32_OK) return rc;
+      }
+      if (pl.slot_words > 0) {
+        const int rc = get_exchange_slots(dev, s, pl.slot_words, &pl.slots);
         if (rc != GEMM_F32_OK) return rc;
       }
       err = v.launch(p, pl, partials, op.epilogue(), s);
@@ -726,19 +775,21 @@ const char* gemm_f32_kernel_name(int index) {
 
 int gemm_f32_release_workspaces(void) {
   std::lock_guard<std::mutex> lk(g_ws_mu);
-  if (!g_ws) return GEMM_F32_OK;
   int rc = GEMM_F32_OK;
   int cur = -1;
   const bool have_cur = hipGetDevice(&cur) == hipSuccess;
-  for (auto& kv : *g_ws) {
-    if (!kv.second.ptr) continue;
-    if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
-        hipFree(kv.second.ptr) != hipSuccess) {
-      (void)hipGetLastError();
-      rc = GEMM_F32_ERR_WORKSPACE;
+  for (auto* m : {g_ws, g_xs}) {
+    if (!m) continue;
+    for (auto& kv : *m) {
+      if (!kv.second.ptr) continue;
+      if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+          hipFree(kv.second.ptr) != hipSuccess) {
+        (void)hipGetLastError();
+        rc = GEMM_F32_ERR_WORKSPACE;
+      }
     }
+    m->clear();
   }
-  g_ws->clear();
   if (have_cur) (void)hipSetDevice(cur);
   return rc;
 }

@@ -94,7 +94,8 @@ int mfma_ex_variant_count();
 const MfmaExVariant& mfma_ex_variant(int i);
 
 // ---- skinny-M kernels (M <= 16) --------------------------------------------
-// Three kernels: B stored K x N (column tiles x K slices, MFMA; kernels_skinny.hip),
+// Three kernels: B stored K x N (column tiles x K slices, MFMA; kernels_skinny.hip,
+// with the slices added by a second dispatch or in-kernel through exchange slots),
 // the same with KiB row runs when B's rows are 16-byte aligned
 // (kernels_skinny_rows.hip), and B stored N x K (rows of B^T streamed whole;
 // kernels_skinny_t.hip).  Both
@@ -106,6 +107,12 @@ struct SkinnyPlan {
   int strips;              // workgroups along N
   size_t partial_floats;   // workspace floats for the partial sums (0 if splits == 1)
   size_t lds_bytes;        // dynamic LDS
+  // Kernels that add their K slices in-kernel through exchange slots: the
+  // 64-bit slots needed (0 for the others), and the slots themselves, which
+  // the dispatcher fills in.  The slots are all zero before a launch and the
+  // kernel leaves them zero.
+  size_t slot_words = 0;
+  unsigned long long* slots = nullptr;
 };
 struct SkinnyVariant {
   const char* name;

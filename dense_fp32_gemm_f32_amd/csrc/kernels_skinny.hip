@@ -9,11 +9,21 @@
 //  - combining partial sums of several workgroups inside one kernel needs an
 //    agent-scope release per workgroup (a whole-L2 writeback on this GPU),
 //    and those are serialised: about 0.16 us each, 40 us for 256 workgroups.
-// So the K range is split over a few slices, each workgroup writes its slice's
-// partial sums, and a second small kernel adds the slices in slice order.
+// So the K range is split over a few slices, and the slices' partial sums are
+// added in one of two ways:
+//  - each workgroup writes its slice's partial sums and a second small kernel
+//    adds the slices in slice order;
+//  - XCH: the slices meet in a binary tree of exchange slots inside this
+//    kernel.  Per output element, the two children of a tree node each swap
+//    (flag, value) into the node's 64-bit slot with one device-scope atomic
+//    exchange; the one that finds the slot full holds both values, adds them
+//    as left + right, empties the slot and carries the sum up.  The carrier
+//    of the root applies the epilogue and writes C.  The value travels inside
+//    the atomic, so no fence and no waiting on another workgroup is needed,
+//    and the additions are fixed by the slice count alone.
 // This is the "combine groups" step of "GPU compute shaders" (How it works,
-// step 6: one partial per group, reduced in a second dispatch); fixing the
-// group count and the order of the sum keeps reruns bitwise identical, as the
+// step 6: one partial per group, then the partials reduced); fixing the group
+// count and the order of the sum keeps reruns bitwise identical, as the
 // Pitfalls section of that page asks.
 //
 // The product inside a tile is read as C^T = B^T A^T on the matrix cores:
@@ -168,10 +178,10 @@ __device__ __forceinline__ void stream_tile(const Problem& p, int lane, int n0, 
 // [sb_begin, sb_end) of its K slice (blockIdx.y).  The row groups are added in
 // LDS in row-group order and the result goes to C (one slice) or to the
 // slice's partial sums.
-template <int NW, int CG, int U, bool VA, bool VB, bool TA>
+template <int NW, int CG, int U, bool VA, bool VB, bool TA, bool XCH>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW >= 16 ? 4 : 2)))
     skinny_tile_kernel(Problem p, int sb_per_slice, int slices, float* __restrict__ part,
-                       Epilogue ep) {
+                       unsigned long long* __restrict__ slots, Epilogue ep) {
   constexpr int NRG = NW / CG;
   static_assert(NW % CG == 0, "whole row groups");
   __shared__ __attribute__((aligned(16))) float red[NW][2][4][64];
@@ -207,15 +217,16 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW
   __syncthreads();
   float* dst;
   int64_t ld;
-  if (slices == 1) {
+  if (slices == 1 || XCH) {
     dst = p.C;
     ld = p.ldc;
   } else {
     dst = part + (size_t)slice * M * N;
     ld = N;
   }
+  constexpr int kTileElems = CG * 2 * 4 * 64;
   // one output per thread: column group, even/odd column, register, lane
-  for (int e = tid; e < CG * 2 * 4 * 64; e += NW * 64) {
+  for (int e = tid; e < kTileElems; e += NW * 64) {
     const int g = e / 512, c = (e / 256) % 2, r = (e / 64) % 4, l = e % 64;
     const int m = l & 15;
     const int n = n_wg + g * kGroupCols + 2 * (4 * (l >> 4) + r) + c;
@@ -225,8 +236,37 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW
       float* d = dst + (int64_t)m * ld + n;
       if (slices == 1) {
         *d = epilogue_apply(ep, s, d, n);
-      } else {
+      } else if (!XCH) {
         *d = s;
+      } else {
+        // Tree over the slices: at each level node j has children 2j, 2j+1;
+        // a node without a right child passes its value up unchanged.  The
+        // slots of a level's nodes follow one another, node j's slot for this
+        // element at ((base + j) * strips + strip) * kTileElems + e, so the
+        // lanes of a wave swap consecutive words.
+        int node = slice, width = slices, base = 0;
+        bool carry = true;
+        while (width > 1) {
+          const int parents = (width + 1) >> 1;
+          if ((node ^ 1) < width) {
+            unsigned long long* slot =
+                slots + ((size_t)(base + (node >> 1)) * gridDim.x + blockIdx.x) * kTileElems + e;
+            const unsigned long long mine = (1ull << 32) | __float_as_uint(s);
+            const unsigned long long old = __hip_atomic_exchange(
+                slot, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((old >> 32) == 0) {   // first of the two: the sibling carries on
+              carry = false;
+              break;
+            }
+            const float other = __uint_as_float((unsigned)old);
+            s = (node & 1) ? other + s : s + other;   // left + right
+            __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          base += parents;
+          node >>= 1;
+          width = parents;
+        }
+        if (carry) *d = epilogue_apply(ep, s, d, n);
       }
     }
   }
@@ -234,7 +274,15 @@ __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW
 
 // Slices: enough workgroups for every CU (or `target` slices if given), each
 // slice at least one super-block.
-template <int CG>
+// Exchange-tree nodes above the leaves for `slices` slices: the slot groups
+// the in-kernel sum uses (one per node, a node without a right child included).
+inline int tree_nodes(int slices) {
+  int total = 0;
+  for (int width = slices; width > 1; width = (width + 1) >> 1) total += (width + 1) >> 1;
+  return total;
+}
+
+template <int CG, bool XCH = false>
 SkinnyPlan plan_tile(const Problem& p, int target) {
   SkinnyPlan pl{};
   pl.strips = (p.N + CG * kGroupCols - 1) / (CG * kGroupCols);
@@ -245,26 +293,29 @@ SkinnyPlan plan_tile(const Problem& p, int target) {
   const int per = nsb > 0 ? (nsb + slices - 1) / slices : 0;
   pl.kslice = per;                                   // super-blocks per slice
   pl.splits = per > 0 ? (nsb + per - 1) / per : 1;   // no empty slice
-  pl.partial_floats = pl.splits > 1 ? (size_t)pl.splits * p.M * p.N : 0;
+  pl.partial_floats = (pl.splits > 1 && !XCH) ? (size_t)pl.splits * p.M * p.N : 0;
+  pl.slot_words = (pl.splits > 1 && XCH)
+                      ? (size_t)tree_nodes(pl.splits) * pl.strips * (CG * 2 * 4 * 64) : 0;
   pl.lds_bytes = 0;
   return pl;
 }
 
-template <int NW, int CG, int U, bool VA, bool VB, bool TA>
+template <int NW, int CG, int U, bool VA, bool VB, bool TA, bool XCH = false>
 hipError_t launch_tile(const Problem& p, const SkinnyPlan& pl, float* partials,
                        const Epilogue& e, hipStream_t s) {
   if (pl.strips <= 0 || pl.splits < 1 || pl.splits > 65535 || p.batch != 1)
     return hipErrorInvalidConfiguration;
-  if (pl.splits > 1 && !partials) return hipErrorInvalidValue;
+  if (pl.splits > 1 && !(XCH ? (void*)pl.slots : (void*)partials)) return hipErrorInvalidValue;
   Problem pp = p;
   int per = pl.kslice, slices = pl.splits;
   float* part = partials;
+  unsigned long long* sl = pl.slots;
   Epilogue ee = e;
-  void* args[] = {&pp, &per, &slices, &part, &ee};
+  void* args[] = {&pp, &per, &slices, &part, &sl, &ee};
   hipError_t err = hipLaunchKernel(
-      reinterpret_cast<const void*>(&skinny_tile_kernel<NW, CG, U, VA, VB, TA>),
+      reinterpret_cast<const void*>(&skinny_tile_kernel<NW, CG, U, VA, VB, TA, XCH>),
       dim3(pl.strips, pl.splits), dim3(NW * 64), args, 0, s);
-  if (err != hipSuccess || pl.splits == 1) return err;
+  if (err != hipSuccess || pl.splits == 1 || XCH) return err;
   return launch_combine(p, slices, partials, s, e);
 }
 
@@ -282,8 +333,20 @@ hipError_t launch_tile(const Problem& p, const SkinnyPlan& pl, float* partials,
   {"skinny_w" #NW "_c" #CG "_u" #U "_s" #S "_tn", 16, NW, U, false, true, S, true, false,   \
    &plan_tile<CG>, &launch_tile<NW, CG, U, false, true, true>}
 
+// K slices added in-kernel through exchange slots (prefix skinnyx_)
+#define GEMMF32_SKINNY_TILE_X(NW, CG, U, S)                                                  \
+  {"skinnyx_w" #NW "_c" #CG "_u" #U "_s" #S "_vec", 16, NW, U, true, true, S, false, false,  \
+   &plan_tile<CG, true>, &launch_tile<NW, CG, U, true, true, false, true>},                  \
+  {"skinnyx_w" #NW "_c" #CG "_u" #U "_s" #S "_scalar", 16, NW, U, false, false, S, false,     \
+   false, &plan_tile<CG, true>, &launch_tile<NW, CG, U, false, false, false, true>}
+
+#define GEMMF32_SKINNY_TILE_X_TA(NW, CG, U, S)                                               \
+  {"skinnyx_w" #NW "_c" #CG "_u" #U "_s" #S "_tn", 16, NW, U, false, true, S, true, false,    \
+   &plan_tile<CG, true>, &launch_tile<NW, CG, U, false, true, true, true>}
+
 // Name: skinny_w<waves>_c<column groups of 32>_u<super-blocks in flight>_s<K
-// slices, 0 = from the shape>_<load widths>, or _tn for A stored transposed.
+// slices, 0 = from the shape>_<load widths>, or _tn for A stored transposed;
+// skinnyx_ for the in-kernel sum of the slices.
 const SkinnyVariant kVariants[] = {
     GEMMF32_SKINNY_TILE(16, 1, 4, 1),    // 32 columns, all of K: no partial sums
     GEMMF32_SKINNY_TILE(8, 1, 4, 1),
@@ -301,6 +364,16 @@ const SkinnyVariant kVariants[] = {
     GEMMF32_SKINNY_TILE(8, 4, 4, 8),     // 8 K slices: two workgroups per CU
     GEMMF32_SKINNY_TILE(8, 4, 8, 8),
     GEMMF32_SKINNY_TILE_TA(8, 4, 4, 0),
+    // 64-column strips, two super-blocks in flight per wave (32 KiB of B per
+    // workgroup): 8 x 8192 x 8192 in 45 us against 48 us with the combine
+    GEMMF32_SKINNY_TILE_X(8, 2, 2, 0),
+    GEMMF32_SKINNY_TILE_X_TA(8, 2, 2, 0),
+    GEMMF32_SKINNY_TILE_X(8, 2, 1, 0),
+    GEMMF32_SKINNY_TILE_X(8, 2, 3, 0),
+    GEMMF32_SKINNY_TILE_X(8, 2, 4, 0),
+    GEMMF32_SKINNY_TILE_X(16, 2, 2, 0),
+    GEMMF32_SKINNY_TILE_X(8, 4, 2, 0),
+    GEMMF32_SKINNY_TILE_X(8, 4, 4, 0),
 };
 
 }  // namespace

@@ -36,7 +36,10 @@ constexpr TuningRow kTuningGfx950[] = {
     // wide skinny products (N above 20k): few K slices of 512-column strips
     // streamed in KiB row runs (8 x 28672 x 4096: 81 us against 92 us)
     {8, 160, "skinnyr_c2_r4_u4_m2x4_s0_nn"},
-    {16, 0, "skinny_w8_c4_u4_s0_vec"},
+    // 64-column strips, K slices added in-kernel through exchange slots
+    // (8 x 8192 x 8192: 45 us against 48 us for 128-column strips and a
+    // combine dispatch; 8 x 512 x 8192: 13 us against 18 us)
+    {16, 0, "skinnyx_w8_c2_u2_s0_vec"},
     // 256 x 256 tiles, 8 waves of 64 x 128 (4096^3: 939 us against 958 us)
     {kAnyM, 768, "mfma_256x256x32_w64x128_d6_vec", 1},
     {kAnyM, 768, "mfma_128x256x16_w64x128_d6_vec"},
@@ -79,8 +82,8 @@ struct TuningRowSkinny {
   const char* kernel;
 };
 constexpr TuningRowSkinny kTuningGfx950Skinny[] = {
-    {16, false, false, "skinny_w8_c4_u4_s0_vec"},
-    {16, true, false, "skinny_w8_c4_u4_s0_tn"},
+    {16, false, false, "skinnyx_w8_c2_u2_s0_vec"},
+    {16, true, false, "skinnyx_w8_c2_u2_s0_tn"},
     {8, false, true, "skinnyt_m8_j4_u2_nt"},
     {16, false, true, "skinnyt_m16_j4_u2_nt"},
     {8, true, true, "skinnyt_m8_j4_u2_tt"},

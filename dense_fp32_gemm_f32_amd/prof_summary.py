@@ -49,6 +49,8 @@ def kernel_sources(kernel: str | None = None) -> list[str]:
         files += ["kernels_skinny_t.hip", "kernels_combine.hip", "mfma_common.h"]
     elif kernel.startswith("skinny_"):
         files += ["kernels_skinny.hip", "kernels_combine.hip"]
+    elif kernel.startswith("skinnyx_"):
+        files += ["kernels_skinny.hip"]
     elif kernel.startswith("reduce_"):
         files += ["kernels_reduce.hip"]
     else:
@@ -83,9 +85,10 @@ def counters(d: Path):
     return out
 
 
-def durations(d: Path, skip: int = 0):
+def durations(d: Path, skip: int = 0, last: int = 0):
     """{kernel name: (calls, avg ns, min ns, max ns)} from a --kernel-trace run,
-    leaving out the first `skip` dispatches of each kernel (clock warm-up)."""
+    leaving out the first `skip` dispatches of each kernel (clock warm-up), or
+    keeping only its `last` dispatches (after a settle phase of the run)."""
     per = defaultdict(list)
     with open(_find(d, "kernel_trace.csv")) as f:
         rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
@@ -93,7 +96,10 @@ def durations(d: Path, skip: int = 0):
         per[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     res = {}
     for name, ds in per.items():
-        ds = ds[skip:] if len(ds) > skip else ds
+        if last:
+            ds = ds[-last:]
+        else:
+            ds = ds[skip:] if len(ds) > skip else ds
         res[name] = (len(ds), sum(ds) / len(ds), min(ds), max(ds))
     return res
 
@@ -122,23 +128,41 @@ def by_launch_shape(d: Path):
     return per
 
 
-def bench_summary(trace: Path, commands, out: Path):
-    """Markdown table of a bench.py kernel trace, split by launch shape."""
+def bench_summary(trace: Path, commands, out: Path, skip: int = 0, bench_log: Path | None = None):
+    """Markdown table of a bench.py kernel trace, split by launch shape; with
+    skip, the first `skip` dispatches of each (kernel, grid) are left out (the
+    warm-up steps), and with bench_log the JSON line the traced run printed is
+    quoted so that its event-timed launch mean can be set beside the trace."""
     lines = ["# bench.py kernel trace (rocprofv3 --kernel-trace --stats)", "",
              "Command (from the repository root on the MI355X box):", ""]
     lines += [f"    {c}" for c in commands] + [""]
-    lines += ["Every dispatch of the run, warm-up included, grouped by kernel and grid "
-              "(grid sizes in threads).", "",
+    what = (f"Dispatches of the run after the first {skip} of each kernel and grid (the "
+            "warm-up steps)" if skip else "Every dispatch of the run, warm-up included")
+    lines += [what + ", grouped by kernel and grid (grid sizes in threads).", "",
               "| kernel | grid | workgroup | calls | avg us | min us | max us |",
               "|---|---|---|---|---|---|---|"]
     rows = sorted(by_launch_shape(trace).items(), key=lambda kv: -sum(kv[1]))
     for (name, grid, wg), ds in rows:
         if "gemmf32" not in name:
             continue
+        ds = ds[skip:] if len(ds) > skip else ds
         short = name.replace("gemmf32::(anonymous namespace)::", "").replace("void ", "")
         short = short.split("(")[0]
         lines.append(f"| `{short}` | {grid} | {wg} | {len(ds)} | {sum(ds) / len(ds) / 1e3:.2f} "
                      f"| {min(ds) / 1e3:.2f} | {max(ds) / 1e3:.2f} |")
+    if bench_log is not None:
+        rec = None
+        for line in Path(bench_log).read_text().splitlines():
+            if line.startswith("{") and '"metric"' in line:
+                rec = json.loads(line)
+        if rec is not None:
+            r = rec.get("roofline", {})
+            lines += ["", "The same run's bench.py line (HIP events around each timed launch):", "",
+                      f"- kernel `{rec['config'].get('kernel')}`, {rec['steps']} timed steps after "
+                      f"{rec['warmup']} warm-up steps",
+                      f"- launch_ms_mean {r.get('launch_ms_mean')}, launch_ms_min "
+                      f"{r.get('launch_ms_min')}, achieved {r.get('achieved')} {r.get('unit')} "
+                      f"(frac {r.get('frac')})"]
     Path(out).write_text("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -146,6 +170,7 @@ def bench_summary(trace: Path, commands, out: Path):
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--bench-trace", help="summarise a bench.py --kernel-trace run instead")
+    ap.add_argument("--bench-log", help="with --bench-trace: the traced run's output")
     ap.add_argument("--workload")
     ap.add_argument("--kernel", help="table name of the kernel")
     ap.add_argument("--match", help="substring of the rocprof kernel name(s)")
@@ -156,6 +181,8 @@ def main(argv=None):
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--skip", type=int, default=0,
                     help="leave out the first SKIP dispatches of each kernel from the durations")
+    ap.add_argument("--last", type=int, default=0,
+                    help="keep only the last LAST dispatches of each kernel (instead of --skip)")
     ap.add_argument("--algo-bytes", type=float, default=0.0)
     ap.add_argument("--flops", type=float, default=0.0)
     ap.add_argument("--mfma-cycles", type=int, default=0,
@@ -164,7 +191,8 @@ def main(argv=None):
     ap.add_argument("--out", required=True)
     args = ap.parse_args(argv)
     if args.bench_trace:
-        bench_summary(Path(args.bench_trace), args.command, Path(args.out))
+        bench_summary(Path(args.bench_trace), args.command, Path(args.out), args.skip,
+                      Path(args.bench_log) if args.bench_log else None)
         return
     if not (args.workload and args.kernel and args.match and args.trace):
         ap.error("--workload, --kernel, --match and --trace are required")
@@ -173,11 +201,13 @@ def main(argv=None):
     lines += ["Commands (from the repository root on the MI355X box):", ""]
     lines += [f"    {c}" for c in args.command] + [""]
 
-    dur = durations(Path(args.trace), args.skip)
+    dur = durations(Path(args.trace), args.skip, args.last)
     names = pick(dur, args.match)
+    which = (f"the last {args.last} dispatches of each kernel (after the run's clock-settle "
+             "phase)" if args.last else
+             f"leaving out the first {args.skip} dispatches of each kernel (clock warm-up)")
     lines += ["## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
-              f"Durations from the trace, leaving out the first {args.skip} dispatches of each "
-              "kernel (clock warm-up).", "",
+              f"Durations from the trace, {which}.", "",
               "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
     tot_avg = 0.0
     for n in names:
@@ -214,10 +244,20 @@ def main(argv=None):
         lines += ["## Core counters (first matched kernel, mean per dispatch)", "",
                   "| counter | value |", "|---|---|"]
         lines += [f"| {k} | {v:.6g} |" for k, v in sorted(c.items())]
-        if "GRBM_GUI_ACTIVE" in c:
+        dur = durations(Path(args.trace), args.skip, args.last)
+        long_enough = n in dur and dur[n][1] >= 200e3
+        if "SQ_INSTS_MFMA" in c and args.mfma_cycles and n in dur:
+            util = c["SQ_INSTS_MFMA"] * args.mfma_cycles / (dur[n][1] * 2.4 * 1024.0)
+            lines += ["", f"MFMA issue over the traced duration at the 2.4 GHz peak clock = "
+                      f"SQ_INSTS_MFMA x {args.mfma_cycles} cycles / (avg duration x 2.4 GHz x "
+                      f"1024 SIMDs) = {100 * util:.1f}%"]
+        if "GRBM_GUI_ACTIVE" in c and not long_enough:
+            lines += ["", "(Clock and MFMA-occupancy figures are derived only for launches of "
+                      "200 us or more: on shorter ones GRBM_GUI_ACTIVE also counts the "
+                      "counter collection around the dispatch.)"]
+        if "GRBM_GUI_ACTIVE" in c and long_enough:
             xcd_cycles = c["GRBM_GUI_ACTIVE"] / 8.0     # summed over the 8 XCDs
             lines.append("")
-            dur = durations(Path(args.trace), args.skip)
             if n in dur:
                 lines.append(f"Clock while the kernel runs = GRBM_GUI_ACTIVE/8 / average duration "
                              f"= {xcd_cycles / dur[n][1]:.3f} GHz")

@@ -27,6 +27,9 @@ def main(argv=None):
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--torch", action="store_true",
                     help="run torch.matmul in fp32 (the vendor library, for comparison) instead")
+    ap.add_argument("--settle-ms", type=float, default=0.0,
+                    help="before the --reps launches, repeat the same call for this long so the "
+                         "clocks leave the idle state (for traces; counter runs leave it 0)")
     ap.add_argument("--reduce", type=int, default=0,
                     help="run reduce_sum_f32 on this many floats (4 copies) instead of a GEMM")
     args = ap.parse_args(argv)
@@ -42,6 +45,7 @@ def main(argv=None):
         out = torch.empty(1, device=dev)
         print(f"reduce_sum_f32 on {args.reduce} floats, {args.reps} launches over 4 copies",
               flush=True)
+        _settle(lambda i: binding.reduce_sum(xs[i % 4], out), args.settle_ms)
         for i in range(args.reps):
             binding.reduce_sum(xs[i % 4], out)
         torch.cuda.synchronize()
@@ -66,11 +70,28 @@ def main(argv=None):
     name = args.kernel or binding.selected_kernel(As[0], Bs[0], Cs[0])
     print(f"workload {w.name}: kernel {name}, {args.reps} launches over {copies} input copies",
           flush=True)
+    _settle(lambda i: binding.run_kernel(name, As[i % copies], Bs[i % copies], Cs[i % copies]),
+            args.settle_ms)
     for i in range(args.reps):
         binding.run_kernel(name, As[i % copies], Bs[i % copies], Cs[i % copies])
     torch.cuda.synchronize()
     _calibration_copy(dev, args.copy_mib)
     return 0
+
+
+def _settle(fn, ms):
+    """Repeat fn for `ms` milliseconds (no-op for 0)."""
+    import time
+    import torch
+    if ms <= 0:
+        return
+    t_end, i = time.perf_counter() + ms * 1e-3, 0
+    while time.perf_counter() < t_end:
+        fn(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
 
 
 def _calibration_copy(dev, mib):

@@ -28,16 +28,19 @@
  * current HIP device can access (hipMalloc or a torch CUDA/HIP tensor).  The
  * library keeps no reference to them after the call returns.  It owns only
  * its code objects and, for the kernels that split K over workgroups (the
- * skinny-M kernel and the K-split MFMA entries), a scratch workspace of
- * per-slice partial sums (per device and stream, allocated on first need,
- * freed by gemm_f32_release_workspaces or at unload).  C must not overlap A
- * or B.
+ * skinny-M kernels and the K-split MFMA entries), scratch workspaces (per
+ * device and stream, allocated on first need, freed by
+ * gemm_f32_release_workspaces or at unload): per-slice partial sums, or the
+ * exchange slots in which the skinny-M kernel adds its K slices.  The slots
+ * are cleared once when allocated and every call leaves them clear.  C must
+ * not overlap A or B.
  *
- * Graph capture.  Every call may be captured into a HIP graph (no memset and
- * no host synchronisation is enqueued).  A call that needs the workspace and
- * would have to allocate or grow it on a stream that is being captured
- * returns GEMM_F32_ERR_WORKSPACE instead: make the same call once on that
- * stream before capturing.
+ * Graph capture.  Every call may be captured into a HIP graph: a call
+ * enqueues no host synchronisation, and no memset except the one that clears
+ * newly allocated exchange slots.  A call that needs a workspace and would
+ * have to allocate or grow it on a stream that is being captured returns
+ * GEMM_F32_ERR_WORKSPACE instead: make the same call once on that stream
+ * before capturing.
  *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
  * stream).  Work is enqueued on it and the call returns without waiting; the

@@ -99,14 +99,14 @@ def test_adjacent_but_not_overlapping_is_not_alias():
     (0, 5, 5, 5, 5, P16, Q16, "empty"),
     (5, 0, 5, 5, 1, P16, Q16, "empty"),
     (5, 5, 0, 1, 5, P16, Q16, "fill_zero_k0"),
-    (8, 8192, 8192, 8192, 8192, P16, Q16, "skinny_w8_c4"),
-    (3, 8192, 8192, 8192, 8192, P16, Q16, "skinny_w8_c4"),
-    (16, 4096, 4096, 4096, 4096, P16, Q16, "skinny_w8_c4"),
-    (8, 3001, 1531, 1531, 3001, P16, Q16, "skinny_w8_c4"),
+    (8, 8192, 8192, 8192, 8192, P16, Q16, "skinnyx_w8_c2_u2"),
+    (3, 8192, 8192, 8192, 8192, P16, Q16, "skinnyx_w8_c2_u2"),
+    (16, 4096, 4096, 4096, 4096, P16, Q16, "skinnyx_w8_c2_u2"),
+    (8, 3001, 1531, 1531, 3001, P16, Q16, "skinnyx_w8_c2_u2"),
     # wide N: KiB row runs, when B's rows are 16-byte aligned; else the tile kernel
     (8, 28672, 4096, 4096, 28672, P16, Q16, "skinnyr_c2_r4"),
-    (8, 28672, 4096, 4096, 28673, P16, Q16, "skinny_w8_c4"),
-    (16, 28672, 4096, 4096, 28672, P16, Q16, "skinny_w8_c4"),
+    (8, 28672, 4096, 4096, 28673, P16, Q16, "skinnyx_w8_c2_u2"),
+    (16, 28672, 4096, 4096, 28672, P16, Q16, "skinnyx_w8_c2_u2"),
     (4096, 4096, 4096, 4096, 4096, P16, Q16, "mfma_256x256x32_w64x128_d6"),
     # 256 x 256 tiles only where they fill whole waves of the 256 CUs
     (8192, 8192, 4096, 4096, 8192, P16, Q16, "mfma_256x256x32_w64x128_d6"),

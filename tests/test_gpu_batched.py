@@ -148,12 +148,15 @@ def test_batched_one_product_is_gemm_f32(gpu_lib):
 # ---- calls captured into a HIP graph ------------------------------------------
 
 def test_graph_capture_replays_match_eager(gpu_lib):
-    """gemm_f32 (an MFMA tile kernel; a skinny kernel with its workspace and
-    combine) and gemm_f32_batched captured into one graph; each replay, with
+    """gemm_f32 (an MFMA tile kernel; the skinny kernel that adds its K slices
+    through exchange slots, which each call must leave clear for the next
+    replay; the skinny kernel with a partials workspace and a combine
+    dispatch) and gemm_f32_batched captured into one graph; each replay, with
     fresh inputs copied in and eager work between replays, matches the eager
     calls bit for bit."""
     s = torch.cuda.Stream()
-    shapes = {"tile": (1000, 999, 777), "skinny": (8, 4096, 4096)}
+    shapes = {"tile": (1000, 999, 777), "skinny": (8, 4096, 4096),
+              "skinny_combine": (8, 2048, 4096)}
     static = {k: (torch.empty((m, kk), device="cuda"), torch.empty((kk, n), device="cuda"),
                   torch.empty((m, n), device="cuda")) for k, (m, n, kk) in shapes.items()}
     bA, bB = torch.empty((16, 128, 96), device="cuda"), torch.empty((16, 96, 64), device="cuda")
@@ -167,8 +170,11 @@ def test_graph_capture_replays_match_eager(gpu_lib):
         bB.copy_(_stack(16, 96, 64, "int2", seed + 200))
 
     def calls():
-        for A, B, C in static.values():
-            gpu_lib.gemm(A, B, C)
+        for k, (A, B, C) in static.items():
+            if k == "skinny_combine":
+                gpu_lib.run_kernel("skinny_w8_c4_u4_s0_vec", A, B, C)
+            else:
+                gpu_lib.gemm(A, B, C)
         gpu_lib.gemm_batched(bA, bB, bC)
 
     # warm up on the capture stream: the skinny kernel's workspace lives per stream

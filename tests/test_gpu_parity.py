@@ -276,36 +276,63 @@ def test_errors_from_the_device_side(gpu_lib):
 
 
 SPLITK = "skinny_w8_c4_u4_s0_vec"   # a kernel that combines K slices in a workspace
+SPLITX = "skinnyx_w8_c2_u2_s0_vec"  # a kernel that adds K slices through exchange slots
 
 
-def test_workspace_failure_is_reported(gpu_lib, monkeypatch):
+@pytest.mark.parametrize("kname", [SPLITK, SPLITX])
+def test_workspace_failure_is_reported(gpu_lib, monkeypatch, kname):
     A = torch.ones((8, 4096), device="cuda")
     B = torch.ones((4096, 4096), device="cuda")
     C = torch.empty((8, 4096), device="cuda")
-    idx = gpu_lib.kernel_index(SPLITK)
+    idx = gpu_lib.kernel_index(kname)
     monkeypatch.setenv("GEMM_F32_TEST_FAIL_WORKSPACE", "1")
     s = torch.cuda.current_stream().cuda_stream
     rc = gpu_lib.gemm_f32_run_kernel(idx, 8, 4096, 4096, A.data_ptr(), 4096, B.data_ptr(),
                                      4096, C.data_ptr(), 4096, s)
     assert rc == 6
     monkeypatch.delenv("GEMM_F32_TEST_FAIL_WORKSPACE")
-    gpu_lib.run_kernel(SPLITK, A, B, C)
+    gpu_lib.run_kernel(kname, A, B, C)
     torch.cuda.synchronize()
     assert torch.all(C == 4096)
 
 
-def test_two_streams_concurrently(gpu_lib):
+@pytest.mark.parametrize("kname", [SPLITK, SPLITX])
+def test_two_streams_concurrently(gpu_lib, kname):
     """Split-K calls on two streams use separate workspaces and both match."""
     A1, B1 = inputs.make_ab(8, 4096, 8192, "normal", "u11", 8001)
     A2, B2 = inputs.make_ab(6, 4096, 8192, "normal", "u11", 8002)
     dA1, dB1, dA2, dB2 = (t.cuda() for t in (A1, B1, A2, B2))
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     torch.cuda.synchronize()
+    H.say(f"two streams {kname}")
     with torch.cuda.stream(s1):
-        C1 = gpu_lib.run_kernel(SPLITK, dA1, dB1)
+        C1 = gpu_lib.run_kernel(kname, dA1, dB1)
     with torch.cuda.stream(s2):
-        C2 = gpu_lib.run_kernel(SPLITK, dA2, dB2)
+        C2 = gpu_lib.run_kernel(kname, dA2, dB2)
     torch.cuda.synchronize()
     for (A, B, C) in ((A1, B1, C1), (A2, B2, C2)):
         C_ref, ABS = H.oracle_of(A, B)
         H.assert_within_tol(C.cpu().numpy(), C_ref, ABS, "two streams")
+
+
+def test_exchange_tree_shapes_in_sequence(gpu_lib):
+    """The in-kernel sum of K slices through exchange slots, over trees of
+    many shapes in a row on one stream: 1, 2, 3, 4, 5, 7, 16 and 128 slices
+    (odd counts leave a node without a right child), the slot buffer growing
+    and then reused by smaller trees.  A slot left full by one call would make
+    a later call take the wrong branch, so every call is checked bit for bit
+    on integers and rerun."""
+    # (M, N, K): 64-column strips and slices = ceil(256 / strips), capped by
+    # the 16-row super-blocks of K
+    shapes = [(8, 64 * 256, 4096), (8, 64 * 128, 2048), (5, 64 * 86, 3000), (8, 64 * 64, 4096),
+              (16, 64 * 52, 1600), (3, 64 * 37, 2100), (8, 1000, 8192), (7, 100, 40000),
+              (8, 64 * 64, 4096), (1, 64 * 86, 333)]
+    for i, (M, N, K) in enumerate(shapes):
+        A, B = inputs.make_ab(M, N, K, "int2", "int2", 8300 + i)
+        H.say(f"exchange tree M={M} N={N} K={K}")
+        C1, flat, ldc = _run(gpu_lib, A, B, ldc=N + 1, kernel=SPLITX)
+        C2, _, _ = _run(gpu_lib, A, B, ldc=N + 1, kernel=SPLITX)
+        C_ref, _ = H.oracle_of(A, B)
+        H.assert_bitexact(C1, C_ref, f"exchange {M}x{N}x{K}")
+        assert np.array_equal(C1, C2)
+        H.check_outside_untouched(flat, M, N, ldc)
