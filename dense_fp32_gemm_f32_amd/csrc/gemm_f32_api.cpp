@@ -202,26 +202,33 @@ int check_pointer(const void* p, int dev) {
   }
 }
 
-// ---- workspace for K-slice partial sums, one per (device, stream) -----------
-// Holds the per-slice partial sums of the skinny and split-K MFMA kernels.  Kept for the life of
-// the process (or until gemm_f32_release_workspaces) and grown on demand.
+// ---- scratch workspaces, one set per (device, stream) -----------------------
+// Per-slice partial sums of the combine-based skinny kernels and the split-K
+// MFMA entries, and the exchange slots of the in-kernel slice sum.  Kept for
+// the life of the process (or until gemm_f32_release_workspaces) and grown on
+// demand.  A buffer that is outgrown is retired, not freed: work already
+// enqueued, and any graph captured earlier on that stream, may still use it.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
+  std::vector<void*> retired;
 };
 std::mutex g_ws_mu;
-std::map<std::pair<int, uintptr_t>, Workspace>* g_ws = nullptr;
+std::map<std::pair<int, uintptr_t>, Workspace>* g_ws = nullptr;   // partial sums
+std::map<std::pair<int, uintptr_t>, Workspace>* g_xs = nullptr;   // exchange slots
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int get_workspace(int dev, hipStream_t s, size_t partial_floats, float** partials) {
-  const size_t need = partial_floats * 4;
+// A buffer of at least `need` bytes from `table` for (dev, s).  clear: a new
+// buffer is zeroed on the stream before any later work on it (the exchange
+// slots start empty).  Caller holds g_ws_mu.
+int grow_workspace(std::map<std::pair<int, uintptr_t>, Workspace>*& table, int dev,
+                   hipStream_t s, size_t need, bool clear, void** out) {
   if (std::getenv("GEMM_F32_TEST_FAIL_WORKSPACE")) return GEMM_F32_ERR_WORKSPACE;
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  if (!g_ws) g_ws = new std::map<std::pair<int, uintptr_t>, Workspace>();
-  Workspace& w = (*g_ws)[{dev, (uintptr_t)s}];
+  if (!table) table = new std::map<std::pair<int, uintptr_t>, Workspace>();
+  Workspace& w = (*table)[{dev, (uintptr_t)s}];
   if (w.bytes < need) {
-    // a stream being captured into a graph can neither wait nor allocate:
+    // a stream being captured into a graph can neither allocate nor clear:
     // the workspace must have been grown by an earlier call on that stream
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
@@ -229,14 +236,6 @@ int get_workspace(int dev, hipStream_t s, size_t partial_floats, float** partial
       return GEMM_F32_ERR_WORKSPACE;
     }
     if (cap != hipStreamCaptureStatusNone) return GEMM_F32_ERR_WORKSPACE;
-    if (w.ptr) {
-      // the stream may still be using the old buffer
-      if (hipStreamSynchronize(s) != hipSuccess || hipFree(w.ptr) != hipSuccess) {
-        (void)hipGetLastError();
-        return GEMM_F32_ERR_WORKSPACE;
-      }
-      w = Workspace{};
-    }
     // grow with headroom so alternating shapes do not reallocate
     const size_t bytes = round_up(need + need / 2, 1 << 20);
     void* p = nullptr;
@@ -244,56 +243,36 @@ int get_workspace(int dev, hipStream_t s, size_t partial_floats, float** partial
       (void)hipGetLastError();
       return GEMM_F32_ERR_WORKSPACE;
     }
-    w.ptr = p;
-    w.bytes = bytes;
-  }
-  *partials = static_cast<float*>(w.ptr);
-  return GEMM_F32_OK;
-}
-
-// ---- exchange slots of the in-kernel K-slice sum, one set per (device, stream)
-// The kernels that use them find every slot zero and leave it zero, so a new
-// or grown buffer is cleared once, on the stream, before its first use.  Kept
-// for the life of the process (or until gemm_f32_release_workspaces).
-std::map<std::pair<int, uintptr_t>, Workspace>* g_xs = nullptr;
-
-int get_exchange_slots(int dev, hipStream_t s, size_t words, unsigned long long** slots) {
-  const size_t need = words * 8;
-  if (std::getenv("GEMM_F32_TEST_FAIL_WORKSPACE")) return GEMM_F32_ERR_WORKSPACE;
-  std::lock_guard<std::mutex> lk(g_ws_mu);
-  if (!g_xs) g_xs = new std::map<std::pair<int, uintptr_t>, Workspace>();
-  Workspace& w = (*g_xs)[{dev, (uintptr_t)s}];
-  if (w.bytes < need) {
-    // neither allocating nor clearing may be captured into a graph
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
-      (void)hipGetLastError();
-      return GEMM_F32_ERR_WORKSPACE;
-    }
-    if (cap != hipStreamCaptureStatusNone) return GEMM_F32_ERR_WORKSPACE;
-    if (w.ptr) {
-      if (hipStreamSynchronize(s) != hipSuccess || hipFree(w.ptr) != hipSuccess) {
-        (void)hipGetLastError();
-        return GEMM_F32_ERR_WORKSPACE;
-      }
-      w = Workspace{};
-    }
-    const size_t bytes = round_up(need + need / 2, 1 << 20);
-    void* p = nullptr;
-    if (hipMalloc(&p, bytes) != hipSuccess) {
-      (void)hipGetLastError();
-      return GEMM_F32_ERR_WORKSPACE;
-    }
-    if (hipMemsetAsync(p, 0, bytes, s) != hipSuccess) {
+    if (clear && hipMemsetAsync(p, 0, bytes, s) != hipSuccess) {
       (void)hipGetLastError();
       (void)hipFree(p);
       return GEMM_F32_ERR_WORKSPACE;
     }
+    if (w.ptr) w.retired.push_back(w.ptr);
     w.ptr = p;
     w.bytes = bytes;
   }
-  *slots = static_cast<unsigned long long*>(w.ptr);
+  *out = w.ptr;
   return GEMM_F32_OK;
+}
+
+int get_workspace(int dev, hipStream_t s, size_t partial_floats, float** partials) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  void* p = nullptr;
+  const int rc = grow_workspace(g_ws, dev, s, partial_floats * 4, false, &p);
+  *partials = static_cast<float*>(p);
+  return rc;
+}
+
+// The exchange slots: every kernel that uses them finds them all zero and
+// leaves them zero, so a new buffer is cleared once, on the stream, before
+// its first use.
+int get_exchange_slots(int dev, hipStream_t s, size_t words, unsigned long long** slots) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  void* p = nullptr;
+  const int rc = grow_workspace(g_xs, dev, s, words * 8, true, &p);
+  *slots = static_cast<unsigned long long*>(p);
+  return rc;
 }
 
 bool log_enabled() {
@@ -781,11 +760,19 @@ int gemm_f32_release_workspaces(void) {
   for (auto* m : {g_ws, g_xs}) {
     if (!m) continue;
     for (auto& kv : *m) {
-      if (!kv.second.ptr) continue;
-      if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
-          hipFree(kv.second.ptr) != hipSuccess) {
+      Workspace& w = kv.second;
+      if (w.ptr) w.retired.push_back(w.ptr);
+      if (w.retired.empty()) continue;
+      if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipGetLastError();
         rc = GEMM_F32_ERR_WORKSPACE;
+        continue;
+      }
+      for (void* p : w.retired) {
+        if (hipFree(p) != hipSuccess) {
+          (void)hipGetLastError();
+          rc = GEMM_F32_ERR_WORKSPACE;
+        }
       }
     }
     m->clear();

@@ -32,15 +32,19 @@
  * device and stream, allocated on first need, freed by
  * gemm_f32_release_workspaces or at unload): per-slice partial sums, or the
  * exchange slots in which the skinny-M kernel adds its K slices.  The slots
- * are cleared once when allocated and every call leaves them clear.  C must
- * not overlap A or B.
+ * are cleared once when allocated and every call leaves them clear.  A
+ * workspace that a larger call outgrows is replaced but kept, not freed,
+ * until gemm_f32_release_workspaces.  C must not overlap A or B.
  *
  * Graph capture.  Every call may be captured into a HIP graph: a call
  * enqueues no host synchronisation, and no memset except the one that clears
  * newly allocated exchange slots.  A call that needs a workspace and would
  * have to allocate or grow it on a stream that is being captured returns
  * GEMM_F32_ERR_WORKSPACE instead: make the same call once on that stream
- * before capturing.
+ * before capturing.  A captured graph keeps the workspace of the stream it
+ * was captured on, which stays valid when later calls outgrow it (until
+ * gemm_f32_release_workspaces); replays of it must not overlap other work
+ * that uses the same workspace (calls on that stream, or other replays).
  *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
  * stream).  Work is enqueued on it and the call returns without waiting; the
@@ -306,8 +310,10 @@ int gemm_f32_run_kernel_fused(int index, int transA, int transB,
 
 /*
  * gemm_f32_release_workspaces -- free every scratch workspace the library
- * holds (all devices, all streams) after synchronising the devices they live
- * on.  Safe to call at any time no call is in flight from another thread.
+ * holds (all devices, all streams, outgrown ones included) after
+ * synchronising the devices they live on.  Safe to call at any time no call
+ * is in flight from another thread; graphs captured before it must not be
+ * replayed after it.
  */
 int gemm_f32_release_workspaces(void);
 

@@ -225,3 +225,68 @@ def test_capture_without_workspace_reports_error(gpu_lib):
                               C.data_ptr(), 2048, s.cuda_stream)
     torch.cuda.synchronize()
     assert rc == 6, rc
+
+
+def test_graph_replay_after_workspace_growth(gpu_lib):
+    """A graph captured while a stream's workspaces were small replays
+    correctly after larger eager calls on that stream have outgrown them: the
+    outgrown buffers are kept, not freed, so the graph's kernels still find
+    their partial sums and exchange slots."""
+    from dense_fp32_gemm_f32_amd import binding
+    torch.cuda.synchronize()
+    assert binding.gemm_f32_release_workspaces() == 0
+    s = torch.cuda.Stream()
+    # small: 2 K slices each (0.5 MiB of exchange slots, 0.25 MiB of partials);
+    # big: 4 and 8 slices (1.5 MiB of slots, 2 MiB of partials), both beyond
+    # the 1 MiB first allocations
+    kx, kc = "skinnyx_w8_c2_u2_s0_vec", "skinny_w8_c4_u4_s0_vec"
+    small = {kx: (8, 4096, 32), kc: (16, 4096, 32)}
+    big = {kx: (8, 4096, 4096), kc: (16, 4096, 4096)}
+    st = {k: (torch.empty((m, kk), device="cuda"), torch.empty((kk, n), device="cuda"),
+              torch.empty((m, n), device="cuda")) for k, (m, n, kk) in small.items()}
+
+    def fill(seed):
+        for i, (k, (m, n, kk)) in enumerate(small.items()):
+            st[k][0].copy_(inputs.draw_matrix(m, kk, "int2", seed + 2 * i))
+            st[k][1].copy_(inputs.draw_matrix(kk, n, "int2", seed + 2 * i + 1))
+
+    def calls():
+        for k, (A, B, C) in st.items():
+            gpu_lib.run_kernel(k, A, B, C)
+
+    fill(9300)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.synchronize()
+    H.say("capture with small workspaces")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        calls()
+    torch.cuda.synchronize()
+    # larger eager calls on the same stream outgrow both workspaces
+    bigs = {}
+    for i, (k, (m, n, kk)) in enumerate(big.items()):
+        A, B = inputs.make_ab(m, n, kk, "int2", "int2", 9400 + i)
+        bigs[k] = (A, B, A.cuda(), B.cuda())
+    H.say("eager calls that grow the workspaces")
+    with torch.cuda.stream(s):
+        outs = {k: gpu_lib.run_kernel(k, dA, dB) for k, (_, _, dA, dB) in bigs.items()}
+    torch.cuda.synchronize()
+    for k, (A, B, _, _) in bigs.items():
+        C_ref, _ = H.oracle_of(A, B)
+        H.assert_bitexact(outs[k].cpu().numpy(), C_ref, f"grown {k}")
+    for rep in range(2):
+        fill(9500 + rep)
+        torch.cuda.synchronize()
+        H.say(f"replay after growth {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        got = {k: C.clone() for k, (_, _, C) in st.items()}
+        with torch.cuda.stream(s):
+            calls()
+        torch.cuda.synchronize()
+        for k, (A, B, C) in st.items():
+            assert torch.equal(got[k], C), f"replay {rep} of {k} differs from the eager call"
+            C_ref, _ = H.oracle_of(A.cpu(), B.cpu())
+            H.assert_bitexact(C.cpu().numpy(), C_ref, f"replay {rep} {k}")
