@@ -237,6 +237,23 @@ def cpu_baseline_config(w, C_gpu, C_gpu_int):
             "max_err_ratio": ratio, "int_bitexact": bool(np.array_equal(C_gpu_int, Ci_ref))}
 
 
+def copies_parity(As, Bs, Cs):
+    """Each rotated input copy's output from the timed calls (the last call on
+    that copy) against the oracle: the largest |dC| / sum|a||b| over the
+    copies, and whether every copy is within the 1e-4 gate."""
+    import numpy as np
+    import oracle
+    worst = 0.0
+    for A, B, C in zip(As, Bs, Cs):
+        C_ref, _, ABS = oracle.gemm(A.cpu().numpy(), B.cpu().numpy(), want_f64=True)
+        err = np.abs(C.cpu().numpy().astype(np.float64) - C_ref.astype(np.float64))
+        ok = err <= 1e-4 * ABS
+        worst = max(worst, float(np.max(np.where(ABS > 0, err / np.where(ABS > 0, ABS, 1.0),
+                                                 np.where(ok, 0.0, np.inf)))))
+    return {"copies": len(As), "copies_max_err_ratio": worst,
+            "copies_within_tol": bool(worst <= 1e-4)}
+
+
 def per_config(args):
     """One JSON line per workload (the per-config record of the measurement
     plan): 5 warm-up calls, then 20 event-timed calls; median and min."""
@@ -283,6 +300,8 @@ def per_config(args):
                           "peak_tbps": PEAK_HBM_GBS / 1e3}}
         if not args.no_cpu_baseline:
             rec.update(cpu_baseline_config(w, C1.numpy(), Ci.numpy()))
+            if copies > 1:
+                rec.update(copies_parity(As, Bs, Cs))
         print(json.dumps(rec), flush=True)
         del As, Bs, Cs
         torch.cuda.empty_cache()
