@@ -101,10 +101,21 @@ __device__ __forceinline__ void dma_k_loop(float* lds_a0, float* lds_b0, float* 
       f.b[s0 + 1][j] = lb[(8 * q + 4 * lk + s0 + 1) * BN + b_off[j]];
     }
   };
+  // A wave tile of one 32 x 32 block would chain every MFMA on one
+  // accumulator; there the odd k-steps go to a second accumulator, added to
+  // the first after the loop (a fixed order: even steps + odd steps).
+  constexpr bool kDual = C_::kFragM * C_::kFragN == 1;
+  floatx16 acc_odd = {};
   auto mfma_one = [&](const Frag& f, int idx) {
     const int s = idx / (C_::kFragM * C_::kFragN);
     const int i = (idx / C_::kFragN) % C_::kFragM, j = idx % C_::kFragN;
     const float a = s == 0 ? f.a[i].x : s == 1 ? f.a[i].y : s == 2 ? f.a[i].z : f.a[i].w;
+    if constexpr (kDual) {
+      if (s & 1) {
+        acc_odd = __builtin_amdgcn_mfma_f32_32x32x2f32(a, f.b[s][j], acc_odd, 0, 0, 0);
+        return;
+      }
+    }
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, f.b[s][j], acc[i][j], 0, 0, 0);
   };
 
@@ -178,6 +189,7 @@ __device__ __forceinline__ void dma_k_loop(float* lds_a0, float* lds_b0, float* 
   }
   // no load into LDS may still be in flight when the workgroup ends
   __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (kDual) acc[0][0] += acc_odd;
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int kMinWaves>
