@@ -210,21 +210,6 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     for (int j = 0; j < C_::kFragN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  // A wave tile of one 32 x 32 block would chain every MFMA on one
-  // accumulator; there the odd k-steps go to a second accumulator, added to
-  // the first after the K loop (a fixed order: even steps + odd steps).  Not
-  // at four waves per SIMD, where the extra 16 registers would spill.
-  constexpr bool kDual = C_::kFragM * C_::kFragN == 1 && kMinWaves <= 2;
-  floatx16 acc_odd = {};
-  auto mma = [&](int i, int j, int s, float a, float b) {
-    if constexpr (kDual) {
-      if (s & 1) {
-        acc_odd = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc_odd, 0, 0, 0);
-        return;
-      }
-    }
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc[i][j], 0, 0, 0);
-  };
 
   // MFMAs of the 8-wide k groups [q0, q1) of LDS buffer `buf`
   auto compute = [&](int buf, int q0, int q1) {
@@ -246,7 +231,8 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
         for (int i = 0; i < C_::kFragM; ++i) {
           const float a = s == 0 ? fa[i].x : s == 1 ? fa[i].y : s == 2 ? fa[i].z : fa[i].w;
 #pragma unroll
-          for (int j = 0; j < C_::kFragN; ++j) mma(i, j, s, a, fb[j]);
+          for (int j = 0; j < C_::kFragN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, fb[j], acc[i][j], 0, 0, 0);
         }
       }
     }
@@ -277,7 +263,8 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
       for (int i = 0; i < C_::kFragM; ++i) {
         const float a = s == 0 ? f.a[i].x : s == 1 ? f.a[i].y : s == 2 ? f.a[i].z : f.a[i].w;
 #pragma unroll
-        for (int j = 0; j < C_::kFragN; ++j) mma(i, j, s, a, f.b[s][j]);
+        for (int j = 0; j < C_::kFragN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, f.b[s][j], acc[i][j], 0, 0, 0);
       }
   };
 
@@ -300,7 +287,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     const int s = idx / (C_::kFragM * C_::kFragN);
     const int i = (idx / C_::kFragN) % C_::kFragM, j = idx % C_::kFragN;
     const float a = s == 0 ? f.a[i].x : s == 1 ? f.a[i].y : s == 2 ? f.a[i].z : f.a[i].w;
-    mma(i, j, s, a, f.b[s][j]);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, f.b[s][j], acc[i][j], 0, 0, 0);
   };
   // Global load number idx (A chunks, then B) of a K-tile that lies inside
   // K, for any output tile.  Rows of A past M and columns of B past N are
@@ -463,7 +450,6 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     }
     for (; t < ktiles; ++t) step(t, std::false_type{}, std::false_type{});
   }
-  if constexpr (kDual) acc[0][0] += acc_odd;
 
   // ---- masked epilogue ----------------------------------------------------
 #pragma unroll

@@ -110,11 +110,6 @@ __global__ void __launch_bounds__(KS * 64)
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  // With one 32 x 32 block every MFMA would chain on one accumulator: the odd
-  // k-steps go to a second accumulator, added to the first after the K loop
-  // (a fixed order: even steps + odd steps).
-  constexpr bool kDual = FM * FN == 1;
-  floatx16 acc_odd = {};
   auto compute = [&](const Group& x) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -123,10 +118,7 @@ __global__ void __launch_bounds__(KS * 64)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const float a = s == 0 ? x.a[i].x : s == 1 ? x.a[i].y : s == 2 ? x.a[i].z : x.a[i].w;
-          if (kDual && (s & 1))
-            acc_odd = __builtin_amdgcn_mfma_f32_32x32x2f32(a, x.b[s][j], acc_odd, 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, x.b[s][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, x.b[s][j], acc[i][j], 0, 0, 0);
         }
   };
 
@@ -172,7 +164,6 @@ __global__ void __launch_bounds__(KS * 64)
         x.b[s][j] = k + s < K ? bcol[j][(int64_t)(8 * g_full + s) * ldb] : 0.f;
     compute(x);
   }
-  if constexpr (kDual) acc[0][0] += acc_odd;
 
   // ---- the waves' partial tiles, added in wave order -------------------------
   if (KS > 1) {
