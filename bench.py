@@ -92,9 +92,9 @@ def time_launches(fn, steps, warmup, stream, settle_s=0.3):
     return wall, per
 
 
-def traffic_for(kernel_name: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if it was taken on a different kernel source."""
+def profile_record(kernel_name: str):
+    """The committed rocprofv3 record of a kernel (profiles/traffic.json), or
+    None if there is none or it was taken on a different kernel source."""
     f = ROOT / "profiles" / "traffic.json"
     if not f.exists():
         return None
@@ -105,7 +105,14 @@ def traffic_for(kernel_name: str):
     from dense_fp32_gemm_f32_amd.prof_summary import source_hash
     if not rec or rec.get("source_sha256") != source_hash(kernel_name):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def traffic_for(kernel_name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if it was taken on a different kernel source."""
+    rec = profile_record(kernel_name)
+    return rec.get("hbm_bytes_per_launch") if rec else None
 
 
 def launch_amortisation(stream, steps, warmup, batch=64, n=512):
@@ -237,6 +244,17 @@ def cpu_baseline_config(w, C_gpu, C_gpu_int):
             "max_err_ratio": ratio, "int_bitexact": bool(np.array_equal(C_gpu_int, Ci_ref))}
 
 
+def _rocprof_fields(kname):
+    """The committed profile summary of the kernel and its calibrated HBM
+    bytes per launch against the algorithmic bytes (None if stale)."""
+    rec = profile_record(kname)
+    if not rec:
+        return None
+    return {"summary": "profiles/" + rec["summary"], "workload": rec["workload"],
+            "hbm_bytes_per_launch": rec["hbm_bytes_per_launch"],
+            "x_algorithmic": round(rec["hbm_bytes_per_launch"] / rec["algo_bytes"], 3)}
+
+
 def copies_parity(As, Bs, Cs):
     """Each rotated input copy's output from the timed calls (the last call on
     that copy) against the oracle: the largest |dC| / sum|a||b| over the
@@ -294,6 +312,7 @@ def per_config(args):
                "pct_hbm_peak": round(100 * w.algo_bytes / (t_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
                "repro_bitexact": bool(torch.equal(C1, C2)),
                "traffic": traffic_for(kname),
+               "rocprof": _rocprof_fields(kname),
                "device": {"name": props.name, "CUs": props.multi_processor_count,
                           "arch": getattr(props, "gcnArchName", ""),
                           "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
