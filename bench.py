@@ -22,6 +22,10 @@ of the same workload (the first R rows of A), scaled to GFLOP/s.
 --configs: one JSON line per workload instead (median and min of 20 timed
 calls, rate and fraction of peak, bitwise rerun check, and the oracle's time
 on the host with the GPU result's agreement with it).
+
+--shards: the same lines for one GPU's share of the 4096^3 and skinny
+products split 8 ways (the kernels at the shapes each GPU of a split would
+run; the collectives around them are not built).
 """
 from __future__ import annotations
 
@@ -51,6 +55,9 @@ def parse():
     ap.add_argument("--configs", action="store_true",
                     help="instead of the single headline line, print one JSON line per "
                          "workload (median/min time, rate, reruns, oracle time and agreement)")
+    ap.add_argument("--shards", action="store_true",
+                    help="the same per-workload lines for one GPU's share of the 4096^3 and "
+                         "skinny products split 8 ways (along M, N or K)")
     return ap.parse_args()
 
 
@@ -272,9 +279,12 @@ def copies_parity(As, Bs, Cs):
             "copies_within_tol": bool(worst <= 1e-4)}
 
 
-def per_config(args):
+def per_config(args, workloads, share_of=None):
     """One JSON line per workload (the per-config record of the measurement
-    plan): 5 warm-up calls, then 20 event-timed calls; median and min."""
+    plan): 300 ms of untimed calls, 5 warm-up calls, then 20 event-timed
+    calls; median and min.  An HBM-bound workload (M <= 16) rotates copies of
+    its inputs (at least 4, about 1 GiB of B in all, at most 16) so that B
+    streams from HBM rather than from the 256 MB last-level cache."""
     import torch
     from dense_fp32_gemm_f32_amd import binding, inputs
     binding.load()
@@ -282,8 +292,10 @@ def per_config(args):
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     props = torch.cuda.get_device_properties(dev)
-    for name, w in inputs.WORKLOADS.items():
-        copies = 4 if name == inputs.SKINNY else 1   # stream B from HBM, not the cache
+    for name, w in workloads.items():
+        hbm_bound = w.M <= 16
+        copies = max(4, -(-1024 * 2 ** 20 // (4 * w.K * w.N))) if hbm_bound else 1
+        copies = min(copies, 16)
         As, Bs, Cs = [], [], []
         for c in range(copies):
             a, b = (inputs.workload_inputs(w) if c == 0 else
@@ -302,8 +314,8 @@ def per_config(args):
         ai, bi = inputs.workload_inputs(w, integer=True)
         Ci = binding.gemm(ai.to(dev), bi.to(dev)).cpu()
         torch.cuda.synchronize()
-        rec = {"config": name, "M": w.M, "N": w.N, "K": w.K, "lda": w.K, "ldb": w.N,
-               "ldc": w.N, "seed": w.seed, "kernel_entry": kname,
+        rec = {"config": name, "M": w.M, "N": w.N, "K": w.K, "lda": w.lda or w.K,
+               "ldb": w.ldb or w.N, "ldc": w.ldc or w.N, "seed": w.seed, "kernel_entry": kname,
                "t_median_us": round(t_med * 1e3, 2), "t_min_us": round(t_min * 1e3, 2),
                "gflops": round(w.flops / (t_med * 1e-3) / 1e9, 1),
                "pct_mfma_peak": round(100 * w.flops / (t_med * 1e-3) / 1e12
@@ -311,12 +323,14 @@ def per_config(args):
                "gbps": round(w.algo_bytes / (t_med * 1e-3) / 1e9, 1),
                "pct_hbm_peak": round(100 * w.algo_bytes / (t_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
                "repro_bitexact": bool(torch.equal(C1, C2)),
-               "traffic": traffic_for(kname),
-               "rocprof": _rocprof_fields(kname),
+               "traffic": traffic_for(kname) if share_of is None else None,
+               "rocprof": _rocprof_fields(kname) if share_of is None else None,
                "device": {"name": props.name, "CUs": props.multi_processor_count,
                           "arch": getattr(props, "gcnArchName", ""),
                           "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
                           "peak_tbps": PEAK_HBM_GBS / 1e3}}
+        if share_of is not None:
+            rec["share_of"] = {"workload": share_of[name], "ways": inputs.SHARD_WAYS}
         if not args.no_cpu_baseline:
             rec.update(cpu_baseline_config(w, C1.numpy(), Ci.numpy()))
             if copies > 1:
@@ -333,8 +347,12 @@ def main():
               "(the library has no multi-GPU path; run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    if args.configs:
-        per_config(args)
+    if args.configs or args.shards:
+        from dense_fp32_gemm_f32_amd import inputs
+        if args.configs:
+            per_config(args, inputs.WORKLOADS)
+        if args.shards:
+            per_config(args, inputs.SHARDS, inputs.SHARD_OF)
         return
 
     import torch

@@ -389,6 +389,7 @@ std::string select_name(const Op& op, int64_t M, int64_t N, int64_t K, int64_t l
   if (!op.plain()) {
     for (const auto& row : gemmf32::kTuningGfx950Skinny) {
       if (M > row.max_m || row.ta != op.ta || row.tb != op.tb) continue;
+      if (row.max_n > 0 && N > row.max_n) continue;
       const int idx = find_entry(row.kernel);
       if (idx >= 0 && accepts(entries()[idx], op, M, N, K, lda, ldb, A, B)) return row.kernel;
     }
@@ -404,6 +405,7 @@ std::string select_name(const Op& op, int64_t M, int64_t N, int64_t K, int64_t l
   }
   for (const auto& row : gemmf32::kTuningGfx950) {
     if (M > row.max_m || tiles < row.min_tiles) continue;
+    if (row.max_tiles > 0 && tiles > row.max_tiles) continue;
     // a row whose kernel cannot take these arguments defers to the next one
     const int idx = find_entry(row.kernel);
     if (idx < 0 || !accepts(entries()[idx], op, M, N, K, lda, ldb, A, B)) continue;
@@ -540,6 +542,7 @@ std::string select_name_batched(int64_t M, int64_t N, int64_t K, int64_t lda, in
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128) * bt.count;
   for (const auto& row : gemmf32::kTuningGfx950) {
     if (M > row.max_m || tiles < row.min_tiles) continue;
+    if (row.max_tiles > 0 && tiles > row.max_tiles) continue;
     const int idx = find_entry(row.kernel);
     if (idx < 0 || entries()[idx].kind != Kind::Mfma) continue;
     if (!accepts(entries()[idx], Op{}, M, N, K, lda, ldb, A, B)) continue;

@@ -15,6 +15,7 @@
 //                them resident per CU, fill their last wave of the 256 CUs to
 //                at least 90 % or make 4 waves or more: a large tile is taken
 //                only where it leaves no part-empty last wave
+//   max_tiles    ... and (if not 0) the grid has at most this many tiles
 #pragma once
 
 #include <cstdint>
@@ -28,6 +29,7 @@ struct TuningRow {
   int64_t min_tiles;
   const char* kernel;
   int wave_slots = 0;
+  int64_t max_tiles = 0;
 };
 
 constexpr int64_t kAnyM = INT64_C(0x7fffffff);
@@ -38,7 +40,10 @@ constexpr TuningRow kTuningGfx950[] = {
     {8, 160, "skinnyr_c2_r4_u4_m2x4_s0_nn"},
     // 64-column strips, K slices added in-kernel through exchange slots
     // (8 x 8192 x 8192: 45 us against 48 us for 128-column strips and a
-    // combine dispatch; 8 x 512 x 8192: 13 us against 18 us)
+    // combine dispatch; 8 x 512 x 8192: 13 us against 18 us).  Up to 2048
+    // columns, 16 waves per workgroup keep more of B in flight (8 x 1024 x
+    // 8192: 13.8 us against 15.2 us; 8 x 512 x 8192: 12.0 against 14.0 us)
+    {16, 0, "skinnyx_w16_c2_u2_s0_vec", 0, 16},
     {16, 0, "skinnyx_w8_c2_u2_s0_vec"},
     // 256 x 256 tiles, 8 waves of 64 x 128 (4096^3: 939 us against 958 us)
     {kAnyM, 768, "mfma_256x256x32_w64x128_d6_vec", 1},
@@ -74,14 +79,16 @@ constexpr TuningRowEx kTuningGfx950Ex[] = {
     {0, "mfmaex_64x64x32_w32x32"},
 };
 
-// M <= 16 with a transposed operand or an epilogue: the first row whose max_m
-// and layout match (ta: A stored K x M, tb: B stored N x K).
+// M <= 16 with a transposed operand or an epilogue: the first row whose max_m,
+// layout (ta: A stored K x M, tb: B stored N x K) and max_n (if not 0) match.
 struct TuningRowSkinny {
   int64_t max_m;
   bool ta, tb;
   const char* kernel;
+  int64_t max_n = 0;
 };
 constexpr TuningRowSkinny kTuningGfx950Skinny[] = {
+    {16, false, false, "skinnyx_w16_c2_u2_s0_vec", 2048},
     {16, false, false, "skinnyx_w8_c2_u2_s0_vec"},
     {16, true, false, "skinnyx_w8_c2_u2_s0_tn"},
     {8, false, true, "skinnyt_m8_j4_u2_nt"},

@@ -62,6 +62,23 @@ WORKLOADS = {
 HEADLINE = "square_4096"
 SKINNY = "skinny_8x8192x8192"
 
+# One GPU's share of a product split 8 ways (each share stored packed on its
+# own GPU).  Along M or N a share is a whole product of its own; along K it
+# is a full-size partial C that a reduce-scatter would add up.
+SHARD_WAYS = 8
+SHARDS = {
+    "square_4096_split_m": Workload("square_4096_split_m", 512, 4096, 4096, "u11", "u11",
+                                    1013, 2013),
+    "square_4096_split_n": Workload("square_4096_split_n", 4096, 512, 4096, "u11", "u11",
+                                    1023, 2023),
+    "square_4096_split_k": Workload("square_4096_split_k", 4096, 4096, 512, "u11", "u11",
+                                    1033, 2033),
+    "skinny_8x8192x8192_split_n": Workload("skinny_8x8192x8192_split_n", 8, 1024, _SKINNY_K,
+                                           "normal", "u_inv_sqrt_k", 1015, 2015),
+}
+SHARD_OF = {"square_4096_split_m": HEADLINE, "square_4096_split_n": HEADLINE,
+            "square_4096_split_k": HEADLINE, "skinny_8x8192x8192_split_n": SKINNY}
+
 
 def _draw(dist: str, rows: int, cols: int, g: torch.Generator, K: int) -> torch.Tensor:
     if dist == "u11":
@@ -106,7 +123,7 @@ def make_ab(M: int, N: int, K: int, dist_a: str, dist_b: str, seed: int,
 def workload_inputs(w: Workload | str, integer: bool = False):
     """A and B of a named workload, float or integer {-2..2} variant."""
     if isinstance(w, str):
-        w = WORKLOADS[w]
+        w = WORKLOADS[w] if w in WORKLOADS else SHARDS[w]
     if integer:
         return make_ab(w.M, w.N, w.K, "int2", "int2", w.int_seed, w.lda, w.ldb)
     return make_ab(w.M, w.N, w.K, w.dist_a, w.dist_b, w.seed, w.lda, w.ldb)

@@ -9,7 +9,8 @@ kernel that accepts the shape runs ``--warmup`` times, then ``--reps`` times
 with a HIP event pair on the launch stream around each call, the candidates
 taking turns (after --spin-ms of load to settle the clocks); the median is
 reported.  Inputs rotate over enough copies to exceed the 256 MB last-level
-cache when B is large, so bandwidth-bound shapes stream from HBM.  Prints one line per (shape, kernel).
+cache when B is large or the shape is skinny (M <= 16), so bandwidth-bound
+shapes stream from HBM.  Prints one line per (shape, kernel).
 """
 from __future__ import annotations
 
@@ -54,7 +55,13 @@ def main(argv=None):
     for shape in args.shapes.split(","):
         M, N, K = parse_shape(shape)
         b_bytes = 4 * K * N
-        copies = max(1, min(4, -(-1024 * 2 ** 20 // max(b_bytes, 1)))) if b_bytes > 32 * 2 ** 20 else 1
+        if M <= 16 and b_bytes >= 2 ** 20:
+            # bound by HBM: about 1 GiB of B in rotation
+            copies = max(1, min(32, -(-1024 * 2 ** 20 // b_bytes)))
+        elif b_bytes > 32 * 2 ** 20:
+            copies = max(1, min(4, -(-1024 * 2 ** 20 // b_bytes)))
+        else:
+            copies = 1
         As, Bs, Cs = [], [], []
         ta, tb = args.layout[0] == "t", args.layout[1] == "t"
         for c in range(copies):

@@ -48,3 +48,18 @@ def test_traffic_is_reported_only_for_matching_sources(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", tmp_path)
     assert bench.traffic_for(name) is None
     assert bench.traffic_for("no_such_kernel") is None
+
+
+@pytest.mark.parametrize("name", list(inputs.SHARDS))
+def test_shard_is_one_share_of_its_workload(name):
+    """Each shard workload is the full product cut 8 ways along one of M, N
+    or K, with the full workload's distributions (B's scale depends on K,
+    which no split of M or N changes)."""
+    s, w = inputs.SHARDS[name], inputs.WORKLOADS[inputs.SHARD_OF[name]]
+    ways = inputs.SHARD_WAYS
+    cuts = [(s.M * ways, s.N, s.K), (s.M, s.N * ways, s.K), (s.M, s.N, s.K * ways)]
+    assert sum(c == (w.M, w.N, w.K) for c in cuts) == 1
+    assert (s.dist_a, s.dist_b) == (w.dist_a, w.dist_b)
+    if w.dist_b == "u_inv_sqrt_k":
+        assert s.K == w.K
+    assert s.flops * ways == w.flops

@@ -14,7 +14,12 @@ from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
-WORKLOADS = list(inputs.WORKLOADS)
+# the measured workloads, and one GPU's share of two of them split 8 ways
+WORKLOADS = list(inputs.WORKLOADS) + list(inputs.SHARDS)
+
+
+def _workload(name):
+    return inputs.WORKLOADS[name] if name in inputs.WORKLOADS else inputs.SHARDS[name]
 
 
 def _run(lib, A_cpu, B_cpu, ldc=None, kernel=None, ref=False, offsets=(0, 0, 0)):
@@ -37,7 +42,7 @@ def _run(lib, A_cpu, B_cpu, ldc=None, kernel=None, ref=False, offsets=(0, 0, 0))
 
 @pytest.mark.parametrize("name", WORKLOADS)
 def test_workload_float(gpu_lib, name):
-    w = inputs.WORKLOADS[name]
+    w = _workload(name)
     A, B = inputs.workload_inputs(w)
     H.say(f"float workload {name} kernel={gpu_lib.selected_kernel(A, B)}")
     C, flat, ldc = _run(gpu_lib, A, B, ldc=w.ldc)
@@ -49,7 +54,7 @@ def test_workload_float(gpu_lib, name):
 
 @pytest.mark.parametrize("name", WORKLOADS)
 def test_workload_integer_bitexact(gpu_lib, name):
-    w = inputs.WORKLOADS[name]
+    w = _workload(name)
     A, B = inputs.workload_inputs(w, integer=True)
     H.say(f"integer workload {name}")
     C, flat, ldc = _run(gpu_lib, A, B, ldc=w.ldc)
