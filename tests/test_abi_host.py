@@ -103,6 +103,11 @@ def test_adjacent_but_not_overlapping_is_not_alias():
     (3, 8192, 8192, 8192, 8192, P16, Q16, "skinnyx_w8_c2_u2"),
     (16, 4096, 4096, 4096, 4096, P16, Q16, "skinnyx_w8_c2_u2"),
     (8, 3001, 1531, 1531, 3001, P16, Q16, "skinnyx_w8_c2_u2"),
+    # up to 2048 columns (16 tiles of 128): 16 waves per workgroup
+    (8, 1024, 8192, 8192, 1024, P16, Q16, "skinnyx_w16_c2_u2"),
+    (16, 2048, 8192, 8192, 2048, P16, Q16, "skinnyx_w16_c2_u2"),
+    (1, 7, 5, 5, 7, P16, Q16, "skinnyx_w16_c2_u2"),
+    (8, 2049, 8192, 8192, 2049, P16, Q16, "skinnyx_w8_c2_u2"),
     # wide N: KiB row runs, when B's rows are 16-byte aligned; else the tile kernel
     (8, 28672, 4096, 4096, 28672, P16, Q16, "skinnyr_c2_r4"),
     (8, 28672, 4096, 4096, 28673, P16, Q16, "skinnyx_w8_c2_u2"),
@@ -341,3 +346,15 @@ def test_fused_selects_the_extended_kernels():
     plain = names.index("mfma_64x64x32_w32x32_p5_vec")
     assert binding.gemm_f32_run_kernel_fused(plain, 0, 0, 4, 4, 4, 1.0, P16, 4, Q16, 4, 0.0,
                                              R16, 4, 0, 1, 0) in (5, 8)
+
+
+def test_extended_skinny_rows_by_width():
+    """With an epilogue, A and B as stored: the 16-wave exchange kernel up to
+    2048 columns, the 8-wave one above; A stored transposed: its own kernel."""
+    sel = binding.gemm_f32_selected_kernel_ex
+    assert sel(0, 0, 8, 1024, 8192, 8192, 1024, 1024, 2.0, 1.0, P16, Q16, R16) == \
+        "skinnyx_w16_c2_u2_s0_vec"
+    assert sel(0, 0, 8, 2049, 8192, 8192, 2049, 2049, 2.0, 1.0, P16, Q16, R16) == \
+        "skinnyx_w8_c2_u2_s0_vec"
+    assert sel(1, 0, 8, 1024, 8192, 8, 1024, 1024, 2.0, 1.0, P16, Q16, R16) == \
+        "skinnyx_w8_c2_u2_s0_tn"
