@@ -332,6 +332,9 @@ const MfmaVariant kDmaVariants[] = {
     GEMMF32_MFMA_DMA(256, 256, 16, 64, 128, 1),
     GEMMF32_MFMA_DMA(256, 256, 32, 128, 64, 1),
     GEMMF32_MFMA_DMA(256, 256, 32, 64, 128, 1),
+    GEMMF32_MFMA_DMA(128, 192, 32, 32, 96, 2),
+    GEMMF32_MFMA_DMA(192, 128, 32, 96, 32, 2),
+    GEMMF32_MFMA_DMA(128, 128, 32, 64, 32, 2),
 };
 
 }  // namespace

@@ -52,6 +52,13 @@ constexpr TuningRow kTuningGfx950[] = {
     // waves (8191^2 x 2001: 128 x 128, 2126 us; 4096 x 4097 x 4096: 128 x 192,
     // 1187 us, against 1217 us for 64 x 64 tiles)
     {kAnyM, 768, "mfma_128x128x32_w64x64_p5_vec", 2},
+    // 128 x 192 or 192 x 128 tiles where one per CU makes whole waves
+    // (2048 x 3072 x 1536: 148 us against 192 us for 128 x 128 tiles)
+    {kAnyM, 192, "mfma_128x192x32_w32x96_d6_vec", 1},
+    {kAnyM, 192, "mfma_192x128x32_w96x32_d6_vec", 1},
+    // 128 x 128 tiles, 8 waves of 64 x 32 (2048^3: 133.5 us against 137.9 us
+    // for 4 waves of 64 x 64, which remain for K a multiple of 16 only)
+    {kAnyM, 192, "mfma_128x128x32_w64x32_d6_vec"},
     {kAnyM, 192, "mfma_128x128x16_w64x64_d6_vec"},
     // 128 x 192 or 192 x 128 tiles of 8 waves where they make whole waves
     // (2047 x 3001 x 1531: 256 tiles, 170 us against 185 us for 64 x 64)

@@ -125,6 +125,13 @@ def test_adjacent_but_not_overlapping_is_not_alias():
     (3001, 2047, 1531, 1531, 2047, P16, Q16, "mfma_192x128x32_w96x32_p5"),   # 256 tiles
     (2049, 2049, 2049, 2049, 2049, P16, Q16, "mfma_64x64x32_w32x32_p5"),     # 187 of 256
     (7936, 7936, 4096, 4096, 7936, P16, Q16, "mfma_256x256x32_w64x128_d6"),  # 961 of 1024
+    # aligned operands: 128 x 192 (or 192 x 128) direct-to-LDS tiles where one
+    # per CU fills whole waves, else 128 x 128
+    (2048, 3072, 1536, 1536, 3072, P16, Q16, "mfma_128x192x32_w32x96_d6"),   # 256 tiles
+    (3072, 2048, 1536, 1536, 2048, P16, Q16, "mfma_192x128x32_w96x32_d6"),   # 256 tiles
+    (2048, 3008, 1536, 1536, 3008, P16, Q16, "mfma_128x192x32_w32x96_d6"),   # 256 tiles
+    (2048, 2048, 2048, 2048, 2048, P16, Q16, "mfma_128x128x32_w64x32_d6"),   # 176 of 256
+    (2048, 2048, 2064, 2064, 2048, P16, Q16, "mfma_128x128x16_w64x64_d6"),   # K % 32 = 16
     (512, 512, 512, 512, 512, P16, Q16, "mfma_32x32x8_k4_g4_small"),
     (768, 768, 768, 768, 768, P16, Q16, "mfma_64x64x32_w32x32_d6"),
     (1024, 1024, 1024, 1024, 1024, P16, Q16, "mfma_64x64x32_w32x32_d6"),
