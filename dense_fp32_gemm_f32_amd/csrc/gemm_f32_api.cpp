@@ -291,7 +291,10 @@ bool accepts(const Entry& e, const Op& op, int64_t M, int64_t N, int64_t K, int6
              int64_t ldb, const void* A, const void* B) {
   if (e.kind == Kind::MfmaEx) {
     const auto& v = gemmf32::mfma_ex_variant(e.sub);
-    return v.trans_a == op.ta && v.trans_b == op.tb;
+    if (v.trans_a != op.ta || v.trans_b != op.tb) return false;
+    if (!v.lds_dma) return true;
+    return K >= v.bk && K % v.bk == 0 && lda % 4 == 0 && ldb % 4 == 0 &&
+           (!op.ta || M % 4 == 0) && (op.tb || N % 4 == 0) && aligned16(A) && aligned16(B);
   }
   if (e.kind == Kind::Skinny) {
     // any alpha and beta; the layout the kernel was built for
@@ -373,9 +376,17 @@ int run_entry(const Entry& e, const Op& op, const Problem& p, int dev, hipStream
 // resident per CU, leave the last wave at least 90 % full, or make four waves
 // or more?  (w waves of work take ceil(w) waves of time.)
 bool fills_waves(const Entry& e, int64_t M, int64_t N, int64_t batch, int slots) {
-  if (e.kind != Kind::Mfma && e.kind != Kind::MfmaSplitK) return true;
-  const auto& v = gemmf32::mfma_variant(e.sub);
-  const int64_t wgs = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn) * batch;
+  int64_t bm, bn;
+  if (e.kind == Kind::Mfma || e.kind == Kind::MfmaSplitK) {
+    bm = gemmf32::mfma_variant(e.sub).bm;
+    bn = gemmf32::mfma_variant(e.sub).bn;
+  } else if (e.kind == Kind::MfmaEx) {
+    bm = gemmf32::mfma_ex_variant(e.sub).bm;
+    bn = gemmf32::mfma_ex_variant(e.sub).bn;
+  } else {
+    return true;
+  }
+  const int64_t wgs = ((M + bm - 1) / bm) * ((N + bn - 1) / bn) * batch;
   const int64_t per_wave = gemmf32::kNumCus * slots;
   const int64_t waves = (wgs + per_wave - 1) / per_wave;
   return waves >= 4 || 10 * wgs >= 9 * waves * per_wave;
@@ -399,7 +410,12 @@ std::string select_name(const Op& op, int64_t M, int64_t N, int64_t K, int64_t l
     if (op.ta || op.tb) {
       for (const auto& row : gemmf32::kTuningGfx950Ex) {
         if (tiles < row.min_tiles) continue;
-        return std::string(row.kernel) + kLayout[op.ta][op.tb];
+        // a row whose kernel cannot take these arguments defers to the next one
+        const std::string name = std::string(row.kernel) + kLayout[op.ta][op.tb];
+        const int idx = find_entry(name.c_str());
+        if (idx < 0 || !accepts(entries()[idx], op, M, N, K, lda, ldb, A, B)) continue;
+        if (row.wave_slots > 0 && !fills_waves(entries()[idx], M, N, 1, row.wave_slots)) continue;
+        return name;
       }
     }
   }

@@ -89,9 +89,16 @@ struct MfmaExVariant {
   int bm, bn, bk;
   bool trans_a, trans_b;
   hipError_t (*launch)(const Problem&, const Epilogue&, hipStream_t);
+  // direct-to-LDS loads: A and B 16-byte aligned, lda and ldb multiples of 4,
+  // K a multiple of bk, M (A^T) or N (B as is) a multiple of 4
+  bool lds_dma = false;
 };
+// The register-staged kernels (kernels_mfma_ex.hip), then the direct-to-LDS
+// ones (kernels_mfma_ex_dma.hip).
 int mfma_ex_variant_count();
 const MfmaExVariant& mfma_ex_variant(int i);
+int mfma_ex_dma_variant_count();
+const MfmaExVariant& mfma_ex_dma_variant(int i);
 
 // ---- skinny-M kernels (M <= 16) --------------------------------------------
 // Three kernels: B stored K x N (column tiles x K slices, MFMA; kernels_skinny.hip,

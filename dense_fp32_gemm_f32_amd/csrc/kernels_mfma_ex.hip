@@ -390,7 +390,12 @@ const MfmaExVariant kExVariants[] = {
 
 }  // namespace
 
-int mfma_ex_variant_count() { return (int)(sizeof(kExVariants) / sizeof(kExVariants[0])); }
-const MfmaExVariant& mfma_ex_variant(int i) { return kExVariants[i]; }
+int mfma_ex_variant_count() {
+  return (int)(sizeof(kExVariants) / sizeof(kExVariants[0])) + mfma_ex_dma_variant_count();
+}
+const MfmaExVariant& mfma_ex_variant(int i) {
+  const int n = (int)(sizeof(kExVariants) / sizeof(kExVariants[0]));
+  return i < n ? kExVariants[i] : mfma_ex_dma_variant(i - n);
+}
 
 }  // namespace gemmf32

@@ -73,16 +73,24 @@ constexpr TuningRow kTuningGfx950[] = {
 };
 
 // A transposed operand (any epilogue): the first row with at least min_tiles
-// tiles of 128 x 128 names the tile; the layout suffix (_nt, _tn, _tt) comes
-// from the call.  A and B as stored with an epilogue (alpha, beta, bias,
-// activation) use the plain table above: its kernels apply the epilogue.
+// tiles of 128 x 128 whose kernel, with the layout suffix (_nt, _tn, _tt) of
+// the call, takes the arguments (and, if wave_slots is not 0, fills whole
+// waves as above).  Direct-to-LDS tiles come first; the register-staged tiles
+// after them take any 4-byte aligned operands.  A and B as stored with an
+// epilogue (alpha, beta, bias, activation) use the plain table above: its
+// kernels apply the epilogue.
 struct TuningRowEx {
   int64_t min_tiles;
   const char* kernel;
+  int wave_slots = 0;
 };
 constexpr TuningRowEx kTuningGfx950Ex[] = {
+    {768, "mfmaex_256x256x32_w64x128_d6", 1},
+    {768, "mfmaex_128x128x32_w64x32_d6"},
     {768, "mfmaex_128x128x16_w64x64"},
+    {192, "mfmaex_128x128x32_w64x32_d6"},
     {192, "mfmaex_128x64x32_w64x32"},
+    {0, "mfmaex_64x64x32_w32x32_d6"},
     {0, "mfmaex_64x64x32_w32x32"},
 };
 

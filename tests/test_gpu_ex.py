@@ -78,6 +78,10 @@ def _shapes_for(kname):
         return [(min(mr, 7), 1003, 2057), (mr, 37, 8200)]
     if kname.startswith("skinny"):
         return [(13, 1003, 2057), (3, 130, 777)]
+    if "_d6_" in kname:
+        # direct-to-LDS loads: K a multiple of the K-tile, M and N multiples of
+        # 4; ragged edges in M and N; one K-tile, two and several
+        return [(300, 268, 192), (132, 68, 32), (68, 260, 64)]
     # ragged edges in M, N and K; M, N not multiples of 4 (element-wise edge
     # loads of a transposed operand); long enough for the branch-free loop
     return [(301, 263, 139), (130, 70, 333)]
@@ -87,8 +91,10 @@ def _shapes_for(kname):
 def test_every_ex_kernel(gpu_lib, kname):
     lay = kname.rsplit("_", 1)[-1][-2:]
     ta, tb = lay[0] == "t", lay[1] == "t"
-    # skinnyr kernels need B's pitch a multiple of 4
-    pads = (3, 4, 7) if kname.startswith("skinnyr_") else (3, 5, 7)
+    # skinnyr kernels need B's pitch a multiple of 4; direct-to-LDS kernels
+    # both pitches
+    pads = ((3, 4, 7) if kname.startswith("skinnyr_") else
+            (4, 8, 7) if "_d6_" in kname else (3, 5, 7))
     for (M, N, K) in _shapes_for(kname):
         _case(gpu_lib, M, N, K, ta, tb, 2.0, -1.0, True, 7001, kernel=kname, pads=pads)
         _case(gpu_lib, M, N, K, ta, tb, 1.0, 0.0, True, 7002, kernel=kname, pads=pads)

@@ -88,6 +88,10 @@ def _shapes_for(kname):
         return [(min(mr, 7), 1003, 2057), (mr, 37, 8200)], (3, 5, 7)
     if kname.startswith("skinny"):
         return [(13, 1003, 2057), (3, 130, 777)], (3, 5, 7)
+    if "_d6_" in kname:
+        # direct-to-LDS loads: K a multiple of the K-tile, M, N and the pitches
+        # of A and B multiples of 4
+        return [(300, 268, 192), (132, 68, 64)], (4, 8, 7)
     return [(301, 263, 139), (130, 70, 333)], (3, 5, 7)
 
 
