@@ -8,7 +8,9 @@ input C and the bias, so every partial sum is an exact binary32 integer
 
 The mix covers the skinny-M path, mid-size grids (K split over workgroups or
 over the waves of a workgroup) and many-tile grids, each in all four layouts.
-A second sweep draws strided batches.
+A second sweep keeps M, N and the pitches multiples of 4 and K a multiple of
+32, the conditions under which the dispatcher takes the kernels with direct
+global-to-LDS loads, plain and transposed.  A third draws strided batches.
 """
 import random
 
@@ -22,6 +24,7 @@ from tests import gpu_helpers as H
 pytestmark = pytest.mark.gpu
 
 CASES = 50
+ALIGNED_CASES = 24
 BATCH_CASES = 12
 
 
@@ -47,11 +50,30 @@ def _draw(rng):
     return M, N, K, ta, tb, pads, alpha, beta, bias, act
 
 
+def _draw_aligned(rng):
+    M, N = 4 * rng.randint(5, 400), 4 * rng.randint(5, 600)
+    K = 32 * rng.randint(1, 32)
+    ta, tb = rng.random() < 0.5, rng.random() < 0.5
+    pads = (rng.choice([0, 4, 8]), rng.choice([0, 4, 12]), rng.choice([0, 1, 5]))
+    alpha = rng.choice([1.0, 2.0, -1.0])
+    beta = rng.choice([0.0, 1.0, -2.0])
+    return M, N, K, ta, tb, pads, alpha, beta, rng.random() < 0.3, 1 if rng.random() < 0.3 else 0
+
+
 @pytest.mark.parametrize("case", range(CASES))
 def test_random_case(gpu_lib, case):
     rng = random.Random(9100 + case)
-    M, N, K, ta, tb, pads, alpha, beta, with_bias, act = _draw(rng)
-    seed = 9200 + 10 * case
+    _check_case(gpu_lib, case, 9200 + 10 * case, *_draw(rng))
+
+
+@pytest.mark.parametrize("case", range(ALIGNED_CASES))
+def test_random_aligned_case(gpu_lib, case):
+    rng = random.Random(9600 + case)
+    kname = _check_case(gpu_lib, 1000 + case, 9700 + 10 * case, *_draw_aligned(rng))
+    assert "_d6_" in kname, kname
+
+
+def _check_case(gpu_lib, case, seed, M, N, K, ta, tb, pads, alpha, beta, with_bias, act):
     A, B = inputs.make_ab(M, N, K, "int2", "int2", seed)
     As, Bs = _stored(A, ta, pads[0]), _stored(B, tb, pads[1])
     ldc = N + pads[2]
@@ -80,6 +102,7 @@ def test_random_case(gpu_lib, case):
                                     bias=None if bias is None else bias.numpy(), act=act)
     H.assert_bitexact(Cd.cpu().numpy(), C_ref, f"random case {case} ({kname})")
     H.check_outside_untouched(flat, M, N, ldc)
+    return kname
 
 
 @pytest.mark.parametrize("case", range(BATCH_CASES))
