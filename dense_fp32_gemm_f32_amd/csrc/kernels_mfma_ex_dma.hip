@@ -28,30 +28,13 @@
 #include <type_traits>
 
 #include "gemm_f32_internal.h"
+#include "lds_dma.h"
 #include "mfma_common.h"
 
 namespace gemmf32 {
 namespace {
 
 using namespace mfma;
-
-// One 16-byte global -> LDS copy per lane (M0 holds the wave's LDS address;
-// saved and restored around the instruction).  Inline assembly, because the
-// compiler's wait-count pass cannot tell the two LDS buffers apart when the
-// builtin is used and would make every LDS read wait for all loads in flight.
-__device__ __forceinline__ void copy_lds16(const float* g, float* lds_wave) {
-  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)((__attribute__((address_space(3))) float*)lds_wave));
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(g), "s"(lds_addr)
-      : "memory");
-}
 
 // One operand's K-tile: R rows (BM for A, BN for B) by BK, kWaves waves.
 template <int R, int BK, int kWaves, bool KC>
@@ -88,7 +71,7 @@ struct DmaOperand {
   }
   __device__ __forceinline__ void copy(int v, float* lds, int64_t ld, int k0, int wave) const {
     const int64_t step = KC ? (int64_t)k0 : (int64_t)k0 * ld;
-    copy_lds16(src[v] + step, lds + (v * kWaves + wave) * 256);
+    load_lds16(src[v] + step, lds + (v * kWaves + wave) * 256);
   }
 
   // Fragment reads of one k group q (8 k) for the wave's blocks starting at

@@ -37,10 +37,11 @@ def kernel_sources(kernel: str | None = None) -> list[str]:
         return every
     files = ["gemm_f32_internal.h"]
     if kernel.startswith("mfmaex_"):
-        files += ["kernels_mfma_ex.hip", "mfma_common.h"]
+        files += (["kernels_mfma_ex_dma.hip", "lds_dma.h"] if "_d6_" in kernel else
+                  ["kernels_mfma_ex.hip"]) + ["mfma_common.h"]
     elif kernel.startswith("mfma_"):
-        files += ["kernels_mfma_dma.hip" if "_d6_" in kernel else "kernels_mfma.hip",
-                  "mfma_common.h"]
+        files += (["kernels_mfma_dma.hip", "lds_dma.h"] if "_d6_" in kernel else
+                  ["kernels_mfma.hip"]) + ["mfma_common.h"]
         if "_sk_" in kernel:
             files.append("kernels_combine.hip")
     elif kernel.startswith("skinnyr_"):
