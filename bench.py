@@ -14,7 +14,9 @@ is timed the same way (with rotating copies of B so it streams from HBM, not
 from the 256 MB last-level cache) and reported under "secondary"; each
 secondary measurement first runs its own call untimed for 300 ms, so that
 short kernels are not timed at the idle clocks the host-side work before
-them leaves.
+them leaves.  Also under "secondary": 64 batched 512^3 products, the sum of
+2^26 floats, 4096^3 with bias and ReLU, and 4096^3 with an operand stored
+transposed (nt, tn, tt).
 
 cpu_baseline: the CPU oracle (binary64 triple loop) timed on a bounded sample
 of the same workload (the first R rows of A), scaled to GFLOP/s.
@@ -204,6 +206,30 @@ def fused_epilogue(stream, steps, warmup):
         mean_ms = sum(per) / len(per)
         out[name] = {"ms": round(mean_ms, 4),
                      "TFLOP/s": round(w.flops / (mean_ms * 1e-3) / 1e12, 2)}
+    return out
+
+
+def transposed_layouts(stream, steps, warmup):
+    """4096^3 with an operand stored transposed (gemm_f32_ex; B stored N x K,
+    A stored K x M, or both), the same inputs as the headline."""
+    import torch
+    from dense_fp32_gemm_f32_amd import binding, inputs
+    w = inputs.WORKLOADS[inputs.HEADLINE]
+    A_cpu, B_cpu = inputs.workload_inputs(w)
+    C = torch.empty((w.M, w.N), device="cuda")
+    out = {}
+    for lay in ("nt", "tn", "tt"):
+        ta, tb = lay[0] == "t", lay[1] == "t"
+        A = (A_cpu.t().contiguous() if ta else A_cpu).cuda()
+        B = (B_cpu.t().contiguous() if tb else B_cpu).cuda()
+        kname = binding.selected_kernel_ex(A, B, C, trans_a=ta, trans_b=tb)
+        _, per = time_launches(lambda _i: binding.gemm_ex(A, B, C, trans_a=ta, trans_b=tb),
+                               steps, warmup, stream)
+        mean_ms = sum(per) / len(per)
+        tflops = w.flops / (mean_ms * 1e-3) / 1e12
+        out[lay] = {"kernel": kname, "ms": round(mean_ms, 4), "TFLOP/s": round(tflops, 2),
+                    "frac": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4)}
+        del A, B
     return out
 
 
@@ -439,6 +465,8 @@ def main():
                                                         args.warmup)
         result["secondary"]["fused_bias_relu_4096"] = fused_epilogue(stream, args.steps,
                                                                      args.warmup)
+        result["secondary"]["transposed_4096"] = transposed_layouts(stream, args.steps,
+                                                                    args.warmup)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
