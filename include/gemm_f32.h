@@ -101,6 +101,12 @@ enum gemm_f32_status {
  * the GEMM Optimization Guide (section 4); the K split and its second pass
  * follow "GPU compute shaders" (How it works, step 6).  Arguments as
  * described above.
+ *
+ * Speed: A and B 16-byte aligned, lda, ldb and N multiples of 4 and K a
+ * multiple of 32 (16 for some tiles) let the dispatcher take the kernels that
+ * load tiles straight from global memory into LDS; any other 4-byte aligned
+ * operands run register-staged kernels of the same tiles, typically 5-25 %
+ * slower.
  */
 int gemm_f32(int64_t M, int64_t N, int64_t K,
              const float *A, int64_t lda,
@@ -127,6 +133,8 @@ int gemm_f32(int64_t M, int64_t N, int64_t K,
  * alpha and beta as they store C (exactly gemm_f32 when alpha = 1, beta = 0);
  * a transposed operand runs the extended-operation kernels.  Same checks and
  * errors as gemm_f32, with the pitches checked against the stored shapes.
+ * Those load tiles straight into LDS under gemm_f32's conditions, with M a
+ * multiple of 4 when A is transposed and N a multiple of 4 when B is not.
  */
 int gemm_f32_ex(int transA, int transB,
                 int64_t M, int64_t N, int64_t K,
