@@ -365,3 +365,30 @@ def test_extended_skinny_rows_by_width():
         "skinnyx_w8_c2_u2_s0_vec"
     assert sel(1, 0, 8, 1024, 8192, 8, 1024, 1024, 2.0, 1.0, P16, Q16, R16) == \
         "skinnyx_w8_c2_u2_s0_tn"
+
+
+def test_extended_direct_loads_only_under_their_conditions():
+    """A transposed operand takes the direct-to-LDS extended kernels only with
+    16-byte aligned A and B, lda and ldb multiples of 4, K a multiple of 32,
+    M a multiple of 4 when A is transposed and N when B is not; otherwise the
+    register-staged kernel of the same row class."""
+    sel = binding.gemm_f32_selected_kernel_ex
+    for ta, tb in [(0, 1), (1, 0), (1, 1)]:
+        lay = f"_{'t' if ta else 'n'}{'t' if tb else 'n'}"
+        good = sel(ta, tb, 1024, 1024, 1024, 1024, 1024, 1024, 1.0, 0.0, P16, Q16, R16)
+        assert good == "mfmaex_64x64x32_w32x32_d6" + lay, good
+        assert sel(ta, tb, 4096, 4096, 4096, 4096, 4096, 4096, 1.0, 0.0, P16, Q16, R16) == \
+            "mfmaex_256x256x32_w64x128_d6" + lay
+        bad = [
+            (1024, 1024, 1040, 1040 if not ta else 1024, 1040 if tb else 1024, P16, Q16),  # K % 32
+            (1024, 1024, 1024, 1025, 1025, P16, Q16),                                    # pitches
+            (1024, 1024, 1024, 1024, 1024, P16 + 4, Q16),                                # A alignment
+        ]
+        if ta:
+            bad.append((1022, 1024, 1024, 1024, 1024, P16, Q16))                         # M % 4, A^T
+        if not tb:
+            bad.append((1024, 1022, 1024, 1024, 1024, P16, Q16))                         # N % 4, B
+        for M, N, K, lda_, ldb_, pa, pb in bad:
+            name = sel(ta, tb, M, N, K, lda_, ldb_, max(N, 1), 1.0, 0.0, pa, pb, R16)
+            assert name.startswith("mfmaex_") and "_d6_" not in name, (ta, tb, M, N, K, name)
+            assert name.endswith(lay), name
