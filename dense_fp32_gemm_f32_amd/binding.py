@@ -46,16 +46,20 @@ class GemmError(RuntimeError):
 _lib = None
 
 
-def load():
-    """Load the HIP library (once).  Raises if it has not been built."""
+def load(lib_path=None):
+    """Load the HIP library (once; ``lib_path`` picks another build of it,
+    such as the sweep library of tune.py).  Raises if it has not been built."""
     global _lib
     if _lib is not None:
+        if lib_path is not None and Path(lib_path) != Path(_lib._name):
+            raise RuntimeError(f"{_lib._name} is already loaded")
         return _lib
-    if not LIB_PATH.exists():
+    path = Path(lib_path) if lib_path is not None else LIB_PATH
+    if not path.exists():
         raise FileNotFoundError(
-            f"{LIB_PATH} is missing: build it with `python -m dense_fp32_gemm_f32_amd.build_lib` "
+            f"{path} is missing: build it with `python -m dense_fp32_gemm_f32_amd.build_lib` "
             "(there is no CPU or PyTorch fallback)")
-    lib = ctypes.CDLL(str(LIB_PATH))
+    lib = ctypes.CDLL(str(path))
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     gemm_args = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
     for name in ("gemm_f32", "gemm_f32_ref_gpu"):

@@ -3,6 +3,10 @@
 Each source under ``csrc/`` is compiled to an object in ``_build/`` (in
 parallel), then linked into ``dense_fp32_gemm_f32_amd/libgemm_f32.so``.
 Run as ``python -m dense_fp32_gemm_f32_amd.build_lib``.
+
+``--sweep`` builds ``libgemm_f32_sweep.so`` instead: the same sources with
+``-DGEMM_F32_SWEEP=1``, whose kernel table also holds the variants that
+tuning sweeps (``tune.py --sweep``) compare the tuned kernels with.
 """
 from __future__ import annotations
 
@@ -17,6 +21,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 BUILD = ROOT / "_build"
 LIB = PKG / "libgemm_f32.so"
+SWEEP_LIB = PKG / "libgemm_f32_sweep.so"
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,8 +36,8 @@ def sources():
     return sorted([*CSRC.glob("*.hip"), *CSRC.glob("*.cpp")])
 
 
-def _compile(src: Path, extra: list[str]) -> Path:
-    obj = BUILD / (src.name + ".o")
+def _compile(src: Path, extra: list[str], build_dir: Path) -> Path:
+    obj = build_dir / (src.name + ".o")
     lang = ["-x", "hip"] if src.suffix == ".hip" else []
     cmd = [HIPCC, *COMMON, *extra, *lang, "-c", str(src), "-o", str(obj)]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,22 +52,31 @@ def _compile(src: Path, extra: list[str]) -> Path:
     return obj
 
 
-def build(extra: list[str] | None = None, jobs: int | None = None) -> Path:
-    """Compile every source and link the shared library.  Always rebuilds."""
+def build(extra: list[str] | None = None, jobs: int | None = None, sweep: bool = False) -> Path:
+    """Compile every source and link the shared library (the sweep library when
+    ``sweep``).  Always rebuilds."""
     extra = list(extra or [])
-    BUILD.mkdir(exist_ok=True)
+    lib = LIB
+    build_dir = BUILD
+    if sweep:
+        extra.append("-DGEMM_F32_SWEEP=1")
+        lib = SWEEP_LIB
+        build_dir = BUILD / "sweep"
+    build_dir.mkdir(parents=True, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
-    tmp = LIB.with_suffix(".so.tmp")
+        objs = list(ex.map(lambda s: _compile(s, extra, build_dir), srcs))
+    tmp = lib.with_suffix(".so.tmp")
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(sys.argv[1:]))
+    args = sys.argv[1:]
+    sweep = "--sweep" in args
+    print(build([a for a in args if a != "--sweep"], sweep=sweep))

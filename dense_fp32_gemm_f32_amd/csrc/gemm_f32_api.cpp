@@ -26,8 +26,8 @@ using gemmf32::Problem;
 
 namespace {
 
-// ---- kernel table: MFMA variants (whole K, then K split), skinny variants,
-// the naive kernel ----------------------------------------------------------
+// ---- kernel table: MFMA variants (whole K; with GEMM_F32_SWEEP also K
+// split), extended-operation and skinny variants, the naive kernel ----------
 enum class Kind { Mfma, MfmaSplitK, MfmaEx, Skinny, Ref };
 struct Entry {
   Kind kind;
@@ -46,8 +46,11 @@ const std::vector<Entry>& entries() {
     std::vector<Entry> t;
     for (int i = 0; i < gemmf32::mfma_variant_count(); ++i)
       t.push_back({Kind::Mfma, i, gemmf32::mfma_variant(i).name});
+#if GEMM_F32_SWEEP
+    // K-split twins: the tuning table picks none of them
     for (int i = 0; i < gemmf32::mfma_variant_count(); ++i)
       t.push_back({Kind::MfmaSplitK, i, split_k_name(gemmf32::mfma_variant(i).name)});
+#endif
     for (int i = 0; i < gemmf32::mfma_ex_variant_count(); ++i)
       t.push_back({Kind::MfmaEx, i, gemmf32::mfma_ex_variant(i).name});
     for (int i = 0; i < gemmf32::skinny_variant_count(); ++i)

@@ -6,6 +6,15 @@
 #include <cstddef>
 #include <cstdint>
 
+// The kernel table of the default build holds the kernels the tuning tables
+// can pick (and the reference kernel).  Building with -DGEMM_F32_SWEEP=1 adds
+// the variants tuning sweeps compare them with: other tiles, schedules and load
+// widths, the _nn twins of the transposed-layout kernels, and a K-split
+// ("_sk_") twin of every MFMA tile kernel.
+#ifndef GEMM_F32_SWEEP
+#define GEMM_F32_SWEEP 0
+#endif
+
 namespace gemmf32 {
 
 // One GEMM call after validation: C[i*ldc+j] = sum_k A[i*lda+k] * B[k*ldb+j]

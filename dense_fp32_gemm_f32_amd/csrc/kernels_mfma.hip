@@ -502,9 +502,15 @@ hipError_t launch(const Problem& p, int slices, int kchunk, float* partials, con
   return launch_combine(p, slices, partials, s, e);
 }
 
-#define GEMMF32_MFMA_S(BM, BN, BK, WM, WN, MW, SC, TAG)                                      \
+// Name: mfma_<BM>x<BN>x<BK>_w<WM>x<WN><schedule>_<load widths>.  The default
+// build holds the tiles the tuning table can pick, with 128-bit loads of A and
+// B (which take any 4-byte aligned operands); a build with GEMM_F32_SWEEP
+// also holds the variants that tuning sweeps compare them with.
+#define GEMMF32_MFMA_VEC(BM, BN, BK, WM, WN, MW, SC, TAG)                                     \
   {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_vec", BM, BN, BK, WM, WN, true, true,    \
-   false, &launch<BM, BN, BK, WM, WN, true, true, MW, SC>},                                    \
+   false, &launch<BM, BN, BK, WM, WN, true, true, MW, SC>}
+#define GEMMF32_MFMA_S(BM, BN, BK, WM, WN, MW, SC, TAG)                                      \
+  GEMMF32_MFMA_VEC(BM, BN, BK, WM, WN, MW, SC, TAG),                                          \
   {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_veca", BM, BN, BK, WM, WN, true, false,  \
    false, &launch<BM, BN, BK, WM, WN, true, false, MW, SC>},                                   \
   {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN TAG "_vecb", BM, BN, BK, WM, WN, false, true,  \
@@ -514,6 +520,38 @@ hipError_t launch(const Problem& p, int slices, int kchunk, float* partials, con
 #define GEMMF32_MFMA(BM, BN, BK, WM, WN, MW) GEMMF32_MFMA_S(BM, BN, BK, WM, WN, MW, 0, "")
 
 const MfmaVariant kVariants[] = {
+    // operands the direct-to-LDS loads cannot take (any pitch, 4-byte aligned)
+    GEMMF32_MFMA_VEC(128, 128, 32, 64, 64, 2, 5, "_p5"),
+    GEMMF32_MFMA_VEC(128, 192, 32, 32, 96, 2, 5, "_p5"),
+    GEMMF32_MFMA_VEC(192, 128, 32, 96, 32, 2, 5, "_p5"),
+    GEMMF32_MFMA_VEC(64, 64, 32, 32, 32, 4, 5, "_p5"),
+#if GEMM_F32_SWEEP
+    // the other load widths of the tiles above
+    {"mfma_128x128x32_w64x64_p5_veca", 128, 128, 32, 64, 64, true, false, false,
+     &launch<128, 128, 32, 64, 64, true, false, 2, 5>},
+    {"mfma_128x128x32_w64x64_p5_vecb", 128, 128, 32, 64, 64, false, true, false,
+     &launch<128, 128, 32, 64, 64, false, true, 2, 5>},
+    {"mfma_128x128x32_w64x64_p5_scalar", 128, 128, 32, 64, 64, false, false, false,
+     &launch<128, 128, 32, 64, 64, false, false, 2, 5>},
+    {"mfma_64x64x32_w32x32_p5_veca", 64, 64, 32, 32, 32, true, false, false,
+     &launch<64, 64, 32, 32, 32, true, false, 4, 5>},
+    {"mfma_64x64x32_w32x32_p5_vecb", 64, 64, 32, 32, 32, false, true, false,
+     &launch<64, 64, 32, 32, 32, false, true, 4, 5>},
+    {"mfma_64x64x32_w32x32_p5_scalar", 64, 64, 32, 32, 32, false, false, false,
+     &launch<64, 64, 32, 32, 32, false, false, 4, 5>},
+    {"mfma_128x192x32_w32x96_p5_veca", 128, 192, 32, 32, 96, true, false, false,
+     &launch<128, 192, 32, 32, 96, true, false, 2, 5>},
+    {"mfma_128x192x32_w32x96_p5_vecb", 128, 192, 32, 32, 96, false, true, false,
+     &launch<128, 192, 32, 32, 96, false, true, 2, 5>},
+    {"mfma_128x192x32_w32x96_p5_scalar", 128, 192, 32, 32, 96, false, false, false,
+     &launch<128, 192, 32, 32, 96, false, false, 2, 5>},
+    {"mfma_192x128x32_w96x32_p5_veca", 192, 128, 32, 96, 32, true, false, false,
+     &launch<192, 128, 32, 96, 32, true, false, 2, 5>},
+    {"mfma_192x128x32_w96x32_p5_vecb", 192, 128, 32, 96, 32, false, true, false,
+     &launch<192, 128, 32, 96, 32, false, true, 2, 5>},
+    {"mfma_192x128x32_w96x32_p5_scalar", 192, 128, 32, 96, 32, false, false, false,
+     &launch<192, 128, 32, 96, 32, false, false, 2, 5>},
+    // tiles and schedules measured against them
     GEMMF32_MFMA(256, 256, 16, 128, 128, 1),
     GEMMF32_MFMA(256, 256, 32, 128, 128, 1),
     GEMMF32_MFMA(256, 128, 16, 128, 64, 2),
@@ -542,20 +580,17 @@ const MfmaVariant kVariants[] = {
     GEMMF32_MFMA_S(128, 64, 64, 64, 32, 1, 3, "_p3"),
     GEMMF32_MFMA_S(64, 64, 64, 32, 32, 2, 3, "_p3"),
     GEMMF32_MFMA_S(128, 128, 64, 64, 64, 1, 5, "_p5"),
-    GEMMF32_MFMA_S(128, 128, 32, 64, 64, 2, 5, "_p5"),
     GEMMF32_MFMA_S(128, 128, 16, 64, 64, 3, 5, "_p5"),
     GEMMF32_MFMA_S(256, 128, 16, 128, 64, 2, 5, "_p5"),
     GEMMF32_MFMA_S(256, 128, 32, 128, 64, 1, 5, "_p5"),
     GEMMF32_MFMA_S(128, 64, 32, 64, 32, 4, 5, "_p5"),
     GEMMF32_MFMA_S(128, 64, 64, 64, 32, 1, 5, "_p5"),
     GEMMF32_MFMA_S(64, 64, 64, 32, 32, 2, 5, "_p5"),
-    GEMMF32_MFMA_S(64, 64, 32, 32, 32, 4, 5, "_p5"),
     GEMMF32_MFMA_S(128, 192, 16, 64, 96, 1, 5, "_p5"),
     GEMMF32_MFMA_S(128, 192, 32, 64, 96, 1, 5, "_p5"),
-    GEMMF32_MFMA_S(128, 192, 32, 32, 96, 2, 5, "_p5"),
     GEMMF32_MFMA_S(256, 192, 16, 128, 96, 1, 5, "_p5"),
-    GEMMF32_MFMA_S(192, 128, 32, 96, 32, 2, 5, "_p5"),
     GEMMF32_MFMA_S(128, 192, 32, 32, 96, 2, 3, "_p3"),
+#endif
 };
 
 }  // namespace

@@ -294,24 +294,28 @@ hipError_t launch_dma(const Problem& p, int slices, int kchunk, float* partials,
   {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_d6_vec", BM, BN, BK, WM, WN, true, true, \
    true, &launch_dma<BM, BN, BK, WM, WN, MW>}
 
+// The default build holds the tiles the tuning table can pick; a build with
+// GEMM_F32_SWEEP also holds the ones tuning sweeps compared them with.
 const MfmaVariant kDmaVariants[] = {
+    GEMMF32_MFMA_DMA(256, 256, 32, 64, 128, 1),
+    GEMMF32_MFMA_DMA(128, 256, 16, 64, 128, 2),
+    GEMMF32_MFMA_DMA(128, 192, 32, 32, 96, 2),
+    GEMMF32_MFMA_DMA(192, 128, 32, 96, 32, 2),
+    GEMMF32_MFMA_DMA(128, 128, 32, 64, 32, 2),
+    GEMMF32_MFMA_DMA(128, 128, 16, 64, 64, 3),
+    GEMMF32_MFMA_DMA(64, 64, 32, 32, 32, 4),
+#if GEMM_F32_SWEEP
     GEMMF32_MFMA_DMA(256, 128, 16, 128, 64, 2),
     GEMMF32_MFMA_DMA(256, 128, 32, 128, 64, 1),
-    GEMMF32_MFMA_DMA(128, 256, 16, 64, 128, 2),
-    GEMMF32_MFMA_DMA(128, 128, 16, 64, 64, 3),
     GEMMF32_MFMA_DMA(128, 128, 32, 64, 64, 2),
     GEMMF32_MFMA_DMA(128, 128, 64, 64, 64, 1),
     GEMMF32_MFMA_DMA(128, 64, 32, 64, 32, 3),
     GEMMF32_MFMA_DMA(128, 64, 64, 64, 32, 2),
-    GEMMF32_MFMA_DMA(64, 64, 32, 32, 32, 4),
     GEMMF32_MFMA_DMA(64, 64, 64, 32, 32, 2),
     GEMMF32_MFMA_DMA(256, 256, 16, 128, 64, 1),
     GEMMF32_MFMA_DMA(256, 256, 16, 64, 128, 1),
     GEMMF32_MFMA_DMA(256, 256, 32, 128, 64, 1),
-    GEMMF32_MFMA_DMA(256, 256, 32, 64, 128, 1),
-    GEMMF32_MFMA_DMA(128, 192, 32, 32, 96, 2),
-    GEMMF32_MFMA_DMA(192, 128, 32, 96, 32, 2),
-    GEMMF32_MFMA_DMA(128, 128, 32, 64, 32, 2),
+#endif
 };
 
 }  // namespace

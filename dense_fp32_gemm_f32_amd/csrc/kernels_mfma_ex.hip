@@ -371,21 +371,31 @@ hipError_t launch_ex(const Problem& p, const Epilogue& e, hipStream_t s) {
 
 // Name: mfmaex_<tile>_<layout>, layout = op(A) op(B) as n (stored as is) or t
 // (stored transposed).  A is KC when not transposed; B is KC when transposed.
-#define GEMMF32_MFMA_EX(BM, BN, BK, WM, WN, MW)                                          \
-  {"mfmaex_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_nn", BM, BN, BK, false, false,      \
-   &launch_ex<BM, BN, BK, WM, WN, true, false, MW>},                                     \
+// The default build holds the tiles the tuning table can pick, in the three
+// layouts with a transposed operand (A and B as stored run the plain
+// kernels); a build with GEMM_F32_SWEEP adds the _nn twins and the other tiles.
+#define GEMMF32_MFMA_EX_T(BM, BN, BK, WM, WN, MW)                                        \
   {"mfmaex_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_nt", BM, BN, BK, false, true,       \
    &launch_ex<BM, BN, BK, WM, WN, true, true, MW>},                                      \
   {"mfmaex_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_tn", BM, BN, BK, true, false,       \
    &launch_ex<BM, BN, BK, WM, WN, false, false, MW>},                                    \
   {"mfmaex_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_tt", BM, BN, BK, true, true,        \
    &launch_ex<BM, BN, BK, WM, WN, false, true, MW>}
+#define GEMMF32_MFMA_EX_NN(BM, BN, BK, WM, WN, MW)                                       \
+  {"mfmaex_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_nn", BM, BN, BK, false, false,      \
+   &launch_ex<BM, BN, BK, WM, WN, true, false, MW>}
 
 const MfmaExVariant kExVariants[] = {
-    GEMMF32_MFMA_EX(256, 128, 16, 128, 64, 1),
-    GEMMF32_MFMA_EX(128, 128, 16, 64, 64, 2),
-    GEMMF32_MFMA_EX(128, 64, 32, 64, 32, 2),
-    GEMMF32_MFMA_EX(64, 64, 32, 32, 32, 2),
+    GEMMF32_MFMA_EX_T(128, 128, 16, 64, 64, 2),
+    GEMMF32_MFMA_EX_T(128, 64, 32, 64, 32, 2),
+    GEMMF32_MFMA_EX_T(64, 64, 32, 32, 32, 2),
+#if GEMM_F32_SWEEP
+    GEMMF32_MFMA_EX_NN(128, 128, 16, 64, 64, 2),
+    GEMMF32_MFMA_EX_NN(128, 64, 32, 64, 32, 2),
+    GEMMF32_MFMA_EX_NN(64, 64, 32, 32, 32, 2),
+    GEMMF32_MFMA_EX_NN(256, 128, 16, 128, 64, 1),
+    GEMMF32_MFMA_EX_T(256, 128, 16, 128, 64, 1),
+#endif
 };
 
 }  // namespace

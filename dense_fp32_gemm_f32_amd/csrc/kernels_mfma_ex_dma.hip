@@ -292,20 +292,28 @@ hipError_t launch_ex_dma(const Problem& p, const Epilogue& e, hipStream_t s) {
 // Name: mfmaex_<tile>_d6_<layout>, layout = op(A) op(B) as n (stored as is)
 // or t (stored transposed).  A is KC when not transposed; B is KC when
 // transposed.
-#define GEMMF32_MFMA_EX_DMA(BM, BN, BK, WM, WN, MW)                                       \
-  {"mfmaex_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_d6_nn", BM, BN, BK, false, false,      \
-   &launch_ex_dma<BM, BN, BK, WM, WN, true, false, MW>, true},                             \
+// The default build holds the three layouts with a transposed operand; a
+// build with GEMM_F32_SWEEP adds the _nn twins.
+#define GEMMF32_MFMA_EX_DMA_T(BM, BN, BK, WM, WN, MW)                                     \
   {"mfmaex_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_d6_nt", BM, BN, BK, false, true,       \
    &launch_ex_dma<BM, BN, BK, WM, WN, true, true, MW>, true},                              \
   {"mfmaex_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_d6_tn", BM, BN, BK, true, false,       \
    &launch_ex_dma<BM, BN, BK, WM, WN, false, false, MW>, true},                            \
   {"mfmaex_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_d6_tt", BM, BN, BK, true, true,        \
    &launch_ex_dma<BM, BN, BK, WM, WN, false, true, MW>, true}
+#define GEMMF32_MFMA_EX_DMA_NN(BM, BN, BK, WM, WN, MW)                                    \
+  {"mfmaex_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_d6_nn", BM, BN, BK, false, false,      \
+   &launch_ex_dma<BM, BN, BK, WM, WN, true, false, MW>, true}
 
 const MfmaExVariant kExDmaVariants[] = {
-    GEMMF32_MFMA_EX_DMA(256, 256, 32, 64, 128, 1),
-    GEMMF32_MFMA_EX_DMA(128, 128, 32, 64, 32, 2),
-    GEMMF32_MFMA_EX_DMA(64, 64, 32, 32, 32, 4),
+    GEMMF32_MFMA_EX_DMA_T(256, 256, 32, 64, 128, 1),
+    GEMMF32_MFMA_EX_DMA_T(128, 128, 32, 64, 32, 2),
+    GEMMF32_MFMA_EX_DMA_T(64, 64, 32, 32, 32, 4),
+#if GEMM_F32_SWEEP
+    GEMMF32_MFMA_EX_DMA_NN(256, 256, 32, 64, 128, 1),
+    GEMMF32_MFMA_EX_DMA_NN(128, 128, 32, 64, 32, 2),
+    GEMMF32_MFMA_EX_DMA_NN(64, 64, 32, 32, 32, 4),
+#endif
 };
 
 }  // namespace

@@ -245,14 +245,16 @@ hipError_t launch_small(const Problem& p, int slices, int kchunk, float* partial
    &launch_small<TM, TN, KS, D>}
 
 const MfmaVariant kSmallVariants[] = {
+    GEMMF32_MFMA_SMALL(32, 32, 4, 4),
+#if GEMM_F32_SWEEP
     GEMMF32_MFMA_SMALL(32, 32, 4, 8),
     GEMMF32_MFMA_SMALL(32, 32, 8, 8),
-    GEMMF32_MFMA_SMALL(32, 32, 4, 4),
     GEMMF32_MFMA_SMALL(32, 64, 4, 8),
     GEMMF32_MFMA_SMALL(64, 32, 4, 8),
     GEMMF32_MFMA_SMALL(64, 64, 4, 4),
     GEMMF32_MFMA_SMALL(64, 64, 2, 4),
     GEMMF32_MFMA_SMALL(64, 64, 4, 2),
+#endif
 };
 
 }  // namespace

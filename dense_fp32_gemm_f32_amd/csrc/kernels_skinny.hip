@@ -333,12 +333,16 @@ hipError_t launch_tile(const Problem& p, const SkinnyPlan& pl, float* partials,
   {"skinny_w" #NW "_c" #CG "_u" #U "_s" #S "_tn", 16, NW, U, false, true, S, true, false,   \
    &plan_tile<CG>, &launch_tile<NW, CG, U, false, true, true>}
 
-// K slices added in-kernel through exchange slots (prefix skinnyx_)
-#define GEMMF32_SKINNY_TILE_X(NW, CG, U, S)                                                  \
+// K slices added in-kernel through exchange slots (prefix skinnyx_); _vec
+// takes any 4-byte aligned operands, _scalar is its 32-bit-load twin
+#define GEMMF32_SKINNY_TILE_X1(NW, CG, U, S)                                                 \
   {"skinnyx_w" #NW "_c" #CG "_u" #U "_s" #S "_vec", 16, NW, U, true, true, S, false, false,  \
-   &plan_tile<CG, true>, &launch_tile<NW, CG, U, true, true, false, true>},                  \
+   &plan_tile<CG, true>, &launch_tile<NW, CG, U, true, true, false, true>}
+#define GEMMF32_SKINNY_TILE_XS(NW, CG, U, S)                                                 \
   {"skinnyx_w" #NW "_c" #CG "_u" #U "_s" #S "_scalar", 16, NW, U, false, false, S, false,     \
    false, &plan_tile<CG, true>, &launch_tile<NW, CG, U, false, false, false, true>}
+#define GEMMF32_SKINNY_TILE_X(NW, CG, U, S) \
+  GEMMF32_SKINNY_TILE_X1(NW, CG, U, S), GEMMF32_SKINNY_TILE_XS(NW, CG, U, S)
 
 #define GEMMF32_SKINNY_TILE_X_TA(NW, CG, U, S)                                               \
   {"skinnyx_w" #NW "_c" #CG "_u" #U "_s" #S "_tn", 16, NW, U, false, true, S, true, false,    \
@@ -347,7 +351,17 @@ hipError_t launch_tile(const Problem& p, const SkinnyPlan& pl, float* partials,
 // Name: skinny_w<waves>_c<column groups of 32>_u<super-blocks in flight>_s<K
 // slices, 0 = from the shape>_<load widths>, or _tn for A stored transposed;
 // skinnyx_ for the in-kernel sum of the slices.
+// The default build holds the kernels the tuning tables can pick; a build
+// with GEMM_F32_SWEEP also holds the ones tuning sweeps compared them with.
 const SkinnyVariant kVariants[] = {
+    // 64-column strips, two super-blocks in flight per wave (32 KiB of B per
+    // workgroup): 8 x 8192 x 8192 in 45 us against 48 us with the combine
+    GEMMF32_SKINNY_TILE_X1(8, 2, 2, 0),
+    GEMMF32_SKINNY_TILE_X_TA(8, 2, 2, 0),
+    GEMMF32_SKINNY_TILE_X1(16, 2, 2, 0),
+#if GEMM_F32_SWEEP
+    GEMMF32_SKINNY_TILE_XS(8, 2, 2, 0),
+    GEMMF32_SKINNY_TILE_XS(16, 2, 2, 0),
     GEMMF32_SKINNY_TILE(16, 1, 4, 1),    // 32 columns, all of K: no partial sums
     GEMMF32_SKINNY_TILE(8, 1, 4, 1),
     GEMMF32_SKINNY_TILE(16, 4, 4, 0),    // 128 columns, K split to fill the GPU
@@ -364,16 +378,12 @@ const SkinnyVariant kVariants[] = {
     GEMMF32_SKINNY_TILE(8, 4, 4, 8),     // 8 K slices: two workgroups per CU
     GEMMF32_SKINNY_TILE(8, 4, 8, 8),
     GEMMF32_SKINNY_TILE_TA(8, 4, 4, 0),
-    // 64-column strips, two super-blocks in flight per wave (32 KiB of B per
-    // workgroup): 8 x 8192 x 8192 in 45 us against 48 us with the combine
-    GEMMF32_SKINNY_TILE_X(8, 2, 2, 0),
-    GEMMF32_SKINNY_TILE_X_TA(8, 2, 2, 0),
     GEMMF32_SKINNY_TILE_X(8, 2, 1, 0),
     GEMMF32_SKINNY_TILE_X(8, 2, 3, 0),
     GEMMF32_SKINNY_TILE_X(8, 2, 4, 0),
-    GEMMF32_SKINNY_TILE_X(16, 2, 2, 0),
     GEMMF32_SKINNY_TILE_X(8, 4, 2, 0),
     GEMMF32_SKINNY_TILE_X(8, 4, 4, 0),
+#endif
 };
 
 }  // namespace

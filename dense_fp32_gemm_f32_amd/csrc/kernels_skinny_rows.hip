@@ -305,17 +305,24 @@ hipError_t launch_rows(const Problem& p, const SkinnyPlan& pl, float* partials,
 
 // Name: skinnyr_c<column groups of 64 VW>_r<row groups>_u<quads in flight>_m<rows
 // of A>[_v<VW>]_s<K slices, 0 = from the shape>_<nn|tn>; without _v, VW = 4.
-#define GEMMF32_SKINNY_ROWS_V(CG, RG, U, MQ, VW, ST, S, VS)                                  \
+#define GEMMF32_SKINNY_ROWS_NN(CG, RG, U, MQ, VW, ST, S, VS)                                 \
   {"skinnyr_c" #CG "_r" #RG "_u" #U "_m" #MQ "x4" VS "_s" #S "_nn", 4 * MQ, CG * RG, U,       \
    false, true, S, false, false, &plan_rows<CG, RG, MQ, VW, ST>,                              \
-   &launch_rows<CG, RG, U, MQ, VW, ST, false>, true},                                         \
+   &launch_rows<CG, RG, U, MQ, VW, ST, false>, true}
+#define GEMMF32_SKINNY_ROWS_TN(CG, RG, U, MQ, VW, ST, S, VS)                                 \
   {"skinnyr_c" #CG "_r" #RG "_u" #U "_m" #MQ "x4" VS "_s" #S "_tn", 4 * MQ, CG * RG, U,       \
    false, true, S, true, false, &plan_rows<CG, RG, MQ, VW, ST>,                               \
    &launch_rows<CG, RG, U, MQ, VW, ST, true>, true}
+#define GEMMF32_SKINNY_ROWS_V(CG, RG, U, MQ, VW, ST, S, VS) \
+  GEMMF32_SKINNY_ROWS_NN(CG, RG, U, MQ, VW, ST, S, VS), GEMMF32_SKINNY_ROWS_TN(CG, RG, U, MQ, VW, ST, S, VS)
 #define GEMMF32_SKINNY_ROWS(CG, RG, U, MQ, S) GEMMF32_SKINNY_ROWS_V(CG, RG, U, MQ, 4, 8, S, "")
 
+// The default build holds the kernel the tuning table picks (A as stored); a
+// build with GEMM_F32_SWEEP also holds the ones tuning sweeps compared it with.
 const SkinnyVariant kRowsVariants[] = {
-    GEMMF32_SKINNY_ROWS(2, 4, 4, 2, 0),
+    GEMMF32_SKINNY_ROWS_NN(2, 4, 4, 2, 4, 8, 0, ""),
+#if GEMM_F32_SWEEP
+    GEMMF32_SKINNY_ROWS_TN(2, 4, 4, 2, 4, 8, 0, ""),
     GEMMF32_SKINNY_ROWS(2, 4, 2, 2, 0),
     GEMMF32_SKINNY_ROWS(4, 2, 2, 2, 0),
     GEMMF32_SKINNY_ROWS(4, 1, 4, 2, 0),
@@ -331,6 +338,7 @@ const SkinnyVariant kRowsVariants[] = {
     // 256-byte runs
     GEMMF32_SKINNY_ROWS_V(1, 8, 2, 2, 1, 32, 0, "_v1"),
     GEMMF32_SKINNY_ROWS_V(1, 8, 4, 2, 1, 32, 0, "_v1"),
+#endif
 };
 
 }  // namespace

@@ -208,12 +208,14 @@ hipError_t launch_t(const Problem& p, const SkinnyPlan& pl, float* partials,
 
 const SkinnyVariant kTVariants[] = {
     GEMMF32_SKINNY_T(8, 4, 2),
+    GEMMF32_SKINNY_T(16, 4, 2),
+#if GEMM_F32_SWEEP
     GEMMF32_SKINNY_T(8, 8, 2),
     GEMMF32_SKINNY_T(8, 4, 4),
-    GEMMF32_SKINNY_T(16, 4, 2),
     GEMMF32_SKINNY_T(8, 8, 1),
     GEMMF32_SKINNY_T(8, 4, 3),
     GEMMF32_SKINNY_T(8, 2, 4),
+#endif
 };
 
 }  // namespace

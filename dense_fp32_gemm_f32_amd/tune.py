@@ -11,6 +11,10 @@ taking turns (after --spin-ms of load to settle the clocks); the median is
 reported.  Inputs rotate over enough copies to exceed the 256 MB last-level
 cache when B is large or the shape is skinny (M <= 16), so bandwidth-bound
 shapes stream from HBM.  Prints one line per (shape, kernel).
+
+``--sweep`` loads the sweep build of the library (``python -m
+dense_fp32_gemm_f32_amd.build_lib --sweep``), whose table also holds the
+variants that are not in the default build.
 """
 from __future__ import annotations
 
@@ -41,12 +45,14 @@ def main(argv=None):
                          "(gemm_f32_ex kernels); the plain kernels run only for nn")
     ap.add_argument("--alpha", type=float, default=1.0)
     ap.add_argument("--beta", type=float, default=0.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the kernels of the sweep build (libgemm_f32_sweep.so)")
     args = ap.parse_args(argv)
 
     import torch
-    from dense_fp32_gemm_f32_amd import binding, inputs
+    from dense_fp32_gemm_f32_amd import binding, build_lib, inputs
 
-    binding.load()
+    binding.load(build_lib.SWEEP_LIB if args.sweep else None)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     names = binding.kernel_names()

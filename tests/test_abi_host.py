@@ -48,7 +48,7 @@ def test_kernel_table():
     names = binding.kernel_names()
     assert len(names) == len(set(names)) == binding.gemm_f32_kernel_count()
     assert any(n.startswith("mfma_") for n in names)
-    assert any(n.startswith("skinny_") for n in names)
+    assert any(n.startswith("skinny") for n in names)
     assert "ref_naive" in names
     assert binding.gemm_f32_kernel_name(-1) is None
     assert binding.gemm_f32_kernel_name(len(names)) is None
@@ -190,13 +190,31 @@ def test_dispatcher_rejects_bad_arguments():
     assert sel(4, 4, 4, 3, 4, 4, P16, Q16, R16) == "invalid"
 
 
-def test_every_mfma_variant_has_a_split_k_twin():
-    names = binding.kernel_names()
-    whole = [n for n in names if n.startswith("mfma_") and "_sk_" not in n]
-    assert whole
-    for n in whole:
-        base, width = n.rsplit("_", 1)
-        assert f"{base}_sk_{width}" in names, n
+def _tuning_table_names():
+    """Every kernel name the gfx950 tuning tables can select, read from the
+    header: the plain and skinny rows as written, the extended-operation rows
+    with each transposed layout's suffix."""
+    import re
+    text = (ROOT / "dense_fp32_gemm_f32_amd" / "csrc" / "tuning_gfx950.h").read_text()
+
+    def rows(table):
+        body = text[text.index(table):]
+        body = body[:body.index("};")]
+        return re.findall(r'^\s*\{[^"]*"([a-z0-9_]+)"', body, re.M)
+    names = set(rows("kTuningGfx950[] = {")) | set(rows("kTuningGfx950Skinny[] = {"))
+    for prefix in rows("kTuningGfx950Ex[] = {"):
+        names |= {prefix + lay for lay in ("_nt", "_tn", "_tt")}
+    return names
+
+
+def test_default_table_is_what_the_tuning_tables_select():
+    """The default build holds every kernel a tuning row names, the reference
+    kernel, and nothing else (sweep-only variants need GEMM_F32_SWEEP)."""
+    names = set(binding.kernel_names())
+    wanted = _tuning_table_names()
+    assert len(wanted) > 20
+    assert wanted <= names, sorted(wanted - names)
+    assert names - wanted == {"ref_naive"}, sorted(names - wanted)
 
 
 # ---- the extended operation (gemm_f32_ex) -------------------------------------
