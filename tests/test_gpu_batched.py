@@ -172,7 +172,7 @@ def test_graph_capture_replays_match_eager(gpu_lib):
     def calls():
         for k, (A, B, C) in static.items():
             if k == "skinny_combine":
-                gpu_lib.run_kernel("skinny_w8_c4_u4_s0_vec", A, B, C)
+                gpu_lib.run_kernel("skinnyr_c2_r4_u4_m2x4_s0_nn", A, B, C)
             else:
                 gpu_lib.gemm(A, B, C)
         gpu_lib.gemm_batched(bA, bB, bC)
@@ -237,11 +237,11 @@ def test_graph_replay_after_workspace_growth(gpu_lib):
     assert binding.gemm_f32_release_workspaces() == 0
     s = torch.cuda.Stream()
     # small: 2 K slices each (0.5 MiB of exchange slots, 0.25 MiB of partials);
-    # big: 4 and 8 slices (1.5 MiB of slots, 2 MiB of partials), both beyond
+    # big: 4 and 32 slices (1.5 MiB of slots, 4 MiB of partials), both beyond
     # the 1 MiB first allocations
-    kx, kc = "skinnyx_w8_c2_u2_s0_vec", "skinny_w8_c4_u4_s0_vec"
-    small = {kx: (8, 4096, 32), kc: (16, 4096, 32)}
-    big = {kx: (8, 4096, 4096), kc: (16, 4096, 4096)}
+    kx, kc = "skinnyx_w8_c2_u2_s0_vec", "skinnyr_c2_r4_u4_m2x4_s0_nn"
+    small = {kx: (8, 4096, 32), kc: (8, 4096, 128)}
+    big = {kx: (8, 4096, 4096), kc: (8, 4096, 4096)}
     st = {k: (torch.empty((m, kk), device="cuda"), torch.empty((kk, n), device="cuda"),
               torch.empty((m, n), device="cuda")) for k, (m, n, kk) in small.items()}
 

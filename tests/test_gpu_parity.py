@@ -274,13 +274,13 @@ def test_errors_from_the_device_side(gpu_lib):
     # unknown kernel index, and a skinny kernel with too many rows
     assert b.gemm_f32_run_kernel(10 ** 6, 64, 64, 64, A.data_ptr(), 64, B.data_ptr(), 64,
                                  C.data_ptr(), 64, s) == 8
-    sk = [i for i, n in enumerate(b.kernel_names()) if n.startswith("skinny_")][0]
+    sk = [i for i, n in enumerate(b.kernel_names()) if n.startswith("skinny")][0]
     assert b.gemm_f32_run_kernel(sk, 64, 64, 64, A.data_ptr(), 64, B.data_ptr(), 64,
                                  C.data_ptr(), 64, s) == 8
     torch.cuda.synchronize()
 
 
-SPLITK = "skinny_w8_c4_u4_s0_vec"   # a kernel that combines K slices in a workspace
+SPLITK = "skinnyr_c2_r4_u4_m2x4_s0_nn"   # a kernel that combines K slices in a workspace
 SPLITX = "skinnyx_w8_c2_u2_s0_vec"  # a kernel that adds K slices through exchange slots
 
 
