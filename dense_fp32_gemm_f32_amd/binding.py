@@ -25,7 +25,7 @@ STATUS_NAMES = {
     0: "GEMM_F32_OK", 1: "GEMM_F32_ERR_INVALID_DIM", 2: "GEMM_F32_ERR_INVALID_LD",
     3: "GEMM_F32_ERR_NULL_PTR", 4: "GEMM_F32_ERR_ALIAS", 5: "GEMM_F32_ERR_DEVICE",
     6: "GEMM_F32_ERR_WORKSPACE", 7: "GEMM_F32_ERR_LAUNCH", 8: "GEMM_F32_ERR_BAD_KERNEL",
-    9: "GEMM_F32_ERR_POINTER", 10: "GEMM_F32_ERR_INVALID_ARG",
+    9: "GEMM_F32_ERR_POINTER", 10: "GEMM_F32_ERR_INVALID_ARG", 11: "GEMM_F32_ERR_SCRATCH",
 }
 ACT_NONE, ACT_RELU = 0, 1
 EXPORTS = ["gemm_f32", "gemm_f32_ex", "gemm_f32_ref_gpu", "gemm_f32_status_string",
@@ -33,7 +33,7 @@ EXPORTS = ["gemm_f32", "gemm_f32_ex", "gemm_f32_ref_gpu", "gemm_f32_status_strin
            "gemm_f32_kernel_count", "gemm_f32_kernel_name", "gemm_f32_run_kernel",
            "gemm_f32_run_kernel_ex", "gemm_f32_release_workspaces", "gemm_f32_batched",
            "gemm_f32_selected_kernel_batched", "reduce_sum_f32", "gemm_f32_fused",
-           "gemm_f32_run_kernel_fused"]
+           "gemm_f32_run_kernel_fused", "gemm_f32_noalloc"]
 
 
 class GemmError(RuntimeError):
@@ -62,7 +62,7 @@ def load(lib_path=None):
     lib = ctypes.CDLL(str(path))
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     gemm_args = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
-    for name in ("gemm_f32", "gemm_f32_ref_gpu"):
+    for name in ("gemm_f32", "gemm_f32_ref_gpu", "gemm_f32_noalloc"):
         getattr(lib, name).argtypes = gemm_args
         getattr(lib, name).restype = ctypes.c_int
     lib.gemm_f32_run_kernel.argtypes = [ctypes.c_int, *gemm_args]
@@ -109,6 +109,10 @@ def load(lib_path=None):
 
 def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
     return load().gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    return load().gemm_f32_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
 def gemm_f32_ex(transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
@@ -237,6 +241,17 @@ def gemm(A, B, C=None):
         rc = gemm_f32(*args)
     if rc != GEMM_F32_OK:
         raise GemmError(rc, "gemm_f32")
+    return C
+
+
+def gemm_noalloc(A, B, C=None):
+    """C = A @ B through gemm_f32_noalloc (the fixed scratch array, no
+    allocation inside the library); returns C."""
+    args, C = _args(A, B, C)
+    with _device(A):
+        rc = gemm_f32_noalloc(*args)
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc, "gemm_f32_noalloc")
     return C
 
 

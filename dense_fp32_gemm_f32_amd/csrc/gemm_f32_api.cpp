@@ -326,7 +326,9 @@ bool entry_accepts(const Entry& e, const Op& op, const Problem& p) {
   return accepts(e, op, p.M, p.N, p.K, p.lda, p.ldb, p.A, p.B);
 }
 
-int run_entry(const Entry& e, const Op& op, const Problem& p, int dev, hipStream_t s) {
+// fixed: the scratch of gemm_f32_noalloc (NULL: this stream's workspaces)
+int run_entry(const Entry& e, const Op& op, const Problem& p, int dev, hipStream_t s,
+              const gemmf32::NoallocScratch* fixed = nullptr) {
   if (log_enabled())
     std::fprintf(stderr, "[gemm_f32] M=%d N=%d K=%d lda=%lld ldb=%lld ldc=%lld -> %s\n", p.M,
                  p.N, p.K, (long long)p.lda, (long long)p.ldb, (long long)p.ldc,
@@ -339,8 +341,14 @@ int run_entry(const Entry& e, const Op& op, const Problem& p, int dev, hipStream
       const MfmaPlan pl = plan_mfma(v, p, e.kind == Kind::MfmaSplitK);
       float* partials = nullptr;
       if (pl.slices > 1) {
-        const int rc = get_workspace(dev, s, (size_t)pl.slices * p.M * p.N, &partials);
-        if (rc != GEMM_F32_OK) return rc;
+        const size_t need = (size_t)pl.slices * p.M * p.N;
+        if (fixed) {
+          if (need > fixed->partial_floats) return GEMM_F32_ERR_SCRATCH;
+          partials = fixed->partials;
+        } else {
+          const int rc = get_workspace(dev, s, need, &partials);
+          if (rc != GEMM_F32_OK) return rc;
+        }
       }
       err = v.launch(p, pl.slices, pl.kchunk, partials, op.epilogue(), s);
       break;
@@ -349,13 +357,20 @@ int run_entry(const Entry& e, const Op& op, const Problem& p, int dev, hipStream
       const auto& v = gemmf32::skinny_variant(e.sub);
       gemmf32::SkinnyPlan pl = v.plan(p, v.target_splits);
       float* partials = nullptr;
-      if (pl.partial_floats > 0) {
-        const int rc = get_workspace(dev, s, pl.partial_floats, &partials);
-        if (rc != GEMM_F32_OK) return rc;
-      }
-      if (pl.slot_words > 0) {
-        const int rc = get_exchange_slots(dev, s, pl.slot_words, &pl.slots);
-        if (rc != GEMM_F32_OK) return rc;
+      if (fixed) {
+        if (pl.partial_floats > fixed->partial_floats || pl.slot_words > fixed->slot_words)
+          return GEMM_F32_ERR_SCRATCH;
+        if (pl.partial_floats > 0) partials = fixed->partials;
+        if (pl.slot_words > 0) pl.slots = fixed->slots;
+      } else {
+        if (pl.partial_floats > 0) {
+          const int rc = get_workspace(dev, s, pl.partial_floats, &partials);
+          if (rc != GEMM_F32_OK) return rc;
+        }
+        if (pl.slot_words > 0) {
+          const int rc = get_exchange_slots(dev, s, pl.slot_words, &pl.slots);
+          if (rc != GEMM_F32_OK) return rc;
+        }
       }
       err = v.launch(p, pl, partials, op.epilogue(), s);
       break;
@@ -477,6 +492,22 @@ int gemm_impl(const Op& op, int64_t M, int64_t N, int64_t K, const float* A, int
   const int idx = find_entry(select_name(op, M, N, K, lda, ldb, A, B));
   if (idx < 0) return GEMM_F32_ERR_BAD_KERNEL;
   return run_entry(entries()[idx], op, r.p, r.dev, s);
+}
+
+// gemm_f32 with the fixed scratch array instead of the stream's workspaces.
+int gemm_noalloc_impl(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                      const float* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+  const Op op;
+  Prepared r = prepare(op, M, N, K, A, lda, B, ldb, C, ldc);
+  if (r.status != GEMM_F32_OK || M == 0 || N == 0) return r.status;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) return run_k0(op, r.p, s);
+  const int idx = find_entry(select_name(op, M, N, K, lda, ldb, A, B));
+  if (idx < 0) return GEMM_F32_ERR_BAD_KERNEL;
+  gemmf32::NoallocScratch fixed;
+  const int rc = gemmf32::noalloc_scratch(r.dev, s, &fixed);
+  if (rc != GEMM_F32_OK) return rc;
+  return run_entry(entries()[idx], op, r.p, r.dev, s, &fixed);
 }
 
 int run_kernel_impl(int index, const Op& op, int64_t M, int64_t N, int64_t K, const float* A,
@@ -628,6 +659,11 @@ int gemm_f32(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const
   return gemm_impl(Op{}, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
+int gemm_f32_noalloc(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                     const float* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+  return gemm_noalloc_impl(M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
 int gemm_f32_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
                 const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
                 int64_t ldc, void* stream) {
@@ -746,6 +782,7 @@ const char* gemm_f32_status_string(int status) {
     case GEMM_F32_ERR_BAD_KERNEL: return "kernel index unknown or unable to run these arguments";
     case GEMM_F32_ERR_POINTER: return "pointer is not device memory the current device can access";
     case GEMM_F32_ERR_INVALID_ARG: return "unknown activation";
+    case GEMM_F32_ERR_SCRATCH: return "the call needs more scratch than gemm_f32_noalloc's fixed array holds";
     default: return "unknown status";
   }
 }

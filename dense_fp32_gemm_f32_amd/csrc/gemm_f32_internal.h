@@ -167,6 +167,19 @@ struct ReducePlan {
 ReducePlan plan_reduce(int64_t n);
 hipError_t launch_reduce_sum(int64_t n, const float* x, float* out, float* part, hipStream_t s);
 
+// ---- the fixed scratch array of gemm_f32_noalloc (scratch_static.hip) ------
+// Device addresses of this device's copy: the exchange slots (all zero
+// between calls) and the partial-sum floats.  Looked up, and the slots
+// cleared, on the first call per device; GEMM_F32_ERR_WORKSPACE if that first
+// call is on a stream being captured, GEMM_F32_ERR_LAUNCH if the clear fails.
+struct NoallocScratch {
+  unsigned long long* slots = nullptr;
+  size_t slot_words = 0;
+  float* partials = nullptr;
+  size_t partial_floats = 0;
+};
+int noalloc_scratch(int dev, hipStream_t s, NoallocScratch* out);
+
 // ---- naive reference and the K == 0 fill ----------------------------------
 hipError_t launch_ref(const Problem& p, hipStream_t s);
 // C = beta * C over the M x N window (C = +0.0 when beta == 0; C not read then)

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GEMM_F32_VERSION 4
+#define GEMM_F32_VERSION 5
 
 /* Activations of gemm_f32_fused. */
 #define GEMM_F32_ACT_NONE 0
@@ -76,6 +76,11 @@ extern "C" {
 
 /* Largest accepted M, N or K (2^31 - 2^16: tile arithmetic stays in int32). */
 #define GEMM_F32_MAX_DIM INT64_C(2147418112)
+
+/* The fixed scratch of gemm_f32_noalloc, per device: exchange slots of the
+ * in-kernel K-slice sum, then per-slice partial sums (16 MiB in all). */
+#define GEMM_F32_NOALLOC_SLOT_BYTES 4194304
+#define GEMM_F32_NOALLOC_PARTIAL_BYTES 12582912
 
 enum gemm_f32_status {
   GEMM_F32_OK = 0,
@@ -88,7 +93,8 @@ enum gemm_f32_status {
   GEMM_F32_ERR_LAUNCH = 7,        /* the kernel launch reported an error */
   GEMM_F32_ERR_BAD_KERNEL = 8,    /* unknown kernel index, or one that cannot run these arguments */
   GEMM_F32_ERR_POINTER = 9,       /* A, B or C not 4-byte aligned, or not memory the current device can access */
-  GEMM_F32_ERR_INVALID_ARG = 10   /* an activation other than GEMM_F32_ACT_NONE / _RELU */
+  GEMM_F32_ERR_INVALID_ARG = 10,  /* an activation other than GEMM_F32_ACT_NONE / _RELU */
+  GEMM_F32_ERR_SCRATCH = 11       /* gemm_f32_noalloc: the call needs more scratch than its fixed array */
 };
 
 /*
@@ -113,6 +119,34 @@ int gemm_f32(int64_t M, int64_t N, int64_t K,
              const float *B, int64_t ldb,
              float *C, int64_t ldc,
              void *stream);
+
+/*
+ * gemm_f32_noalloc -- gemm_f32 for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, checks, kernel choice and result as gemm_f32,
+ * bit for bit; the kernels that split K over workgroups take their scratch
+ * from a fixed array compiled into the library instead of a per-stream
+ * workspace, so no call allocates or frees anything.
+ *
+ * The array is GEMM_F32_NOALLOC_SLOT_BYTES of exchange slots plus
+ * GEMM_F32_NOALLOC_PARTIAL_BYTES of partial sums, one copy per device, held
+ * from the library's load until the process ends.  A call whose kernel needs
+ * more than either region returns GEMM_F32_ERR_SCRATCH and enqueues nothing
+ * (only M <= 16 products split K: e.g. 8 x 28672 x 4096 needs 7.3 MB of
+ * partial sums, 8 x 8192 x 8192 1 MiB of slots; gemm_f32 has no such limit).
+ * The first call on each device looks the array up and clears the slot region,
+ * waiting for that on `stream`; when that first call is on a stream being
+ * captured it returns GEMM_F32_ERR_WORKSPACE instead (make one call outside
+ * capture first).  Every call on a device shares that device's array: calls
+ * that may overlap on one device (other streams, graph replays) race and must
+ * be ordered by the caller.  gemm_f32, gemm_f32_ex and the others keep their
+ * own workspaces and never touch the array.
+ */
+int gemm_f32_noalloc(int64_t M, int64_t N, int64_t K,
+                     const float *A, int64_t lda,
+                     const float *B, int64_t ldb,
+                     float *C, int64_t ldc,
+                     void *stream);
 
 /*
  * gemm_f32_ex -- C = alpha * op(A) op(B) + beta * C, the BLAS-style form for

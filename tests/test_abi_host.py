@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert binding.gemm_f32_version() == 4
+    assert binding.gemm_f32_version() == 5
 
 
 def test_status_strings():
@@ -78,12 +78,14 @@ R16 = 0x190000000
 def test_argument_errors_before_any_device_call(args, code):
     assert binding.gemm_f32(*args, 0) == code
     assert binding.gemm_f32_ref_gpu(*args, 0) == code
+    assert binding.gemm_f32_noalloc(*args, 0) == code
     assert binding.gemm_f32_run_kernel(0, *args, 0) == code
 
 
 def test_empty_problems_succeed_without_a_device():
     assert binding.gemm_f32(0, 4, 4, 0, 4, Q16, 4, 0, 4, 0) == 0
     assert binding.gemm_f32(4, 0, 4, P16, 4, 0, 1, 0, 1, 0) == 0
+    assert binding.gemm_f32_noalloc(0, 4, 4, 0, 4, Q16, 4, 0, 4, 0) == 0
     # a NULL A is fine when A has no elements, even if M > 0 (K == 0), but the
     # K == 0 fill needs a device, so only the M == 0 / N == 0 cases run here
 
