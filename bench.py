@@ -3,9 +3,13 @@
 fraction of the MI355X fp32 MFMA peak.
 
 One step = one gemm_f32 call (C = A x B, fp32, row-major) on the 4096^3
-workload with A and B already resident in HBM.  W untimed warm-up steps, then
-K timed steps bracketed by a device synchronisation on both sides.  Prints
-ONE JSON line.
+workload with A and B already resident in HBM.  --settle seconds (0.3 by
+default) of untimed calls, W untimed warm-up steps, then K timed steps
+bracketed by a device synchronisation on both sides.  Prints ONE JSON line;
+its "timing" object declares the settle and holds every launch's duration,
+the means of the first and last quarter of the timed launches, and the shader
+clock (gemm_f32_clock_probe) before the settle and right after the timed
+steps.
 
 Kernel time is measured with HIP events recorded on the stream the library
 launches on (torch's current stream), one pair per launch; the roofline
@@ -54,6 +58,10 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed headline calls before the --warmup steps, so the "
+                         "timed steps do not start at the idle clocks input generation leaves "
+                         "(declared in the record; 0 for none)")
     ap.add_argument("--configs", action="store_true",
                     help="instead of the single headline line, print one JSON line per "
                          "workload (median/min time, rate, reruns, oracle time and agreement)")
@@ -67,7 +75,7 @@ def settle(fn, seconds=0.3):
     """Untimed: keep calling fn for `seconds`, so that the GPU clocks have left
     the idle state that host-side work (input generation, oracle checks) puts
     them in; a few dozen warm-up launches of a 50 us kernel take 2 ms, too
-    short for that."""
+    short for that.  Returns the number of calls made."""
     import torch
     t_end, i = time.perf_counter() + seconds, 0
     while time.perf_counter() < t_end:
@@ -76,15 +84,19 @@ def settle(fn, seconds=0.3):
         if i % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    return i
 
 
-def time_launches(fn, steps, warmup, stream, settle_s=0.3):
+def time_launches(fn, steps, warmup, stream, settle_s=0.3, stats=None):
     """Settle the clocks (settle_s seconds of untimed calls), run fn() warmup
     times, then steps times with an event pair around each launch on
-    `stream`.  Returns (wall ms per step, list of per-launch ms)."""
+    `stream`.  Returns (wall ms per step, list of per-launch ms); the number
+    of settle calls goes to stats["settle_calls"] when stats is a dict."""
     import torch
     if settle_s > 0:
-        settle(fn, settle_s)
+        n = settle(fn, settle_s)
+        if stats is not None:
+            stats["settle_calls"] = n
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
@@ -122,6 +134,17 @@ def traffic_for(kernel_name: str):
     None if it was taken on a different kernel source."""
     rec = profile_record(kernel_name)
     return rec.get("hbm_bytes_per_launch") if rec else None
+
+
+def _clock_summary(probe):
+    """Median, min and max of the per-workgroup clocks of one probe, in GHz,
+    with the counter rates it was read against."""
+    ghz, wall_khz, peak_khz = probe
+    if not ghz:
+        return None
+    g = sorted(ghz)
+    return {"median": round(g[len(g) // 2], 4), "min": round(g[0], 4), "max": round(g[-1], 4),
+            "wall_counter_khz": wall_khz, "device_peak_khz": peak_khz}
 
 
 def launch_amortisation(stream, steps, warmup, batch=64, n=512):
@@ -396,10 +419,16 @@ def main():
     A, B = A_cpu.to(dev), B_cpu.to(dev)
     C = torch.empty((w.M, w.N), device=dev)
     kname = binding.selected_kernel(A, B, C)
-    # exactly W warm-up steps before the K timed ones (no extra settle)
+    # The shader clock as the timed region is entered from idle, then the
+    # declared settle (--settle seconds of the same call, untimed), the W
+    # warm-up steps and the K timed steps; the clock again right after them.
+    clock_before = _clock_summary(binding.clock_probe())
+    st = {"settle_calls": 0}
     wall_ms, per = time_launches(lambda i: binding.gemm(A, B, C), args.steps, args.warmup,
-                                 stream, settle_s=0)
+                                 stream, settle_s=args.settle, stats=st)
+    clock_after = _clock_summary(binding.clock_probe())
     mean_launch_ms = sum(per) / len(per)
+    q = max(1, len(per) // 4)
     flops = w.flops
     value = flops / (wall_ms * 1e-3) / 1e9
     achieved_tflops = flops / (mean_launch_ms * 1e-3) / 1e12
@@ -426,6 +455,20 @@ def main():
                      "traffic": traffic,
                      "launch_ms_mean": round(mean_launch_ms, 4),
                      "launch_ms_min": round(min(per), 4)},
+        # how the timed steps were reached, and the clock they ran at
+        "timing": {"settle_s": args.settle, "settle_calls": st["settle_calls"],
+                   "warmup_steps": args.warmup, "events": "one HIP event pair per launch on "
+                   "the launch stream",
+                   "launch_ms": [round(x, 4) for x in per],
+                   "first_quarter_ms_mean": round(sum(per[:q]) / q, 4),
+                   "last_quarter_ms_mean": round(sum(per[-q:]) / q, 4),
+                   "clock_ghz_before_settle": clock_before,
+                   "clock_ghz_after_timed": clock_after,
+                   "clock_method": "gemm_f32_clock_probe: s_memtime cycles over s_memrealtime "
+                                   "ticks (at wall_counter_khz) across ~1 ms of fp32 MFMA load "
+                                   "on every SIMD, median over 1024 workgroups",
+                   "peak_at_clock_after_tflops": round(
+                       256 * 256 * clock_after["median"] / 1e3, 1) if clock_after else None},
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
     }

@@ -33,7 +33,8 @@ EXPORTS = ["gemm_f32", "gemm_f32_ex", "gemm_f32_ref_gpu", "gemm_f32_status_strin
            "gemm_f32_kernel_count", "gemm_f32_kernel_name", "gemm_f32_run_kernel",
            "gemm_f32_run_kernel_ex", "gemm_f32_release_workspaces", "gemm_f32_batched",
            "gemm_f32_selected_kernel_batched", "reduce_sum_f32", "gemm_f32_fused",
-           "gemm_f32_run_kernel_fused", "gemm_f32_noalloc"]
+           "gemm_f32_run_kernel_fused", "gemm_f32_noalloc", "gemm_f32_clock_probe"]
+CLOCK_PROBE_WORKGROUPS = 1024
 
 
 class GemmError(RuntimeError):
@@ -93,6 +94,8 @@ def load(lib_path=None):
     lib.gemm_f32_kernel_name.restype = ctypes.c_char_p
     lib.gemm_f32_release_workspaces.argtypes = []
     lib.gemm_f32_release_workspaces.restype = ctypes.c_int
+    lib.gemm_f32_clock_probe.argtypes = [i64, vp, vp, vp, vp]
+    lib.gemm_f32_clock_probe.restype = ctypes.c_int
     lib.reduce_sum_f32.argtypes = [i64, vp, vp, vp]
     lib.reduce_sum_f32.restype = ctypes.c_int
     lib.gemm_f32_batched.argtypes = [i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64,
@@ -154,6 +157,10 @@ def gemm_f32_selected_kernel_batched(M, N, K, lda, strideA, ldb, strideB, ldc, b
                                      B=0) -> str:
     return load().gemm_f32_selected_kernel_batched(M, N, K, lda, strideA, ldb, strideB, ldc,
                                                    batch, A, B).decode()
+
+
+def gemm_f32_clock_probe(iters, stamps, wall_khz=None, max_khz=None, stream=0) -> int:
+    return load().gemm_f32_clock_probe(iters, stamps, wall_khz, max_khz, stream)
 
 
 def reduce_sum_f32(n, x, out, stream=0) -> int:
@@ -334,6 +341,26 @@ def reduce_sum(x, out=None):
     if rc != GEMM_F32_OK:
         raise GemmError(rc, "reduce_sum_f32")
     return out
+
+
+def clock_probe(iters=2400, device=None):
+    """Run gemm_f32_clock_probe on torch's current stream of ``device`` and
+    wait for it.  Returns (per-workgroup achieved shader clocks in GHz, the
+    constant counter's rate in kHz, the device's peak shader clock in kHz)."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    stamps = torch.zeros(4 * CLOCK_PROBE_WORKGROUPS, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    wall, peak = ctypes.c_int(0), ctypes.c_int(0)
+    with _device(stamps):
+        rc = gemm_f32_clock_probe(iters, stamps.data_ptr(), ctypes.byref(wall),
+                                  ctypes.byref(peak), stream)
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc, "gemm_f32_clock_probe")
+    torch.cuda.synchronize(dev)
+    w = stamps.view(-1, 4).cpu().tolist()
+    ghz = [wall.value * 1e-6 * (t1 - t0) / (r1 - r0) for t0, r0, t1, r1 in w if r1 > r0]
+    return ghz, wall.value, peak.value
 
 
 def _args_ex(A, B, C, trans_a, trans_b):

@@ -769,6 +769,31 @@ int gemm_f32_run_kernel_ex(int index, int transA, int transB, int64_t M, int64_t
                          C, ldc, stream);
 }
 
+int gemm_f32_clock_probe(int64_t iters, unsigned long long* stamps, int* wall_khz,
+                         int* max_khz, void* stream) {
+  static_assert(GEMM_F32_CLOCK_PROBE_WORKGROUPS == gemmf32::kClockProbeWorkgroups,
+                "one probe grid size");
+  if (iters < 1 || iters > (INT64_C(1) << 24)) return GEMM_F32_ERR_INVALID_DIM;
+  if (!stamps) return GEMM_F32_ERR_NULL_PTR;
+  if (((uintptr_t)stamps & 7u) != 0) return GEMM_F32_ERR_POINTER;
+  int dev = -1;
+  int rc = check_device(&dev);
+  if (rc != GEMM_F32_OK) return rc;
+  if ((rc = check_pointer(stamps, dev)) != GEMM_F32_OK) return rc;
+  if ((wall_khz &&
+       hipDeviceGetAttribute(wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) ||
+      (max_khz && hipDeviceGetAttribute(max_khz, hipDeviceAttributeClockRate, dev) != hipSuccess)) {
+    (void)hipGetLastError();
+    return GEMM_F32_ERR_DEVICE;
+  }
+  if (gemmf32::launch_clock_probe((int)iters, stamps, static_cast<hipStream_t>(stream)) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return GEMM_F32_ERR_LAUNCH;
+  }
+  return GEMM_F32_OK;
+}
+
 const char* gemm_f32_status_string(int status) {
   switch (status) {
     case GEMM_F32_OK: return "ok";

@@ -180,6 +180,13 @@ struct NoallocScratch {
 };
 int noalloc_scratch(int dev, hipStream_t s, NoallocScratch* out);
 
+// ---- the shader clock under fp32 MFMA load (clock_probe.hip) ---------------
+// kClockProbeWorkgroups workgroups of 4 waves, each wave 4 x iters MFMAs;
+// workgroup w writes [s_memtime, s_memrealtime] at its start and end to
+// stamps[4w .. 4w + 3].
+constexpr int kClockProbeWorkgroups = 1024;
+hipError_t launch_clock_probe(int iters, unsigned long long* stamps, hipStream_t s);
+
 // ---- naive reference and the K == 0 fill ----------------------------------
 hipError_t launch_ref(const Problem& p, hipStream_t s);
 // C = beta * C over the M x N window (C = +0.0 when beta == 0; C not read then)

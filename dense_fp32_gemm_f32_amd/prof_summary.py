@@ -189,6 +189,7 @@ def main(argv=None):
     ap.add_argument("--mfma-cycles", type=int, default=0,
                     help="cycles one MFMA of the kernel occupies the pipe (32x32x2 f32: 64)")
     ap.add_argument("--command", action="append", default=[])
+    ap.add_argument("--log", help="stdout of the trace run (for its clock-probe line)")
     ap.add_argument("--out", required=True)
     args = ap.parse_args(argv)
     if args.bench_trace:
@@ -218,6 +219,13 @@ def main(argv=None):
     lines += ["", f"Sum of average durations of the matched kernels: {tot_avg / 1e3:.2f} us "
               f"-> {args.flops / (tot_avg * 1e-9) / 1e12:.2f} TFLOP/s, "
               f"{args.algo_bytes / (tot_avg * 1e-9) / 1e9:.1f} GB/s of algorithmic traffic", ""]
+    if args.log:
+        probe = [l.strip() for l in Path(args.log).read_text().splitlines()
+                 if l.startswith("clock probe:")]
+        if probe:
+            lines += [f"Shader clock right after the traced launches, same run "
+                      f"(gemm_f32_clock_probe: s_memtime over the 100 MHz s_memrealtime across "
+                      f"about 1 ms of fp32 MFMA load): {probe[-1][len('clock probe: '):]}", ""]
 
     traffic = None
     if args.fetch and args.write:
@@ -257,11 +265,11 @@ def main(argv=None):
                       "200 us or more: on shorter ones GRBM_GUI_ACTIVE also counts the "
                       "counter collection around the dispatch.)"]
         if "GRBM_GUI_ACTIVE" in c and long_enough:
+            # Both terms of each ratio below come from the same counter run.  No
+            # clock is derived here: GRBM_GUI_ACTIVE comes from the counter run
+            # and the duration from the trace run, two different launches.
             xcd_cycles = c["GRBM_GUI_ACTIVE"] / 8.0     # summed over the 8 XCDs
             lines.append("")
-            if n in dur:
-                lines.append(f"Clock while the kernel runs = GRBM_GUI_ACTIVE/8 / average duration "
-                             f"= {xcd_cycles / dur[n][1]:.3f} GHz")
             busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
             if busy is not None and busy < 2.0 ** 31 * 0.999:
                 util = busy / (xcd_cycles * 1024.0)

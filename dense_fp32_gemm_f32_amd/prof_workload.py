@@ -6,6 +6,10 @@ size, for rocprofv3 kernel traces and hardware counters.
     rocprofv3 --pmc FETCH_SIZE -d OUT -o fetch -f csv -- \
         python3 -m dense_fp32_gemm_f32_amd.prof_workload --workload square_4096
 
+A run with ``--settle-ms`` (a trace run) also prints the shader clock right
+after the launches (``gemm_f32_clock_probe``), which ``prof_summary --log``
+quotes.
+
 The copy (``torch.Tensor.copy_`` of ``--copy-mib`` MiB, a plain streaming
 kernel that reads and writes exactly that many bytes) calibrates the
 FETCH_SIZE / WRITE_SIZE counters: HBM bytes of a GEMM launch are its counter
@@ -49,6 +53,8 @@ def main(argv=None):
         for i in range(args.reps):
             binding.reduce_sum(xs[i % 4], out)
         torch.cuda.synchronize()
+        if args.settle_ms > 0:
+            _clock(binding)
         _calibration_copy(dev, args.copy_mib)
         return 0
     w = inputs.WORKLOADS[args.workload]
@@ -75,8 +81,20 @@ def main(argv=None):
     for i in range(args.reps):
         binding.run_kernel(name, As[i % copies], Bs[i % copies], Cs[i % copies])
     torch.cuda.synchronize()
+    if args.settle_ms > 0:
+        _clock(binding)
     _calibration_copy(dev, args.copy_mib)
     return 0
+
+
+def _clock(binding):
+    """The shader clock right after the launches, from gemm_f32_clock_probe in
+    the same process (its own kernel in the trace)."""
+    ghz, wall_khz, peak_khz = binding.clock_probe()
+    g = sorted(ghz)
+    print(f"clock probe: median {g[len(g) // 2]:.4f} GHz (min {g[0]:.4f}, max {g[-1]:.4f}) "
+          f"over {len(g)} workgroups; constant counter {wall_khz} kHz, device peak clock "
+          f"{peak_khz} kHz", flush=True)
 
 
 def _settle(fn, ms):

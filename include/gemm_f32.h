@@ -270,6 +270,31 @@ int gemm_f32_ref_gpu(int64_t M, int64_t N, int64_t K,
  */
 int reduce_sum_f32(int64_t n, const float *x, float *out, void *stream);
 
+/*
+ * gemm_f32_clock_probe -- for measurement records: the shader clock the GPU
+ * sustains under fp32 matrix-core load at the time of the call.  The fp32
+ * MFMA peak is 256 FLOP per clock per CU, so a throughput is read against
+ * the clock it ran at ("GPU compute shaders", Performance: GPU-timed runs).
+ * Launches GEMM_F32_CLOCK_PROBE_WORKGROUPS workgroups of 4 waves (4 per CU on
+ * MI355X, every SIMD busy), each wave issuing 4 * iters
+ * v_mfma_f32_32x32x2_f32 on registers only (about 1 ms for iters = 2400).
+ * Workgroup w writes four 64-bit words to stamps[4w .. 4w + 3]: the shader
+ * cycle counter (s_memtime) and the constant-rate counter (s_memrealtime)
+ * after a barrier at its start, then both again after a barrier at its end.
+ * The achieved clock in kHz is wall_khz * (word 2 - word 0) / (word 3 - word
+ * 1).  stamps: device memory of 4 * GEMM_F32_CLOCK_PROBE_WORKGROUPS uint64,
+ * caller-owned.  wall_khz, max_khz: host ints (either may be NULL) that
+ * receive the constant counter's rate (hipDeviceAttributeWallClockRate) and
+ * the device's peak shader clock (hipDeviceAttributeClockRate), in kHz.
+ * Errors: iters outside [1, 2^24] GEMM_F32_ERR_INVALID_DIM; NULL stamps
+ * GEMM_F32_ERR_NULL_PTR; stamps not 8-byte aligned or not reachable
+ * GEMM_F32_ERR_POINTER; then the device check of gemm_f32.  The kernel is
+ * asynchronous on `stream`; the two rates are written before the call returns.
+ */
+#define GEMM_F32_CLOCK_PROBE_WORKGROUPS 1024
+int gemm_f32_clock_probe(int64_t iters, unsigned long long *stamps, int *wall_khz,
+                         int *max_khz, void *stream);
+
 /* Human-readable text for a status code (static storage, never NULL). */
 const char *gemm_f32_status_string(int status);
 

@@ -141,27 +141,40 @@ def test_ex_k_zero_scales_c(gpu_lib, beta):
     assert np.array_equal(C.cpu().numpy(), want)
 
 
-@pytest.mark.parametrize("ta,tb", LAYOUTS)
-def test_ex_full_size_sampled(gpu_lib, ta, tb):
-    """4096^3 in every layout with alpha, beta: sampled outputs against the
-    oracle evaluated element by element on the explicit product."""
+@pytest.mark.parametrize("integer", [False, True])
+@pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)])
+def test_ex_full_size(gpu_lib, ta, tb, integer):
+    """4096^3 with an operand stored transposed (the kernels bench.py times
+    for nt, tn and tt), alpha and beta: every element against the oracle.
+    The oracle runs on the logical operands as stored untransposed; its pins
+    show that the transposed storage gives the same bits (C, sums and
+    magnitudes), and this keeps its reads sequential at this size.  Integer
+    inputs with integer alpha and beta: bit-exact."""
     w = inputs.WORKLOADS["square_4096"]
-    A, B = inputs.workload_inputs(w)
-    Cin = inputs.uniform_matrix(w.M, w.N, 7500)
-    alpha, beta = 1.25, -0.5
-    H.say(f"ex 4096^3 trans={int(ta)}{int(tb)}")
+    A, B = inputs.workload_inputs(w, integer=integer)
+    if integer:
+        Cin = inputs.int_matrix(w.M, w.N, 7502, -5, 5)
+        alpha, beta = 2.0, -1.0
+    else:
+        Cin = inputs.uniform_matrix(w.M, w.N, 7500)
+        alpha, beta = 1.25, -0.5
+    H.say(f"ex 4096^3 trans={int(ta)}{int(tb)} int={integer}")
     Ad, Bd = A.cuda(), B.cuda()
     As = Ad.t().contiguous() if ta else Ad
     Bs = Bd.t().contiguous() if tb else Bd
+    del Ad, Bd
     C = Cin.cuda()
+    kname = gpu_lib.selected_kernel_ex(As, Bs, C, trans_a=ta, trans_b=tb, alpha=alpha, beta=beta)
+    assert "_d6_" in kname, kname   # the direct-to-LDS kernel the bench times
     gpu_lib.gemm_ex(As, Bs, C, trans_a=ta, trans_b=tb, alpha=alpha, beta=beta)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(7501)
-    r = rng.integers(0, w.M, 512)
-    c = rng.integers(0, w.N, 512)
-    # the plain product's binary64 sums, then the update as gemm_ex defines it
-    _, Sd, ABS = oracle.gemm_elems(A.numpy(), B.numpy(), r, c)
-    got = C.cpu().numpy()[r, c].astype(np.float64)
-    ref = np.float32(alpha) * Sd + np.float32(beta) * Cin.numpy()[r, c].astype(np.float64)
-    scale = abs(alpha) * ABS + abs(beta) * np.abs(Cin.numpy()[r, c].astype(np.float64))
-    assert np.all(np.abs(got - ref) <= H.REL_TOL * scale)
+    got = C.cpu().numpy()
+    del As, Bs, C
+    C_ref, _, ABS = oracle.gemm_ex(A.numpy(), B.numpy(), alpha=alpha, beta=beta,
+                                   C_in=Cin.numpy())
+    what = f"{kname} 4096^3 trans={int(ta)}{int(tb)}"
+    if integer:
+        H.assert_bitexact(got, C_ref, what)
+    else:
+        ratio = H.assert_within_tol(got, C_ref, ABS, what)
+        print(f"{what}: max |dC| / scale = {ratio:.3e}")
