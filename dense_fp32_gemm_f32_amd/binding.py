@@ -10,11 +10,14 @@ in the HIP kernels:
   which read sizes, pitches and pointers from the tensors and enqueue on
   torch's current stream of the tensors' device.
 
-There is no fallback: if the library is missing, ``load()`` raises.
+There is no fallback: if the library is missing, ``load()`` raises.  The
+environment variable ``GEMM_F32_LIB`` names another build of the same library
+to load instead (the host-sanitizer build of ``sanitize_host.py``).
 """
 from __future__ import annotations
 
 import ctypes
+import os
 from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
@@ -55,6 +58,8 @@ def load(lib_path=None):
         if lib_path is not None and Path(lib_path) != Path(_lib._name):
             raise RuntimeError(f"{_lib._name} is already loaded")
         return _lib
+    if lib_path is None and os.environ.get("GEMM_F32_LIB"):
+        lib_path = os.environ["GEMM_F32_LIB"]
     path = Path(lib_path) if lib_path is not None else LIB_PATH
     if not path.exists():
         raise FileNotFoundError(
