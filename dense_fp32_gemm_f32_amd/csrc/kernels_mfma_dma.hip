@@ -235,27 +235,9 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
                                  K / BK, acc);
 
   // ---- masked epilogue ------------------------------------------------------
-  const int wmi = wave % C_::kWavesM, wni = wave / C_::kWavesM;
-  const int lr = lane & 31, lk = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < C_::kFragM; ++i) {
-#pragma unroll
-    for (int j = 0; j < C_::kFragN; ++j) {
-      const int col = n0 + wni * WN + 32 * j + lr;
-      const int rbase = m0 + wmi * WM + 32 * i + 4 * lk;
-      if (col < N) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + 8 * (r >> 2) + (r & 3);
-          if (row < M) {
-            // a K slice writes its raw partial sum; the combine applies the update
-            float* c = p.C + (int64_t)row * p.ldc + col;
-            *c = part ? acc[i][j][r] : epilogue_apply(ep, acc[i][j][r], c, col);
-          }
-        }
-      }
-    }
-  }
+  store_blocks<C_::kFragM, C_::kFragN>(acc, p.C, p.ldc, M, N, m0 + (wave % C_::kWavesM) * WM,
+                                       n0 + (wave / C_::kWavesM) * WN, lane, part != nullptr,
+                                       ep);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int kMinWaves>

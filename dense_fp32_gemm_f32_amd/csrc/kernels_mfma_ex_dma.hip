@@ -247,24 +247,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
   if constexpr (kDual) acc[0][0] += acc_odd;
 
   // ---- masked epilogue: C = act(alpha * acc + beta * C + bias) ---------------
-#pragma unroll
-  for (int i = 0; i < kFragM; ++i) {
-#pragma unroll
-    for (int j = 0; j < kFragN; ++j) {
-      const int col = n0 + wr_b + 32 * j + lr;
-      const int rbase = m0 + wr_a + 32 * i + 4 * lk;
-      if (col < N) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = rbase + 8 * (r >> 2) + (r & 3);
-          if (row < M) {
-            float* c = p.C + (int64_t)row * p.ldc + col;
-            *c = epilogue_apply(ep, acc[i][j][r], c, col);
-          }
-        }
-      }
-    }
-  }
+  store_blocks<kFragM, kFragN>(acc, p.C, p.ldc, M, N, m0 + wr_a, n0 + wr_b, lane, false, ep);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, bool A_KC, bool B_KC, int kMinWaves>

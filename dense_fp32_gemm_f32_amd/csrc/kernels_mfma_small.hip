@@ -191,24 +191,7 @@ __global__ void __launch_bounds__(KS * 64)
   }
 
   // ---- masked store; a K slice writes its raw partial ------------------------
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = n0 + 32 * j + lr;
-      const int rbase = m0 + 32 * i + 4 * lk;
-      if (col < N) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int row = rbase + 8 * (q >> 2) + (q & 3);
-          if (row < M) {
-            float* c = p.C + (int64_t)row * p.ldc + col;
-            *c = part ? acc[i][j][q] : epilogue_apply(ep, acc[i][j][q], c, col);
-          }
-        }
-      }
-    }
-  }
+  store_blocks<FM, FN>(acc, p.C, p.ldc, M, N, m0, n0, lane, part != nullptr, ep);
 }
 
 template <int TM, int TN, int KS, int D>

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "gemm_f32_internal.h"
+
 namespace gemmf32 {
 namespace mfma {
 
@@ -76,6 +78,47 @@ __device__ __forceinline__ int swz_a(int m) {
 // B tile in LDS: n of row k is XORed with 32 when bit 2 of k is set, so the
 // rows k and k + 4 read together by one fragment land in opposite bank halves.
 __device__ __forceinline__ int swz_b(int k) { return ((k >> 2) & 1) << 5; }
+
+// Masked store of a wave's accumulator blocks (32 x 32 each, block (i, j) at
+// rows row0 + 32 i, columns col0 + 32 j of C) with the update `ep`: register
+// r of lane l is element (8 (r / 4) + 4 (l / 32) + r % 4, l % 32) of its block.
+// raw: a K slice's partial sum, stored as is (the combine applies the update).
+// The plain product (alpha 1, beta 0, no bias, identity) stores the sums
+// directly, which is what the update computes for it (1 * s == s); the branch
+// is uniform, so each store loop is free of per-element tests of the update.
+template <int KFM, int KFN>
+__device__ __forceinline__ void store_blocks(const floatx16 (&acc)[KFM][KFN], float* C,
+                                             int64_t ldc, int M, int N, int row0, int col0,
+                                             int lane, bool raw, const Epilogue& ep) {
+  const int lr = lane & 31, lk = lane >> 5;
+  const bool direct = raw || (ep.alpha == 1.f && ep.beta == 0.f && !ep.bias && ep.act == 0);
+#pragma unroll
+  for (int i = 0; i < KFM; ++i) {
+#pragma unroll
+    for (int j = 0; j < KFN; ++j) {
+      const int col = col0 + 32 * j + lr;
+      const int rbase = row0 + 32 * i + 4 * lk;
+      if (col < N) {
+        if (direct) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rbase + 8 * (r >> 2) + (r & 3);
+            if (row < M) C[(int64_t)row * ldc + col] = acc[i][j][r];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rbase + 8 * (r >> 2) + (r & 3);
+            if (row < M) {
+              float* c = C + (int64_t)row * ldc + col;
+              *c = epilogue_apply(ep, acc[i][j][r], c, col);
+            }
+          }
+        }
+      }
+    }
+  }
+}
 
 // MFMA k-slot assignment.  One ds_read_b128 gives lane l four consecutive k
 // of its A row: k = 8q + 4*(l/32) + s for s = 0..3.  MFMA step s therefore
