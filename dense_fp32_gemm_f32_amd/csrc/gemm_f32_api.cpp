@@ -303,8 +303,10 @@ bool accepts(const Entry& e, const Op& op, int64_t M, int64_t N, int64_t K, int6
     // any alpha and beta; the layout the kernel was built for
     const auto& v = gemmf32::skinny_variant(e.sub);
     if (M > v.mr || v.trans_a != op.ta || v.trans_b != op.tb) return false;
+    if (v.a16 && (lda % 4 != 0 || !aligned16(A))) return false;
     if (v.b16) {
-      if (N % 4 != 0 || ldb % 4 != 0 || !aligned16(B)) return false;
+      // whole 16-byte units of B's rows (and, for B stored K x N, of its columns)
+      if ((!v.trans_b && N % 4 != 0) || ldb % 4 != 0 || !aligned16(B)) return false;
       Problem p{static_cast<const float*>(A), static_cast<const float*>(B), nullptr, lda, ldb,
                 0, (int)M, (int)N, (int)K};
       if (v.plan(p, v.target_splits).splits > 65535) return false;

@@ -142,8 +142,11 @@ struct SkinnyVariant {
   SkinnyPlan (*plan)(const Problem&, int target_splits);
   hipError_t (*launch)(const Problem&, const SkinnyPlan&, float* partials, const Epilogue&,
                        hipStream_t);
-  // needs B 16-byte aligned with N and ldb multiples of 4 (whole float4 row runs)
+  // needs B 16-byte aligned with ldb a multiple of 4 (whole 16-byte units of
+  // its rows), and N a multiple of 4 too when B is stored K x N
   bool b16 = false;
+  // needs A 16-byte aligned with lda a multiple of 4
+  bool a16 = false;
 };
 int skinny_variant_count();          // all three kernels
 const SkinnyVariant& skinny_variant(int i);
@@ -151,6 +154,8 @@ int skinny_t_variant_count();        // B stored N x K
 const SkinnyVariant& skinny_t_variant(int i);
 int skinny_rows_variant_count();     // B stored K x N, KiB row runs
 const SkinnyVariant& skinny_rows_variant(int i);
+int skinny_tm_variant_count();       // B stored N x K, on the matrix cores
+const SkinnyVariant& skinny_tm_variant(int i);
 
 // ---- sum of K-slice partials: C = part[0] + part[1] + ... (slice order) ---
 // With alpha and beta: C = alpha * (sum of slices) + beta * C (C not read when beta == 0).

@@ -390,14 +390,16 @@ const SkinnyVariant kVariants[] = {
 
 int skinny_variant_count() {
   return (int)(sizeof(kVariants) / sizeof(kVariants[0])) + skinny_t_variant_count() +
-         skinny_rows_variant_count();
+         skinny_rows_variant_count() + skinny_tm_variant_count();
 }
 const SkinnyVariant& skinny_variant(int i) {
   const int n = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
   if (i < n) return kVariants[i];
   i -= n;
   if (i < skinny_t_variant_count()) return skinny_t_variant(i);
-  return skinny_rows_variant(i - skinny_t_variant_count());
+  i -= skinny_t_variant_count();
+  if (i < skinny_rows_variant_count()) return skinny_rows_variant(i);
+  return skinny_tm_variant(i - skinny_rows_variant_count());
 }
 
 }  // namespace gemmf32

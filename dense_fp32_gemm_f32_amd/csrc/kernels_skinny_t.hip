@@ -206,10 +206,15 @@ hipError_t launch_t(const Problem& p, const SkinnyPlan& pl, float* partials,
   {"skinnyt_m" #MR "_j" #JC "_u" #U "_tt", MR, kWavesPerGroup, U, false, true, 0, true,  \
    true, &plan_t<JC>, &launch_t<MR, JC, U, true>}
 
+// The default build holds the kernel the tuning table picks (M <= 8, B^T
+// not 16-byte aligned); a build with GEMM_F32_SWEEP also holds the others.
 const SkinnyVariant kTVariants[] = {
-    GEMMF32_SKINNY_T(8, 4, 2),
-    GEMMF32_SKINNY_T(16, 4, 2),
+    {"skinnyt_m8_j4_u2_nt", 8, kWavesPerGroup, 2, true, true, 0, false, true, &plan_t<4>,
+     &launch_t<8, 4, 2, false>},
 #if GEMM_F32_SWEEP
+    {"skinnyt_m8_j4_u2_tt", 8, kWavesPerGroup, 2, false, true, 0, true, true, &plan_t<4>,
+     &launch_t<8, 4, 2, true>},
+    GEMMF32_SKINNY_T(16, 4, 2),
     GEMMF32_SKINNY_T(8, 8, 2),
     GEMMF32_SKINNY_T(8, 4, 4),
     GEMMF32_SKINNY_T(8, 8, 1),

@@ -106,10 +106,16 @@ constexpr TuningRowSkinny kTuningGfx950Skinny[] = {
     {16, false, false, "skinnyx_w16_c2_u2_s0_vec", 2048},
     {16, false, false, "skinnyx_w8_c2_u2_s0_vec"},
     {16, true, false, "skinnyx_w8_c2_u2_s0_tn"},
+    // B stored N x K: rows of B^T copied into LDS in 256-byte runs and
+    // multiplied on the matrix cores (16 x 8192 x 8192: 50.6 us against
+    // 95.7 us, with A stored transposed 46.1 against 530 us); B^T not 16-byte
+    // aligned: the vector-ALU dot products for M <= 8, 64-byte runs on the
+    // matrix cores above that
+    {16, false, true, "skinnytl_w16_b1_k64_nt"},
     {8, false, true, "skinnyt_m8_j4_u2_nt"},
-    {16, false, true, "skinnyt_m16_j4_u2_nt"},
-    {8, true, true, "skinnyt_m8_j4_u2_tt"},
-    {16, true, true, "skinnyt_m16_j4_u2_tt"},
+    {16, false, true, "skinnytm_w8_j1_u4_nt"},
+    {16, true, true, "skinnytl_w16_b1_k64_tt"},
+    {16, true, true, "skinnytm_w8_j1_u4_tt"},
 };
 
 // K split of the "_sk_" MFMA entries: used only when the tile grid has fewer

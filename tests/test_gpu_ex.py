@@ -72,6 +72,14 @@ def _shapes_for(kname):
         # columns; K split into slices, then too short to split
         mr = 4 * int([t for t in kname.split("_") if t.endswith("x4")][0][1:-2])
         return [(mr - 1, 1004, 2057), (min(mr, 3), 132, 21)]
+    if kname.startswith("skinnytl_"):
+        # B^T's pitch K + 3 a multiple of 4 (copies into LDS need 16-byte
+        # rows); a K % 256 remainder; few columns, so K is split; a short K
+        return [(16, 1003, 2057), (5, 37, 8201), (16, 4100, 333)]
+    if kname.startswith("skinnytm_"):
+        # ragged N and K (a K % 16 tail); few columns, so K is split over
+        # workgroups; M = 16 with many columns and a short K
+        return [(16, 1003, 2057), (5, 37, 8200), (16, 4100, 333)]
     if kname.startswith("skinnyt_m"):
         mr = int(kname.split("_")[1][1:])
         # ragged N and K; the second shape has few columns, so K is split
@@ -94,6 +102,7 @@ def test_every_ex_kernel(gpu_lib, kname):
     # skinnyr kernels need B's pitch a multiple of 4; direct-to-LDS kernels
     # both pitches
     pads = ((3, 4, 7) if kname.startswith("skinnyr_") else
+            (3, 3, 7) if kname.startswith("skinnytl_") else
             (4, 8, 7) if "_d6_" in kname else (3, 5, 7))
     for (M, N, K) in _shapes_for(kname):
         _case(gpu_lib, M, N, K, ta, tb, 2.0, -1.0, True, 7001, kernel=kname, pads=pads)
