@@ -19,8 +19,9 @@ from the 256 MB last-level cache) and reported under "secondary"; each
 secondary measurement first runs its own call untimed for 300 ms, so that
 short kernels are not timed at the idle clocks the host-side work before
 them leaves.  Also under "secondary": 64 batched 512^3 products, the sum of
-2^26 floats, 4096^3 with bias and ReLU, and 4096^3 with an operand stored
-transposed (nt, tn, tt).
+2^26 floats, 4096^3 with bias and ReLU, 4096^3 with an operand stored
+transposed (nt, tn, tt), and the skinny product with B stored transposed
+(8 and 16 rows).
 
 cpu_baseline: the CPU oracle (binary64 triple loop) timed on a bounded sample
 of the same workload (the first R rows of A), scaled to GFLOP/s.
@@ -253,6 +254,39 @@ def transposed_layouts(stream, steps, warmup):
         out[lay] = {"kernel": kname, "ms": round(mean_ms, 4), "TFLOP/s": round(tflops, 2),
                     "frac": round(tflops / PEAK_FP32_MFMA_TFLOPS, 4)}
         del A, B
+    return out
+
+
+def skinny_transposed(stream, steps, warmup, copies=4):
+    """The skinny product with B stored transposed (gemm_f32_ex, N x K), M = 8
+    (the skinny workload's shape) and M = 16: 4 rotating copies of B^T (1 GiB)
+    so it streams from HBM, against 8 TB/s."""
+    import torch
+    from dense_fp32_gemm_f32_amd import binding, inputs
+    ws = inputs.WORKLOADS[inputs.SKINNY]
+    out = {}
+    for M in (8, 16):
+        As, Bs = [], []
+        for c in range(copies):
+            a_cpu, b_cpu = inputs.make_ab(M, ws.N, ws.K, ws.dist_a, ws.dist_b, ws.seed + 100 * c)
+            As.append(a_cpu.cuda())
+            Bs.append(b_cpu.t().contiguous().cuda())
+        Cs = [torch.empty((M, ws.N), device="cuda") for _ in range(copies)]
+        kname = binding.selected_kernel_ex(As[0], Bs[0], Cs[0], trans_b=True)
+        _, per = time_launches(
+            lambda i: binding.gemm_ex(As[i % copies], Bs[i % copies], Cs[i % copies],
+                                      trans_b=True), steps, warmup, stream)
+        mean_ms = sum(per) / len(per)
+        algo = 4.0 * (M * ws.K + ws.K * ws.N + M * ws.N)
+        gbs = algo / (mean_ms * 1e-3) / 1e9
+        out[f"{M}x{ws.N}x{ws.K}_nt"] = {
+            "kernel": kname, "launch_us_mean": round(mean_ms * 1e3, 2),
+            "launch_us_min": round(min(per) * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": traffic_for(kname)}}
+        del As, Bs, Cs
+        torch.cuda.empty_cache()
     return out
 
 
@@ -510,6 +544,8 @@ def main():
                                                                      args.warmup)
         result["secondary"]["transposed_4096"] = transposed_layouts(stream, args.steps,
                                                                     args.warmup)
+        result["secondary"]["skinny_b_transposed"] = skinny_transposed(
+            stream, max(args.steps, 20), args.warmup)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -34,6 +34,10 @@ def main(argv=None):
     ap.add_argument("--settle-ms", type=float, default=0.0,
                     help="before the --reps launches, repeat the same call for this long so the "
                          "clocks leave the idle state (for traces; counter runs leave it 0)")
+    ap.add_argument("--trans-b", action="store_true",
+                    help="B stored transposed (N x K), through gemm_f32_ex")
+    ap.add_argument("--rows", type=int, default=0,
+                    help="use this many rows of A instead of the workload's M")
     ap.add_argument("--reduce", type=int, default=0,
                     help="run reduce_sum_f32 on this many floats (4 copies) instead of a GEMM")
     args = ap.parse_args(argv)
@@ -58,13 +62,14 @@ def main(argv=None):
         _calibration_copy(dev, args.copy_mib)
         return 0
     w = inputs.WORKLOADS[args.workload]
+    M = args.rows or w.M
     copies = args.copies or (4 if 4 * w.K * w.N > 128 * 2 ** 20 else 1)
     As, Bs, Cs = [], [], []
     for c in range(copies):
-        a, b = inputs.make_ab(w.M, w.N, w.K, w.dist_a, w.dist_b, w.seed + 100 * c)
+        a, b = inputs.make_ab(M, w.N, w.K, w.dist_a, w.dist_b, w.seed + 100 * c)
         As.append(a.contiguous().to(dev))
-        Bs.append(b.contiguous().to(dev))
-        Cs.append(torch.empty((w.M, w.N), device=dev))
+        Bs.append((b.t() if args.trans_b else b).contiguous().to(dev))
+        Cs.append(torch.empty((M, w.N), device=dev))
     if args.torch:
         torch.backends.cuda.matmul.allow_tf32 = False
         print(f"workload {w.name}: torch.matmul, {args.reps} launches", flush=True)
@@ -73,13 +78,21 @@ def main(argv=None):
         torch.cuda.synchronize()
         _calibration_copy(dev, args.copy_mib)
         return 0
-    name = args.kernel or binding.selected_kernel(As[0], Bs[0], Cs[0])
-    print(f"workload {w.name}: kernel {name}, {args.reps} launches over {copies} input copies",
-          flush=True)
-    _settle(lambda i: binding.run_kernel(name, As[i % copies], Bs[i % copies], Cs[i % copies]),
-            args.settle_ms)
+    tb = args.trans_b
+    name = args.kernel or (binding.selected_kernel_ex(As[0], Bs[0], Cs[0], trans_b=True) if tb
+                           else binding.selected_kernel(As[0], Bs[0], Cs[0]))
+    print(f"workload {w.name}{' with B stored transposed' if tb else ''}, {M} rows: kernel "
+          f"{name}, {args.reps} launches over {copies} input copies", flush=True)
+
+    def call(i):
+        if tb:
+            binding.gemm_ex(As[i % copies], Bs[i % copies], Cs[i % copies], trans_b=True,
+                            kernel=name)
+        else:
+            binding.run_kernel(name, As[i % copies], Bs[i % copies], Cs[i % copies])
+    _settle(call, args.settle_ms)
     for i in range(args.reps):
-        binding.run_kernel(name, As[i % copies], Bs[i % copies], Cs[i % copies])
+        call(i)
     torch.cuda.synchronize()
     if args.settle_ms > 0:
         _clock(binding)
