@@ -98,15 +98,17 @@ def time_launches(fn, steps, warmup, stream, settle_s=0.3, stats=None):
         n = settle(fn, settle_s)
         if stats is not None:
             stats["settle_calls"] = n
-    for _ in range(warmup):
-        fn(0)
+    # fn(i) takes input copy i % copies: consecutive calls read different
+    # copies, so none finds its inputs in the cache from the call before
+    for i in range(warmup):
+        fn(i)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         evs[i][0].record(stream)
-        fn(i)
+        fn(warmup + i)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps

@@ -421,6 +421,7 @@ std::string select_name(const Op& op, int64_t M, int64_t N, int64_t K, int64_t l
     for (const auto& row : gemmf32::kTuningGfx950Skinny) {
       if (M > row.max_m || row.ta != op.ta || row.tb != op.tb) continue;
       if (row.max_n > 0 && N > row.max_n) continue;
+      if (row.min_k > 0 && K < row.min_k) continue;
       const int idx = find_entry(row.kernel);
       if (idx >= 0 && accepts(entries()[idx], op, M, N, K, lda, ldb, A, B)) return row.kernel;
     }

@@ -48,7 +48,7 @@ def kernel_sources(kernel: str | None = None) -> list[str]:
         files += ["kernels_skinny_rows.hip", "kernels_combine.hip"]
     elif kernel.startswith("skinnyt_"):
         files += ["kernels_skinny_t.hip", "kernels_combine.hip", "mfma_common.h"]
-    elif kernel.startswith(("skinnytl_", "skinnytm_")):
+    elif kernel.startswith(("skinnytl_", "skinnytm_", "skinnytc_")):
         files += ["kernels_skinny_tm.hip", "kernels_combine.hip", "lds_dma.h", "mfma_common.h"]
     elif kernel.startswith("skinny_"):
         files += ["kernels_skinny.hip", "kernels_combine.hip"]

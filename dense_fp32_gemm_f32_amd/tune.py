@@ -7,10 +7,11 @@ tuning table in ``csrc/tuning_gfx950.h`` is chosen from).
 A shape is MxNxK (row-major, packed pitches, 16-byte aligned bases).  Each
 kernel that accepts the shape runs ``--warmup`` times, then ``--reps`` times
 with a HIP event pair on the launch stream around each call, the candidates
-taking turns (after --spin-ms of load to settle the clocks); the median is
-reported.  Inputs rotate over enough copies to exceed the 256 MB last-level
-cache when B is large or the shape is skinny (M <= 16), so bandwidth-bound
-shapes stream from HBM.  Prints one line per (shape, kernel).
+taking turns (after --spin-ms of load to settle the clocks), each timed call
+right after --lead untimed calls of the same kernel; the median is reported.
+Inputs rotate over enough copies to exceed the 256 MB last-level cache when B
+is large or the shape is skinny (M <= 16), so bandwidth-bound shapes stream
+from HBM.  Prints one line per (shape, kernel).
 
 ``--sweep`` loads the sweep build of the library (``python -m
 dense_fp32_gemm_f32_amd.build_lib --sweep``), whose table also holds the
@@ -35,6 +36,8 @@ def main(argv=None):
     ap.add_argument("--filter", default="", help="comma-separated kernel-name prefixes")
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--lead", type=int, default=1,
+                    help="untimed calls of a candidate right before each of its timed calls")
     ap.add_argument("--spin-ms", type=float, default=300.0,
                     help="keep the GPU busy this long before timing a shape")
     ap.add_argument("--json", default="")
@@ -113,26 +116,35 @@ def main(argv=None):
             calls.append((name, call))
         if not calls:
             continue
+        # Every call takes the next copy in rotation, whichever candidate
+        # makes it, so that no call finds its inputs left in the last-level
+        # cache by the call before it (with the same copy for every candidate
+        # of a round, all but the first would read B partly from the cache).
+        seq = iter(range(1 << 62))
         # settle the clocks: keep the GPU busy for --spin-ms before timing
         torch.cuda.synchronize()
         t_end = time.perf_counter() + args.spin_ms * 1e-3
-        i = 0
         while time.perf_counter() < t_end:
             for _, call in calls:
-                call(i)
-            i += 1
+                call(next(seq))
             torch.cuda.synchronize()
         for _, call in calls:
-            for i in range(args.warmup):
-                call(i)
+            for _ in range(args.warmup):
+                call(next(seq))
         torch.cuda.synchronize()
-        # round-robin over the candidates so that clock drift hits all alike
+        # round-robin over the candidates so that clock drift hits all alike;
+        # each timed call follows --lead untimed calls of the same kernel, so
+        # it never runs right after another candidate (a streaming kernel
+        # without the non-temporal hint leaves the caches in a state that
+        # costs the next kernel about 10 us at 16 x 8192 x 8192)
         evs = {name: [] for name, _ in calls}
         for r in range(args.reps):
             for name, call in calls:
+                for _ in range(args.lead):
+                    call(next(seq))
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-                call(r)
+                call(next(seq))
                 b.record(stream)
                 evs[name].append((a, b))
         torch.cuda.synchronize()

@@ -72,7 +72,7 @@ def _shapes_for(kname):
         # columns; K split into slices, then too short to split
         mr = 4 * int([t for t in kname.split("_") if t.endswith("x4")][0][1:-2])
         return [(mr - 1, 1004, 2057), (min(mr, 3), 132, 21)]
-    if kname.startswith("skinnytl_"):
+    if kname.startswith(("skinnytl_", "skinnytc_")):
         # B^T's pitch K + 3 a multiple of 4 (copies into LDS need 16-byte
         # rows); a K % 256 remainder; few columns, so K is split; a short K
         return [(16, 1003, 2057), (5, 37, 8201), (16, 4100, 333)]
@@ -102,7 +102,7 @@ def test_every_ex_kernel(gpu_lib, kname):
     # skinnyr kernels need B's pitch a multiple of 4; direct-to-LDS kernels
     # both pitches
     pads = ((3, 4, 7) if kname.startswith("skinnyr_") else
-            (3, 3, 7) if kname.startswith("skinnytl_") else
+            (3, 3, 7) if kname.startswith(("skinnytl_", "skinnytc_")) else
             (4, 8, 7) if "_d6_" in kname else (3, 5, 7))
     for (M, N, K) in _shapes_for(kname):
         _case(gpu_lib, M, N, K, ta, tb, 2.0, -1.0, True, 7001, kernel=kname, pads=pads)
@@ -187,3 +187,42 @@ def test_ex_full_size(gpu_lib, ta, tb, integer):
     else:
         ratio = H.assert_within_tol(got, C_ref, ABS, what)
         print(f"{what}: max |dC| / scale = {ratio:.3e}")
+
+
+@pytest.mark.parametrize("integer", [False, True])
+@pytest.mark.parametrize("M,ta", [(8, False), (16, False), (16, True)])
+def test_skinny_b_transposed_full_size(gpu_lib, M, ta, integer):
+    """M x 8192 x 8192 with B stored transposed (the skinny shapes bench.py
+    times, on the shared-ring kernel the dispatcher picks for K >= 8192), A
+    stored as is or transposed: every element against the oracle, which runs
+    on the logical operands.  Integer inputs: bit-exact."""
+    N = K = 8192
+    dist = "int2" if integer else "u11"
+    A, B = inputs.make_ab(M, N, K, dist, dist, 7600 + M)
+    H.say(f"ex skinny B^T {M}x{N}x{K} trans_a={int(ta)} int={integer}")
+    Ad = A.t().contiguous().cuda() if ta else A.cuda()
+    Bd = B.t().contiguous().cuda()
+    C = torch.full((M, N), float("nan"), device="cuda")
+    kname = gpu_lib.selected_kernel_ex(Ad, Bd, C, trans_a=ta, trans_b=True)
+    assert kname.startswith("skinnytc_"), kname
+    gpu_lib.gemm_ex(Ad, Bd, C, trans_a=ta, trans_b=True)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy()
+    C_ref, _, ABS = oracle.gemm_ex(A.numpy(), B.numpy())
+    what = f"{kname} {M}x{N}x{K}"
+    if integer:
+        H.assert_bitexact(got, C_ref, what)
+    else:
+        ratio = H.assert_within_tol(got, C_ref, ABS, what)
+        print(f"{what}: max |dC| / scale = {ratio:.3e}")
+
+
+@pytest.mark.parametrize("ta", [False, True])
+@pytest.mark.parametrize("shape", [(16, 1000, 8200), (5, 4100, 8448), (16, 40, 16400)])
+def test_skinny_b_transposed_long_k_dispatch(gpu_lib, ta, shape):
+    """B stored transposed with K >= 8192 through the dispatcher (the ring
+    kernels): ragged N, a K % 256 tail, few columns (K split into slices),
+    with alpha and beta; pitches padded to multiples of 4."""
+    M, N, K = shape
+    _case(gpu_lib, M, N, K, ta, True, -2.0, 3.0, True, 7700 + M, pads=(3, 4, 7))
+    _case(gpu_lib, M, N, K, ta, True, 0.75, 0.0, False, 7800 + M, pads=(3, 4, 7))

@@ -86,7 +86,7 @@ def _shapes_for(kname):
     if kname.startswith("skinnyt_m"):
         mr = int(kname.split("_")[1][1:])
         return [(min(mr, 7), 1003, 2057), (mr, 37, 8200)], (3, 5, 7)
-    if kname.startswith("skinnytl_"):
+    if kname.startswith(("skinnytl_", "skinnytc_")):
         # B^T's pitch K + 3 a multiple of 4 (its rows are copied into LDS)
         return [(13, 1003, 2057), (16, 37, 8201)], (3, 3, 7)
     if kname.startswith("skinny"):

@@ -54,7 +54,7 @@ def _case(kname):
         return 7, 1004, 2057, (3, 4)        # B: N and pitch multiples of 4
     if kname.startswith("skinnyt_"):
         return 7, 1003, 2057, (3, 5)
-    if kname.startswith("skinnytl_"):
+    if kname.startswith(("skinnytl_", "skinnytc_")):
         return 13, 1003, 2057, (3, 3)      # B^T's pitch a multiple of 4
     if kname.startswith("skinnytm_"):
         return 13, 1003, 2057, (3, 5)
