@@ -89,6 +89,8 @@ int mfma_dma_variant_count();      // the direct-to-LDS kernels
 const MfmaVariant& mfma_dma_variant(int i);
 int mfma_small_variant_count();    // fragments from global memory, K split over waves
 const MfmaVariant& mfma_small_variant(int i);
+int mfma_dma_ks_variant_count();   // direct-to-LDS loads, K-tiles shared by wave groups
+const MfmaVariant& mfma_dma_ks_variant(int i);
 
 // ---- MFMA kernel for C = alpha * op(A) op(B) + beta * C ------------------
 // trans_a: A stored K x M (op(A) = A^T); trans_b: B stored N x K.  The
