@@ -131,16 +131,25 @@ def by_launch_shape(d: Path):
     return per
 
 
-def bench_summary(trace: Path, commands, out: Path, skip: int = 0, bench_log: Path | None = None):
+def bench_summary(trace: Path, commands, out: Path, skip: int = 0, bench_log: Path | None = None,
+                  last: int = 0):
     """Markdown table of a bench.py kernel trace, split by launch shape; with
     skip, the first `skip` dispatches of each (kernel, grid) are left out (the
-    warm-up steps), and with bench_log the JSON line the traced run printed is
-    quoted so that its event-timed launch mean can be set beside the trace."""
+    warm-up steps); with last, only the last `last` are kept (the timed steps,
+    after the settle and warm-up calls); with bench_log the JSON line the
+    traced run printed is quoted so that its event-timed launch mean can be set
+    beside the trace."""
     lines = ["# bench.py kernel trace (rocprofv3 --kernel-trace --stats)", "",
              "Command (from the repository root on the MI355X box):", ""]
     lines += [f"    {c}" for c in commands] + [""]
-    what = (f"Dispatches of the run after the first {skip} of each kernel and grid (the "
-            "warm-up steps)" if skip else "Every dispatch of the run, warm-up included")
+    if last:
+        what = (f"The last {last} dispatches of each kernel and grid (the timed steps; the "
+                "settle and warm-up calls come before them)")
+    elif skip:
+        what = (f"Dispatches of the run after the first {skip} of each kernel and grid (the "
+                "warm-up steps)")
+    else:
+        what = "Every dispatch of the run, warm-up included"
     lines += [what + ", grouped by kernel and grid (grid sizes in threads).", "",
               "| kernel | grid | workgroup | calls | avg us | min us | max us |",
               "|---|---|---|---|---|---|---|"]
@@ -148,7 +157,10 @@ def bench_summary(trace: Path, commands, out: Path, skip: int = 0, bench_log: Pa
     for (name, grid, wg), ds in rows:
         if "gemmf32" not in name:
             continue
-        ds = ds[skip:] if len(ds) > skip else ds
+        if last:
+            ds = ds[-last:]
+        elif len(ds) > skip:
+            ds = ds[skip:]
         short = name.replace("gemmf32::(anonymous namespace)::", "").replace("void ", "")
         short = short.split("(")[0]
         lines.append(f"| `{short}` | {grid} | {wg} | {len(ds)} | {sum(ds) / len(ds) / 1e3:.2f} "
@@ -166,6 +178,16 @@ def bench_summary(trace: Path, commands, out: Path, skip: int = 0, bench_log: Pa
                       f"- launch_ms_mean {r.get('launch_ms_mean')}, launch_ms_min "
                       f"{r.get('launch_ms_min')}, achieved {r.get('achieved')} {r.get('unit')} "
                       f"(frac {r.get('frac')})"]
+            t = rec.get("timing") or {}
+            if t:
+                lines.append(f"- settle {t.get('settle_s')} s ({t.get('settle_calls')} calls); "
+                             f"first and last quarter of the timed launches "
+                             f"{t.get('first_quarter_ms_mean')} / {t.get('last_quarter_ms_mean')} ms")
+                for key in ("clock_ghz_before_settle", "clock_ghz_after_timed"):
+                    c = t.get(key)
+                    if c:
+                        lines.append(f"- {key}: median {c.get('median')} (min {c.get('min')}, "
+                                     f"max {c.get('max')})")
     Path(out).write_text("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -196,7 +218,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.bench_trace:
         bench_summary(Path(args.bench_trace), args.command, Path(args.out), args.skip,
-                      Path(args.bench_log) if args.bench_log else None)
+                      Path(args.bench_log) if args.bench_log else None, args.last)
         return
     if not (args.workload and args.kernel and args.match and args.trace):
         ap.error("--workload, --kernel, --match and --trace are required")
