@@ -734,10 +734,11 @@ int reduce_sum_f32(int64_t n, const float* x, float* out, void* stream) {
   if ((rc = check_pointer(out, dev)) != GEMM_F32_OK) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const gemmf32::ReducePlan pl = gemmf32::plan_reduce(n);
-  float* part = nullptr;
-  if (pl.groups > 0 && (rc = get_workspace(dev, s, (size_t)pl.groups, &part)) != GEMM_F32_OK)
+  unsigned long long* slots = nullptr;
+  if (pl.groups > 1 &&
+      (rc = get_exchange_slots(dev, s, (size_t)pl.groups, &slots)) != GEMM_F32_OK)
     return rc;
-  if (gemmf32::launch_reduce_sum(n, x, out, part, s) != hipSuccess) {
+  if (gemmf32::launch_reduce_sum(n, x, out, slots, s) != hipSuccess) {
     (void)hipGetLastError();
     return GEMM_F32_ERR_LAUNCH;
   }

@@ -165,14 +165,18 @@ hipError_t launch_combine(const Problem& p, int slices, const float* partials, h
                           const Epilogue& e = Epilogue{});
 
 // ---- deterministic sum of an fp32 array ------------------------------------
-// Pass 1: `groups` workgroups, group g sums x[g*chunk, min(n, (g+1)*chunk))
-// into part[g]; pass 2 adds the partials into *out.  Both depend on n only.
+// Pass 1: `groups` workgroups, group g sums x[g*chunk, min(n, (g+1)*chunk));
+// pass 2, in group 0 of the same dispatch, adds the partials into *out.  Both
+// depend on n only.
 struct ReducePlan {
-  int groups = 0;      // 0 for n == 0 (pass 2 alone writes +0.0)
+  int groups = 0;      // 0 for n == 0 (a one-thread kernel writes +0.0)
   int64_t chunk = 0;   // elements per group, a multiple of 4
 };
 ReducePlan plan_reduce(int64_t n);
-hipError_t launch_reduce_sum(int64_t n, const float* x, float* out, float* part, hipStream_t s);
+// slots: exchange slots (plan_reduce(n).groups words; may be null for one
+// group), all zero before the launch and left zero by it
+hipError_t launch_reduce_sum(int64_t n, const float* x, float* out, unsigned long long* slots,
+                             hipStream_t s);
 
 // ---- the fixed scratch array of gemm_f32_noalloc (scratch_static.hip) ------
 // Device addresses of this device's copy: the exchange slots (all zero

@@ -13,7 +13,16 @@
 //          non-temporal); then (s0 + s1) + (s2 + s3), a butterfly across the
 //          wave (xor 32, 16, ..., 1: fp addition commutes, so every lane ends
 //          with the same value), and the four waves in LDS in wave order.
-//  pass 2: one group adds the G partials the same way and writes *out.
+//  pass 2: the G partials are added the same way, thread t holding partial
+//          t, and the sum is written to *out.  Group 0 does this at the end of
+//          pass 1, in the same dispatch: every other group posts its partial
+//          as one 64-bit word (a flag in the high half, the value in the low
+//          half) in exchange slot g with a device-scope atomic store, and
+//          thread t of group 0 swaps slot t for zero until it finds the flag,
+//          so the value arrives with the flag and no fence is needed, and
+//          every slot is left empty.  Only group 0 waits, and on groups that
+//          never wait, so the dispatch always completes.  A second dispatch
+//          for the G partials measured 4.5 us on its own.
 //
 // The order of every addition is a function of n alone: with 16-byte aligned
 // x the loads are float4, otherwise four scalar loads of the same elements
@@ -34,6 +43,7 @@ constexpr int kThreads = 256;             // 4 waves
 constexpr int kUnroll = 16;               // float4 loads in flight per thread (16 KiB per wave)
 constexpr int kMaxGroups = 256;           // one per CU of MI355X
 constexpr int64_t kMinPerGroup = 16384;   // elements; smaller arrays use fewer groups
+constexpr int kMaxPolls = 1 << 20;        // group 0's bound on polling one slot
 
 __device__ __forceinline__ float block_sum(float s, float* lds) {
   // butterfly across the wave: after the step with distance d, lanes l and
@@ -53,10 +63,12 @@ __device__ __forceinline__ floatx4 load4(const float* x, int64_t e) {
   return floatx4{x[e], x[e + 1], x[e + 2], x[e + 3]};
 }
 
+// Pass 1 and, in group 0, pass 2 (groups <= kThreads): group g > 0 posts its
+// partial in slots[g]; group 0 collects slots 1 .. groups - 1.
 template <bool VEC>
 __global__ void __launch_bounds__(kThreads)
-    reduce_partial_kernel(const float* __restrict__ x, int64_t n, int64_t chunk,
-                          float* __restrict__ part) {
+    reduce_kernel(const float* __restrict__ x, int64_t n, int64_t chunk,
+                  unsigned long long* __restrict__ slots, float* __restrict__ out) {
   __shared__ float lds[kThreads / 64];
   const int64_t begin = (int64_t)blockIdx.x * chunk;
   const int64_t end = begin + chunk < n ? begin + chunk : n;
@@ -81,17 +93,40 @@ __global__ void __launch_bounds__(kThreads)
   // the last (end - begin) % 4 elements (only the last group has any)
   const int64_t rem = (end - begin) - 4 * n4;
   if (threadIdx.x < rem) acc[0] += xc[4 * n4 + threadIdx.x];
-  const float s = block_sum((acc[0] + acc[1]) + (acc[2] + acc[3]), lds);
-  if (threadIdx.x == 0) part[blockIdx.x] = s;
+  const float part = block_sum((acc[0] + acc[1]) + (acc[2] + acc[3]), lds);
+  if (blockIdx.x != 0) {
+    if (threadIdx.x == 0)
+      __hip_atomic_store(slots + blockIdx.x, (1ull << 32) | __float_as_uint(part),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  // group 0: thread t takes partial t (its own for t = 0), then the same sum
+  // as for any pass-1 thread values
+  float s = 0.f;
+  const int t = threadIdx.x;
+  if (t == 0) {
+    s += part;
+  } else if (t < (int)gridDim.x) {
+    // The other groups never wait, so their partials arrive within the time
+    // of the stream; the bound on polling (about 1-2 s at one atomic round
+    // trip per poll) only guarantees that the dispatch ends, with NaN as the
+    // sum, should a partial never arrive.
+    unsigned long long w = 0;
+    for (int poll = 0; poll < kMaxPolls; ++poll) {
+      w = __hip_atomic_exchange(slots + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((w >> 32) != 0) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    s += (w >> 32) != 0 ? __uint_as_float((unsigned)w) : __builtin_nanf("");
+  }
+  __syncthreads();   // every wave has read lds in the block_sum above
+  s = block_sum(s, lds);
+  if (t == 0) *out = s;
 }
 
-__global__ void __launch_bounds__(kThreads)
-    reduce_final_kernel(const float* __restrict__ part, int groups, float* __restrict__ out) {
-  __shared__ float lds[kThreads / 64];
-  float s = 0.f;
-  for (int i = threadIdx.x; i < groups; i += kThreads) s += part[i];
-  s = block_sum(s, lds);
-  if (threadIdx.x == 0) *out = s;
+// n == 0: the empty sum, +0.
+__global__ void reduce_empty_kernel(float* __restrict__ out) {
+  if (threadIdx.x == 0) *out = 0.f;
 }
 
 }  // namespace
@@ -108,28 +143,25 @@ ReducePlan plan_reduce(int64_t n) {
   return pl;
 }
 
-hipError_t launch_reduce_sum(int64_t n, const float* x, float* out, float* part,
+hipError_t launch_reduce_sum(int64_t n, const float* x, float* out, unsigned long long* slots,
                              hipStream_t s) {
   const ReducePlan pl = plan_reduce(n);
-  if (pl.groups > 0) {
-    if (!part) return hipErrorInvalidValue;
-    const float* xx = x;
-    int64_t nn = n, ch = pl.chunk;
-    float* pp = part;
-    void* args[] = {&xx, &nn, &ch, &pp};
-    const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
-    const hipError_t err = hipLaunchKernel(
-        vec ? reinterpret_cast<const void*>(&reduce_partial_kernel<true>)
-            : reinterpret_cast<const void*>(&reduce_partial_kernel<false>),
-        dim3(pl.groups), dim3(kThreads), args, 0, s);
-    if (err != hipSuccess) return err;
+  if (pl.groups == 0) {
+    float* o = out;
+    void* args[] = {&o};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&reduce_empty_kernel), dim3(1), dim3(64),
+                           args, 0, s);
   }
-  const float* pp = part;
-  int groups = pl.groups;
+  if (pl.groups > kThreads || (pl.groups > 1 && !slots)) return hipErrorInvalidValue;
+  const float* xx = x;
+  int64_t nn = n, ch = pl.chunk;
+  unsigned long long* sl = slots;
   float* o = out;
-  void* args[] = {&pp, &groups, &o};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&reduce_final_kernel), dim3(1),
-                         dim3(kThreads), args, 0, s);
+  void* args[] = {&xx, &nn, &ch, &sl, &o};
+  const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  return hipLaunchKernel(vec ? reinterpret_cast<const void*>(&reduce_kernel<true>)
+                             : reinterpret_cast<const void*>(&reduce_kernel<false>),
+                         dim3(pl.groups), dim3(kThreads), args, 0, s);
 }
 
 }  // namespace gemmf32

@@ -252,9 +252,11 @@ int gemm_f32_ref_gpu(int64_t M, int64_t N, int64_t K,
  * The reduction of "GPU compute shaders" (How it works: one partial sum per
  * workgroup from a grid-stride loop and a shared-memory tree, then the
  * partials combined; the Pitfalls section's fixed group count and order for
- * a reproducible result), measured there on 2^26 values.  Two launches: up to
- * 256 workgroups each sum a contiguous chunk into the workspace, then one
- * workgroup adds those partials and writes *out.  The error is at most about
+ * a reproducible result), measured there on 2^26 values.  One launch: up to
+ * 256 workgroups each sum a contiguous chunk; each hands its partial to
+ * workgroup 0 through a per-stream exchange slot (a flag and the value in one
+ * 64-bit word, written with a device-scope atomic), and workgroup 0 adds the
+ * partials in index order and writes *out.  The error is at most about
  * d 2^-24 sum|x[i]|, with d the depth of the summation tree (276 for n =
  * 2^26; d grows as n / 2^18 beyond that); exact when every partial sum is
  * an integer below 2^24 in magnitude.  n == 0 writes +0.0.  NaN and Inf
@@ -265,7 +267,8 @@ int gemm_f32_ref_gpu(int64_t M, int64_t N, int64_t K,
  * owned.  Errors: n < 0 GEMM_F32_ERR_INVALID_DIM; NULL x (n > 0) or out
  * GEMM_F32_ERR_NULL_PTR; misaligned or unreachable pointers
  * GEMM_F32_ERR_POINTER; out inside x GEMM_F32_ERR_ALIAS; then the device and
- * workspace checks of gemm_f32 (it shares the per-stream workspace).
+ * workspace checks of gemm_f32 (it uses the per-stream exchange slots of the
+ * skinny kernels, which every call leaves clear).
  * Asynchronous on `stream` like gemm_f32.
  */
 int reduce_sum_f32(int64_t n, const float *x, float *out, void *stream);

@@ -100,3 +100,74 @@ def test_sum_special_values(gpu_lib):
     y = x.clone()
     y[10], y[90000] = float("inf"), float("-inf")
     assert np.isnan(_gpu_sum(gpu_lib, _device(y)))
+
+
+def _int_vector(n, seed):
+    x = inputs.int_matrix(1, n, seed).reshape(-1)
+    prefix = np.concatenate([[0], np.cumsum(x.numpy().astype(np.int64))])
+    assert 256 * (prefix.max() - prefix.min()) < 2 ** 24, "pick another seed"
+    return x
+
+
+def test_sum_and_exchange_kernels_share_the_slots(gpu_lib):
+    """The sum's groups hand their partials to group 0 through the per-stream
+    exchange slots that the skinny kernel's K slices also use.  Sums of several
+    sizes and skinny products in turn on one stream: every call must find the
+    slots clear and leave them clear, so every result matches the oracle
+    (integer data: bit-exact)."""
+    s = torch.cuda.Stream()
+    A, B = inputs.make_ab(8, 4096, 4096, "int2", "int2", 9900)
+    C_ref, _, _ = oracle.gemm(A.numpy(), B.numpy())
+    Ad, Bd = A.cuda(), B.cuda()
+    torch.cuda.synchronize()
+    for rep, n in enumerate([N_FULL, 5000, 2 ** 20 + 3, 16385, 2 ** 22]):
+        x = _int_vector(n, 9910 + rep)
+        xd = _device(x)
+        out = torch.full((1,), float("nan"), device="cuda")
+        C = torch.full((8, 4096), float("nan"), device="cuda")
+        H.say(f"reduce and skinny on one stream n={n}")
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            gpu_lib.reduce_sum(xd, out)
+            gpu_lib.run_kernel("skinnyx_w8_c2_u2_s0_vec", Ad, Bd, C)
+            gpu_lib.reduce_sum(xd, out)
+        torch.cuda.synchronize()
+        ref, _, _ = oracle.sum_f32(x.numpy())
+        assert out.cpu().numpy()[0] == ref, f"n={n}"
+        H.assert_bitexact(C.cpu().numpy(), C_ref, f"skinny after reduce n={n}")
+
+
+def test_sum_in_graph_replays(gpu_lib):
+    """reduce_sum_f32 captured into a HIP graph: each replay, with new data
+    copied into the captured input and eager sums of other sizes on the same
+    stream between replays, gives the eager result bit for bit."""
+    n = 2 ** 22
+    s = torch.cuda.Stream()
+    xd = torch.empty(n, device="cuda")
+    out = torch.full((1,), float("nan"), device="cuda")
+    other = _device(_int_vector(70000, 9930))
+    other_out = torch.empty(1, device="cuda")
+    xd.copy_(_int_vector(n, 9940))
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gpu_lib.reduce_sum(xd, out)   # the stream's slots exist before capture
+    torch.cuda.synchronize()
+    H.say("reduce graph capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        gpu_lib.reduce_sum(xd, out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        x = _int_vector(n, 9950 + rep)
+        xd.copy_(x)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        H.say(f"reduce graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()[0]
+        ref, _, _ = oracle.sum_f32(x.numpy())
+        assert got == ref, f"replay {rep}: {got} != {ref}"
+        with torch.cuda.stream(s):
+            gpu_lib.reduce_sum(other, other_out)
+        torch.cuda.synchronize()
