@@ -14,15 +14,24 @@
 // l + 16, l + 32, l + 48 read 64 contiguous bytes of row j0 + l % 16, and
 // each k of the block is used exactly once.
 //
-// Work split: a workgroup of W waves owns JG groups of 16 columns; its waves
-// take the 16-k blocks of the K range in turn (wave w: blocks w, w + W, ...),
-// so at any time the workgroup reads neighbouring blocks of the same rows,
-// U blocks in flight per wave.  The waves' partial tiles are added in LDS in
-// wave order -- the per-group partials and their fixed-order sum of "GPU
-// compute shaders" (How it works; Pitfalls: a fixed group count and order
-// give the same bits on every run).  When the column groups alone leave the
-// GPU short of waves, K is also split over workgroups; the slices then go
-// through the workspace and the combine kernel, added in slice order.
+// Three kernels share this layout and differ in how B^T reaches the lanes:
+//  - skinny_tm_kernel: straight into registers, one 64-byte piece of each of
+//    16 rows per load (any alignment of B^T);
+//  - skinny_tl_kernel: each wave copies its own chunks of 16 rows into LDS
+//    (global_load_lds_dwordx4; 16-byte aligned B^T);
+//  - skinny_tc_kernel: a ring of 16-row chunks in LDS shared by the
+//    workgroup, each copy one whole 1 KiB run of one row (long K).
+//
+// Work split (skinny_tm_kernel): a workgroup of W waves owns JG groups of 16
+// columns; its waves take the 16-k blocks of the K range in turn (wave w:
+// blocks w, w + W, ...), so at any time the workgroup reads neighbouring
+// blocks of the same rows, U blocks in flight per wave.  In every kernel the
+// waves' partial tiles are added in LDS in wave order -- the per-group
+// partials and their fixed-order sum of "GPU compute shaders" (How it works;
+// Pitfalls: a fixed group count and order give the same bits on every run).
+// When the column groups alone leave the GPU short of waves, K is also split
+// over workgroups; the slices then go through the workspace and the combine
+// kernel, added in slice order.
 #include <cstdint>
 #include <type_traits>
 
@@ -376,9 +385,9 @@ __global__ void __launch_bounds__(W * 64)
 // flight while the waves multiply the one that has landed.  Few bytes in
 // flight stream best here: two buffers (one chunk in flight, 32 KiB per CU at
 // two workgroups per CU) take 49.8 us at 16 x 8192 x 8192 with 16 waves,
-// three buffers 55.2 us and four 55.8 us.  Wave w multiplies 16-k blocks w, w + W, ... of every chunk, so the
-// multiply-adds of a chunk are spread over the SIMDs rather than waiting on
-// one wave.  One barrier per chunk: after it the chunk is in LDS and every
+// three buffers 55.2 us and four 55.8 us.  Wave w multiplies 16-k blocks
+// w, w + W, ... of every chunk, so the multiply-adds of a chunk are spread
+// over the SIMDs rather than waiting on one wave.  One barrier per chunk: after it the chunk is in LDS and every
 // wave is done with the previous one, whose buffer then takes the copies of
 // chunk t + NBUF - 1.  The copies of row r fetch 16-byte unit l ^ r for lane
 // l (the swizzle of the kernel above), and the operand of op(A) for a block
