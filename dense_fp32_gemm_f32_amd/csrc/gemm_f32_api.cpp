@@ -317,6 +317,9 @@ bool accepts(const Entry& e, const Op& op, int64_t M, int64_t N, int64_t K, int6
     // A and B as stored; any epilogue
     if (op.ta || op.tb) return false;
     const auto& v = gemmf32::mfma_variant(e.sub);
+    if (v.copy4)
+      return e.kind == Kind::Mfma && K >= 2 * v.bk && (int64_t)v.bm * lda < (INT64_C(1) << 29) &&
+             (int64_t)v.bk * ldb < (INT64_C(1) << 29);
     if (!v.lds_dma) return true;
     return K % v.bk == 0 && lda % 4 == 0 && ldb % 4 == 0 && N % 4 == 0 && aligned16(A) &&
            aligned16(B);

@@ -82,6 +82,10 @@ struct MfmaVariant {
   // e: the update written to C (applied by the combine when K is split)
   hipError_t (*launch)(const Problem&, int slices, int kchunk, float* partials, const Epilogue& e,
                        hipStream_t);
+  // Direct global -> LDS copies of single floats: any pitch and alignment, K
+  // at least two K-tiles, no K split, and 32-bit offsets within a tile
+  // (bm lda and bk ldb below 2^29 floats).
+  bool copy4 = false;
 };
 int mfma_variant_count();          // all three kinds below
 const MfmaVariant& mfma_variant(int i);
@@ -91,6 +95,8 @@ int mfma_small_variant_count();    // fragments from global memory, K split over
 const MfmaVariant& mfma_small_variant(int i);
 int mfma_dma_ks_variant_count();   // direct-to-LDS loads, K-tiles shared by wave groups
 const MfmaVariant& mfma_dma_ks_variant(int i);
+int mfma_d4_variant_count();       // direct-to-LDS copies of single floats, any pitch
+const MfmaVariant& mfma_d4_variant(int i);
 
 // ---- MFMA kernel for C = alpha * op(A) op(B) + beta * C ------------------
 // trans_a: A stored K x M (op(A) = A^T); trans_b: B stored N x K.  The

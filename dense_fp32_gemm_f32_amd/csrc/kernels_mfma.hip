@@ -581,7 +581,7 @@ const MfmaVariant kVariants[] = {
 
 int mfma_variant_count() {
   return (int)(sizeof(kVariants) / sizeof(kVariants[0])) + mfma_dma_variant_count() +
-         mfma_small_variant_count() + mfma_dma_ks_variant_count();
+         mfma_small_variant_count() + mfma_dma_ks_variant_count() + mfma_d4_variant_count();
 }
 const MfmaVariant& mfma_variant(int i) {
   const int n = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
@@ -590,7 +590,9 @@ const MfmaVariant& mfma_variant(int i) {
   if (i < mfma_dma_variant_count()) return mfma_dma_variant(i);
   i -= mfma_dma_variant_count();
   if (i < mfma_small_variant_count()) return mfma_small_variant(i);
-  return mfma_dma_ks_variant(i - mfma_small_variant_count());
+  i -= mfma_small_variant_count();
+  if (i < mfma_dma_ks_variant_count()) return mfma_dma_ks_variant(i);
+  return mfma_d4_variant(i - mfma_dma_ks_variant_count());
 }
 
 }  // namespace gemmf32

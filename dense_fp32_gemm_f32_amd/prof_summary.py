@@ -40,8 +40,15 @@ def kernel_sources(kernel: str | None = None) -> list[str]:
         files += (["kernels_mfma_ex_dma.hip", "lds_dma.h"] if "_d6_" in kernel else
                   ["kernels_mfma_ex.hip"]) + ["mfma_common.h"]
     elif kernel.startswith("mfma_"):
-        files += (["kernels_mfma_dma.hip", "lds_dma.h"] if "_d6_" in kernel else
-                  ["kernels_mfma.hip"]) + ["mfma_common.h"]
+        if "_d4_" in kernel:
+            files += ["kernels_mfma_dma4.hip"]
+        elif "_kw" in kernel:
+            files += ["kernels_mfma_dma_ks.hip", "lds_dma.h"]
+        elif "_d6_" in kernel:
+            files += ["kernels_mfma_dma.hip", "lds_dma.h"]
+        else:
+            files += ["kernels_mfma.hip"]
+        files += ["mfma_common.h"]
         if "_sk_" in kernel:
             files.append("kernels_combine.hip")
     elif kernel.startswith("skinnyr_"):

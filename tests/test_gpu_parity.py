@@ -87,6 +87,10 @@ def _kernel_case(name):
         return _skinnyr_rows(name) - 1, 1004, 2057, 2058, 1008
     if name.startswith("skinny"):
         M, N, K = 13, 1000 + 3, 2050 + 7
+    elif "_d4_" in name:
+        # single-float direct copies: odd pitches, ragged M, N and K (K % 32
+        # != 0: a padded first K-tile)
+        return 301, 263, 139, 141, 265
     elif "_d6_" in name:
         # direct-to-LDS loads: N, K, lda, ldb multiples of 4 (K of 64), ragged M
         # and N edges; with "_sk_", a last K slice shorter than the others
@@ -131,6 +135,10 @@ def test_every_kernel_variant(gpu_lib, kname):
     if kname.startswith("skinnyr_"):
         # K too short to split: one slice, written straight to C
         cases.append((M, N, 21, 24, ldb))
+    if "_d4_" in kname:
+        # K a multiple of the K-tile (no padded first tile), the shortest K
+        # taken, odd pitches
+        cases += [(130, 70, 96, 97, 73), (67, 200, 64, 67, 201)]
     for (M, N, K, lda, ldb), integer in [(c, i) for c in cases for i in (True, False)]:
         dist = "int2" if integer else "u11"
         A, B = inputs.make_ab(M, N, K, dist, dist, 3001 + integer, lda=lda, ldb=ldb)
