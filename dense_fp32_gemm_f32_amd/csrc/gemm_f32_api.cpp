@@ -47,9 +47,11 @@ const std::vector<Entry>& entries() {
     for (int i = 0; i < gemmf32::mfma_variant_count(); ++i)
       t.push_back({Kind::Mfma, i, gemmf32::mfma_variant(i).name});
 #if GEMM_F32_SWEEP
-    // K-split twins: the tuning table picks none of them
+    // K-split twins: the tuning table picks none of them (none for the
+    // single-float copy tiles, which take no K split)
     for (int i = 0; i < gemmf32::mfma_variant_count(); ++i)
-      t.push_back({Kind::MfmaSplitK, i, split_k_name(gemmf32::mfma_variant(i).name)});
+      if (!gemmf32::mfma_variant(i).copy4)
+        t.push_back({Kind::MfmaSplitK, i, split_k_name(gemmf32::mfma_variant(i).name)});
 #endif
     for (int i = 0; i < gemmf32::mfma_ex_variant_count(); ++i)
       t.push_back({Kind::MfmaEx, i, gemmf32::mfma_ex_variant(i).name});

@@ -350,6 +350,7 @@ const MfmaVariant kD4Variants[] = {
     GEMMF32_MFMA_D4(128, 128, 32, 64, 64, 2),
     GEMMF32_MFMA_D4(128, 64, 32, 64, 32, 3),
     GEMMF32_MFMA_D4(64, 128, 32, 32, 64, 3),
+    GEMMF32_MFMA_D4(64, 64, 64, 32, 32, 4),
 #endif
 };
 

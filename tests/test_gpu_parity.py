@@ -137,8 +137,9 @@ def test_every_kernel_variant(gpu_lib, kname):
         cases.append((M, N, 21, 24, ldb))
     if "_d4_" in kname:
         # K a multiple of the K-tile (no padded first tile), the shortest K
-        # taken, odd pitches
-        cases += [(130, 70, 96, 97, 73), (67, 200, 64, 67, 201)]
+        # taken (two K-tiles), odd pitches
+        bk = int(kname.split("_")[1].split("x")[2])
+        cases += [(130, 70, 3 * bk, 3 * bk + 1, 73), (67, 200, 2 * bk, 2 * bk + 3, 201)]
     for (M, N, K, lda, ldb), integer in [(c, i) for c in cases for i in (True, False)]:
         dist = "int2" if integer else "u11"
         A, B = inputs.make_ab(M, N, K, dist, dist, 3001 + integer, lda=lda, ldb=ldb)
