@@ -340,9 +340,13 @@ hipError_t launch_d4(const Problem& p, int slices, int kchunk, float* partials, 
 // The default build holds the tiles the tuning table can pick; a build with
 // GEMM_F32_SWEEP also holds the ones tuning sweeps compared them with.
 const MfmaVariant kD4Variants[] = {
-    // 64 x 64: the fastest with these copies at every unaligned shape tried,
-    // from 767 x 769 x 771 to 4096 x 4097 x 4096
+    // 64 x 64: the fastest tile with these copies at every unaligned shape
+    // tried, from 767 x 769 x 771 to 4096 x 4097 x 4096; BK = 16 (16 KiB of
+    // LDS, up to 7 waves per SIMD) for the larger grids (2047 x 3001 x 1531:
+    // 150.3 against 152.9 us; 4095^3: 1030 against 1052 us), BK = 32 below
+    // (1023 x 1025 x 1027: 42.6 against 43.8 us)
     GEMMF32_MFMA_D4(64, 64, 32, 32, 32, 4),
+    GEMMF32_MFMA_D4(64, 64, 16, 32, 32, 6),
 #if GEMM_F32_SWEEP
     GEMMF32_MFMA_D4(128, 192, 32, 32, 96, 2),
     GEMMF32_MFMA_D4(192, 128, 32, 96, 32, 2),

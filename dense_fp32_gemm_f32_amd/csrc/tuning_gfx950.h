@@ -50,11 +50,11 @@ constexpr TuningRow kTuningGfx950[] = {
     {kAnyM, 768, "mfma_128x256x16_w64x128_d6_vec"},
     // operands the 16-byte direct loads cannot take (pitches or N not
     // multiples of 4, K not a multiple of the K-tile): 64 x 64 tiles copied
-    // into LDS one float per lane (4095^3: 1036 us against 1063 us staged
+    // into LDS one float per lane (4095^3: 1030 us against 1063 us staged
     // through registers; 4096 x 4097 x 4096: 1070 us against 1158 us for the
     // best larger tile); then the register-staged tile whose grid fills its
     // waves (K below two K-tiles, or pitches beyond 32-bit tile offsets)
-    {kAnyM, 768, "mfma_64x64x32_w32x32_d4_vec"},
+    {kAnyM, 768, "mfma_64x64x16_w32x32_d4_vec"},
     {kAnyM, 768, "mfma_128x128x32_w64x64_p5_vec", 2},
     // 128 x 192 or 192 x 128 tiles where one per CU makes whole waves
     // (2048 x 3072 x 1536: 148 us against 192 us for 128 x 128 tiles)
@@ -65,10 +65,10 @@ constexpr TuningRow kTuningGfx950[] = {
     {kAnyM, 192, "mfma_128x128x32_w64x32_d6_vec"},
     {kAnyM, 192, "mfma_128x128x16_w64x64_d6_vec"},
     // unaligned operands: single-float direct copies (2047 x 3001 x 1531:
-    // 156.4 us against 166.0 us for the register-staged 128 x 192 tile;
+    // 150.3 us against 166.0 us for the register-staged 128 x 192 tile;
     // 2048 x 2048 x 2047: 139.3 against 148.3 us), then 128 x 192 or 192 x
     // 128 register-staged tiles of 8 waves where they make whole waves
-    {kAnyM, 192, "mfma_64x64x32_w32x32_d4_vec"},
+    {kAnyM, 192, "mfma_64x64x16_w32x32_d4_vec"},
     {kAnyM, 192, "mfma_128x192x32_w32x96_p5_vec", 1},
     {kAnyM, 192, "mfma_192x128x32_w96x32_p5_vec", 1},
     {kAnyM, 192, "mfma_64x64x32_w32x32_p5_vec"},

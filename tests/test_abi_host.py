@@ -120,20 +120,22 @@ def test_adjacent_but_not_overlapping_is_not_alias():
     (6144, 6144, 4096, 4096, 6144, P16, Q16, "mfma_128x256x16_w64x128_d6"),
     # operands the 16-byte direct loads cannot take: 64 x 64 tiles copied
     # into LDS one float per lane
-    (4096, 4097, 4096, 4096, 4097, P16, Q16, "mfma_64x64x32_w32x32_d4"),
-    (8191, 8191, 2001, 2001, 8191, P16, Q16, "mfma_64x64x32_w32x32_d4"),
-    (2047, 3001, 1531, 1531, 3001, P16, Q16, "mfma_64x64x32_w32x32_d4"),
-    (3001, 2047, 1531, 1531, 2047, P16, Q16, "mfma_64x64x32_w32x32_d4"),
+    (4096, 4097, 4096, 4096, 4097, P16, Q16, "mfma_64x64x16_w32x32_d4"),
+    (8191, 8191, 2001, 2001, 8191, P16, Q16, "mfma_64x64x16_w32x32_d4"),
+    (2047, 3001, 1531, 1531, 3001, P16, Q16, "mfma_64x64x16_w32x32_d4"),
+    (3001, 2047, 1531, 1531, 2047, P16, Q16, "mfma_64x64x16_w32x32_d4"),
+    (2047, 3001, 32, 32, 3001, P16, Q16, "mfma_64x64x16_w32x32_d4"),
     (767, 769, 771, 771, 769, P16, Q16, "mfma_64x64x32_w32x32_d4"),
     # ... unless K is below two K-tiles or a tile's offsets exceed 32 bits:
     # the register-staged tile whose grid leaves its last wave at least 90 %
     # full (or makes 4+ waves)
-    (4096, 4097, 63, 63, 4097, P16, Q16, "mfma_128x192x32_w32x96_p5"),      # 704 of 768
-    (8191, 8191, 63, 63, 8191, P16, Q16, "mfma_128x128x32_w64x64_p5"),      # 8 waves of 512
+    (4096, 4097, 31, 31, 4097, P16, Q16, "mfma_128x192x32_w32x96_p5"),      # 704 of 768
+    (8191, 8191, 31, 31, 8191, P16, Q16, "mfma_128x128x32_w64x64_p5"),      # 8 waves of 512
     (6001, 6001, 999, 2 ** 23 + 1, 6001, P16, Q16, "mfma_128x128x32_w64x64_p5"),  # 4.3 waves
-    (2047, 3001, 63, 63, 3001, P16, Q16, "mfma_128x192x32_w32x96_p5"),      # 256 tiles
-    (3001, 2047, 63, 63, 2047, P16, Q16, "mfma_192x128x32_w96x32_p5"),      # 256 tiles
-    (2049, 2049, 63, 63, 2049, P16, Q16, "mfma_64x64x32_w32x32_p5"),        # 187 of 256
+    (2047, 3001, 31, 31, 3001, P16, Q16, "mfma_128x192x32_w32x96_p5"),      # 256 tiles
+    (3001, 2047, 31, 31, 2047, P16, Q16, "mfma_192x128x32_w96x32_p5"),      # 256 tiles
+    (2049, 2049, 31, 31, 2049, P16, Q16, "mfma_64x64x32_w32x32_p5"),        # 187 of 256
+    (767, 769, 63, 63, 769, P16, Q16, "mfma_64x64x32_w32x32_p5"),
     (7936, 7936, 4096, 4096, 7936, P16, Q16, "mfma_256x256x32_w64x128_d6"),  # 961 of 1024
     # aligned operands: 128 x 192 (or 192 x 128) direct-to-LDS tiles where one
     # per CU fills whole waves, else 128 x 128
