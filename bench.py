@@ -116,9 +116,10 @@ def time_launches(fn, steps, warmup, stream, settle_s=0.3, stats=None):
     return wall, per
 
 
-def profile_record(kernel_name: str):
+def profile_record(kernel_name: str, workload: str):
     """The committed rocprofv3 record of a kernel (profiles/traffic.json), or
-    None if there is none or it was taken on a different kernel source."""
+    None if there is none, it was taken on another workload, or on a
+    different kernel source."""
     f = ROOT / "profiles" / "traffic.json"
     if not f.exists():
         return None
@@ -127,15 +128,18 @@ def profile_record(kernel_name: str):
     except ValueError:
         return None
     from dense_fp32_gemm_f32_amd.prof_summary import source_hash
-    if not rec or rec.get("source_sha256") != source_hash(kernel_name):
+    if not rec or rec.get("workload") != workload:
+        return None
+    if rec.get("source_sha256") != source_hash(kernel_name):
         return None
     return rec
 
 
-def traffic_for(kernel_name: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if it was taken on a different kernel source."""
-    rec = profile_record(kernel_name)
+def traffic_for(kernel_name: str, workload: str):
+    """HBM bytes per launch of the kernel on this workload from the committed
+    rocprofv3 counter summary, or None if there is no such summary or it was
+    taken on a different kernel source."""
+    rec = profile_record(kernel_name, workload)
     return rec.get("hbm_bytes_per_launch") if rec else None
 
 
@@ -286,7 +290,7 @@ def skinny_transposed(stream, steps, warmup, copies=4):
             "launch_us_min": round(min(per) * 1e3, 2),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": traffic_for(kname)}}
+                         "traffic": traffic_for(kname, f"skinny_{M}x{ws.N}x{ws.K}_bt")}}
         del As, Bs, Cs
         torch.cuda.empty_cache()
     return out
@@ -336,10 +340,11 @@ def cpu_baseline_config(w, C_gpu, C_gpu_int):
             "max_err_ratio": ratio, "int_bitexact": bool(np.array_equal(C_gpu_int, Ci_ref))}
 
 
-def _rocprof_fields(kname):
-    """The committed profile summary of the kernel and its calibrated HBM
-    bytes per launch against the algorithmic bytes (None if stale)."""
-    rec = profile_record(kname)
+def _rocprof_fields(kname, workload):
+    """The committed profile summary of the kernel on this workload and its
+    calibrated HBM bytes per launch against the algorithmic bytes (None if
+    there is none or it is stale)."""
+    rec = profile_record(kname, workload)
     if not rec:
         return None
     return {"summary": "profiles/" + rec["summary"], "workload": rec["workload"],
@@ -408,8 +413,8 @@ def per_config(args, workloads, share_of=None):
                "gbps": round(w.algo_bytes / (t_med * 1e-3) / 1e9, 1),
                "pct_hbm_peak": round(100 * w.algo_bytes / (t_med * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
                "repro_bitexact": bool(torch.equal(C1, C2)),
-               "traffic": traffic_for(kname) if share_of is None else None,
-               "rocprof": _rocprof_fields(kname) if share_of is None else None,
+               "traffic": traffic_for(kname, name) if share_of is None else None,
+               "rocprof": _rocprof_fields(kname, name) if share_of is None else None,
                "device": {"name": props.name, "CUs": props.multi_processor_count,
                           "arch": getattr(props, "gcnArchName", ""),
                           "peak_tflops": PEAK_FP32_MFMA_TFLOPS,
@@ -468,7 +473,7 @@ def main():
     flops = w.flops
     value = flops / (wall_ms * 1e-3) / 1e9
     achieved_tflops = flops / (mean_launch_ms * 1e-3) / 1e12
-    traffic = traffic_for(kname)
+    traffic = traffic_for(kname, w.name)
     result = {
         "metric": "fp32 GEMM GFLOP/s (2MNK/t) at 4096^3 and % of MI355X fp32 MFMA peak",
         "value": round(value, 1),
@@ -533,7 +538,7 @@ def main():
             "GFLOP/s": round(ws.flops / (mean_s * 1e-3) / 1e9, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": traffic_for(sk)}}}
+                         "traffic": traffic_for(sk, ws.name)}}}
         del As, Bs, Cs
         torch.cuda.empty_cache()
 

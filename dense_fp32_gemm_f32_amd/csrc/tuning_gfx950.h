@@ -119,17 +119,19 @@ constexpr TuningRowSkinny kTuningGfx950Skinny[] = {
     {16, true, false, "skinnyx_w8_c2_u2_s0_tn"},
     // B stored N x K, 16-byte aligned rows: for K >= 8192 a ring of 16-row
     // chunks shared by the workgroup with one chunk in flight (16 x 8192 x
-    // 8192: 45.0 us, A stored transposed 46.4 us; 8 waves up to N = 8192,
-    // 16 waves above: 16 x 16384 x 8192 93.6 against 101.8 us); shorter K:
-    // each wave copies its own chunks (16 x 8192 x 4096: 30.0 against
-    // 53.2 us).  B^T not 16-byte aligned: the vector-ALU dot products for
-    // M <= 8, 64-byte runs on the matrix cores above that.
-    {16, false, true, "skinnytc_w8_n2_nt", 8192, 8192},
+    // 8192: 45.0 us, A stored transposed 46.4 us); 8 waves for M <= 8 up to
+    // N = 8192 (8 x 8192 x 8192 timed back to back: 46.2 against 48.7 us),
+    // 16 waves otherwise (16 x 8192 x 8192: 49.0 against 49.6 us; 16 x
+    // 16384 x 8192: 93.6 against 101.8 us); shorter K: each wave copies its
+    // own chunks (16 x 8192 x 4096: 30.0 against 53.2 us).  B^T not 16-byte
+    // aligned: the vector-ALU dot products for M <= 8, 64-byte runs on the
+    // matrix cores above that.
+    {8, false, true, "skinnytc_w8_n2_nt", 8192, 8192},
     {16, false, true, "skinnytc_w16_n2_nt", 0, 8192},
     {16, false, true, "skinnytl_w16_b1_k64_nt"},
     {8, false, true, "skinnyt_m8_j4_u2_nt"},
     {16, false, true, "skinnytm_w8_j1_u4_nt"},
-    {16, true, true, "skinnytc_w8_n2_tt", 8192, 8192},
+    {8, true, true, "skinnytc_w8_n2_tt", 8192, 8192},
     {16, true, true, "skinnytc_w16_n2_tt", 0, 8192},
     {16, true, true, "skinnytl_w16_b1_k64_tt"},
     {16, true, true, "skinnytm_w8_j1_u4_tt"},

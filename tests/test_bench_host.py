@@ -40,14 +40,16 @@ def test_traffic_is_reported_only_for_matching_sources(tmp_path, monkeypatch):
     # a figure is reported exactly when its recorded hash matches the sources
     for k, v in rec.items():
         want = v["hbm_bytes_per_launch"] if v["source_sha256"] == source_hash(k) else None
-        assert bench.traffic_for(k) == want
+        assert bench.traffic_for(k, v["workload"]) == want
+        # nor is a figure reported for another workload of the same kernel
+        assert bench.traffic_for(k, v["workload"] + "_other") is None
     # a figure taken on other sources is not reported
     fake = tmp_path / "profiles"
     fake.mkdir()
     (fake / "traffic.json").write_text(json.dumps({name: dict(entry, source_sha256="0" * 64)}))
     monkeypatch.setattr(bench, "ROOT", tmp_path)
-    assert bench.traffic_for(name) is None
-    assert bench.traffic_for("no_such_kernel") is None
+    assert bench.traffic_for(name, entry["workload"]) is None
+    assert bench.traffic_for("no_such_kernel", entry["workload"]) is None
 
 
 @pytest.mark.parametrize("name", list(inputs.SHARDS))

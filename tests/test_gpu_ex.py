@@ -224,12 +224,12 @@ def test_skinny_b_transposed_long_k_dispatch(gpu_lib, ta, shape):
     """B stored transposed with K >= 8192 through the dispatcher (the ring
     kernels, 16 waves above N = 8192): ragged N, a K % 256 tail, few columns
     (K split into slices), with alpha and beta; pitches padded to multiples
-    of 4."""
+    of 4.  8 waves for M <= 8 up to N = 8192, else 16."""
     M, N, K = shape
     A, B = inputs.make_ab(M, N, K, "int2", "int2", 7650)
     As = (A.t().contiguous() if ta else A).cuda()
     Bs = H.to_device(_stored(B, True, 4))
     kname = gpu_lib.selected_kernel_ex(As, Bs, trans_a=ta, trans_b=True)
-    assert kname.startswith("skinnytc_w16" if N > 8192 else "skinnytc_w8"), kname
+    assert kname.startswith("skinnytc_w16" if N > 8192 or M > 8 else "skinnytc_w8"), kname
     _case(gpu_lib, M, N, K, ta, True, -2.0, 3.0, True, 7700 + M, pads=(3, 4, 7))
     _case(gpu_lib, M, N, K, ta, True, 0.75, 0.0, False, 7800 + M, pads=(3, 4, 7))
