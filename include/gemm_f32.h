@@ -256,7 +256,13 @@ int gemm_f32_ref_gpu(int64_t M, int64_t N, int64_t K,
  * 256 workgroups each sum a contiguous chunk; each hands its partial to
  * workgroup 0 through a per-stream exchange slot (a flag and the value in one
  * 64-bit word, written with a device-scope atomic), and workgroup 0 adds the
- * partials in index order and writes *out.  The error is at most about
+ * partials in index order and writes *out.  Workgroup 0 waits only on
+ * workgroups that never wait, so the launch always completes; should a
+ * partial still be missing after about 2^20 polls of its slot (seconds, so
+ * only a GPU held by other work that long could cause it), *out is NaN and
+ * the late partial may be left in its slot: then call
+ * gemm_f32_release_workspaces before the next call on that stream, which
+ * would otherwise read it.  The error is at most about
  * d 2^-24 sum|x[i]|, with d the depth of the summation tree (276 for n =
  * 2^26; d grows as n / 2^18 beyond that); exact when every partial sum is
  * an integer below 2^24 in magnitude.  n == 0 writes +0.0.  NaN and Inf
