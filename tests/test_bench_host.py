@@ -65,3 +65,14 @@ def test_shard_is_one_share_of_its_workload(name):
     if w.dist_b == "u_inv_sqrt_k":
         assert s.K == w.K
     assert s.flops * ways == w.flops
+
+
+def test_every_traffic_record_has_its_summary():
+    """Each recorded traffic figure belongs to a committed profile summary of
+    the same kernel on the same workload (no record outlives its summary)."""
+    rec = json.loads((ROOT / "profiles" / "traffic.json").read_text())
+    for kernel, v in rec.items():
+        summary = ROOT / "profiles" / v["summary"]
+        assert summary.exists(), (kernel, v["summary"])
+        first = summary.read_text().splitlines()[0]
+        assert first == f"# {kernel} on {v['workload']}", (kernel, first)
