@@ -20,7 +20,11 @@
 #include <vector>
 
 #include "gemm_f32_internal.h"
+#include "stamps.h"
 #include "tuning_gfx950.h"
+#if GEMM_F32_SWEEP
+#include "../../include/gemm_f32_sweep.h"
+#endif
 
 using gemmf32::Problem;
 
@@ -873,5 +877,38 @@ int gemm_f32_release_workspaces(void) {
   if (have_cur) (void)hipSetDevice(cur);
   return rc;
 }
+
+#if GEMM_F32_SWEEP
+int gemm_f32_stamped(int index, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                     const float* B, int64_t ldb, float* C, int64_t ldc,
+                     unsigned long long* stamps, int64_t stamp_words, void* stream) {
+  const auto& t = entries();
+  if (index < 0 || index >= (int)t.size() || t[index].kind != Kind::Mfma)
+    return GEMM_F32_ERR_BAD_KERNEL;
+  // the entry's tile among the direct-to-LDS ones
+  int tile = -1;
+  for (int i = 0; i < gemmf32::mfma_dma_variant_count(); ++i)
+    if (t[index].name == gemmf32::mfma_dma_variant(i).name) tile = i;
+  if (tile < 0) return GEMM_F32_ERR_BAD_KERNEL;
+  const Op op;
+  Prepared r = prepare(op, M, N, K, A, lda, B, ldb, C, ldc);
+  if (r.status != GEMM_F32_OK) return r.status;
+  if (M == 0 || N == 0 || K == 0 || !entry_accepts(t[index], op, r.p))
+    return GEMM_F32_ERR_BAD_KERNEL;
+  const auto& v = gemmf32::mfma_dma_variant(tile);
+  const int64_t tiles = ((M + v.bm - 1) / v.bm) * ((N + v.bn - 1) / v.bn);
+  if (!stamps) return GEMM_F32_ERR_NULL_PTR;
+  if (((uintptr_t)stamps & 7u) != 0) return GEMM_F32_ERR_POINTER;
+  if (stamp_words < 6 * tiles) return GEMM_F32_ERR_INVALID_DIM;
+  int rc = check_pointer(stamps, r.dev);
+  if (rc != GEMM_F32_OK) return rc;
+  if (gemmf32::launch_dma_stamped(tile, r.p, op.epilogue(), stamps, stamp_words,
+                                  static_cast<hipStream_t>(stream)) != hipSuccess) {
+    (void)hipGetLastError();
+    return GEMM_F32_ERR_LAUNCH;
+  }
+  return GEMM_F32_OK;
+}
+#endif
 
 }  // extern "C"

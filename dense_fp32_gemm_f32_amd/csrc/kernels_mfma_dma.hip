@@ -24,6 +24,7 @@
 #include "gemm_f32_internal.h"
 #include "lds_dma.h"
 #include "mfma_common.h"
+#include "stamps.h"
 
 namespace gemmf32 {
 namespace {
@@ -169,16 +170,24 @@ __device__ __forceinline__ void dma_k_loop(float* lds_a0, float* lds_b0, float* 
   if constexpr (kDual) acc[0][0] += acc_odd;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int kMinWaves>
-__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
-    __attribute__((amdgpu_waves_per_eu(kMinWaves)))
-    mfma_dma_kernel(Problem p, int tiles_m, int tiles_n, int kchunk, float* part, Epilogue ep) {
+// One workgroup's tile.  With kStamp (the instrumented kernel of the sweep
+// build), thread 0 also writes six 64-bit words to stamps[6 w ..] for
+// workgroup w: the constant 100 MHz counter (s_memrealtime) at the start,
+// after the K loop and after the C stores, then the shader cycle counter
+// (s_memtime) at the same three points.  Barriers before the second and third
+// readings make them cover every wave, and the third waits for the stores.
+template <int BM, int BN, int BK, int WM, int WN, bool kStamp>
+__device__ __forceinline__ void dma_tile(float* lds_a0, float* lds_a1, float* lds_b0,
+                                         float* lds_b1, Problem p, int tiles_m, int tiles_n,
+                                         int kchunk, float* part, const Epilogue& ep,
+                                         unsigned long long* stamps) {
   using C_ = Cfg<BM, BN, BK, WM, WN>;
   constexpr int kWaves = C_::kThreads / 64;
-  __shared__ __attribute__((aligned(16))) float lds_a0[C_::kLdsA];
-  __shared__ __attribute__((aligned(16))) float lds_a1[C_::kLdsA];
-  __shared__ __attribute__((aligned(16))) float lds_b0[C_::kLdsB];
-  __shared__ __attribute__((aligned(16))) float lds_b1[C_::kLdsB];
+  unsigned long long rt[3] = {}, mt[3] = {};
+  if constexpr (kStamp) {
+    rt[0] = __builtin_amdgcn_s_memrealtime();
+    mt[0] = __builtin_amdgcn_s_memtime();
+  }
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -233,11 +242,43 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 
   dma_k_loop<BM, BN, BK, WM, WN>(lds_a0, lds_b0, lds_a1, lds_b1, a_src, b_src, p.ldb, wave, lane,
                                  K / BK, acc);
+  if constexpr (kStamp) {
+    __syncthreads();
+    rt[1] = __builtin_amdgcn_s_memrealtime();
+    mt[1] = __builtin_amdgcn_s_memtime();
+  }
 
   // ---- masked epilogue ------------------------------------------------------
   store_blocks<C_::kFragM, C_::kFragN>(acc, p.C, p.ldc, M, N, m0 + (wave % C_::kWavesM) * WM,
                                        n0 + (wave / C_::kWavesM) * WN, lane, part != nullptr,
                                        ep);
+  if constexpr (kStamp) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    rt[2] = __builtin_amdgcn_s_memrealtime();
+    mt[2] = __builtin_amdgcn_s_memtime();
+    if (tid == 0) {
+      unsigned long long* w = stamps + 6 * (size_t)blockIdx.x;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        w[i] = rt[i];
+        w[3 + i] = mt[i];
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int kMinWaves>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+    __attribute__((amdgpu_waves_per_eu(kMinWaves)))
+    mfma_dma_kernel(Problem p, int tiles_m, int tiles_n, int kchunk, float* part, Epilogue ep) {
+  using C_ = Cfg<BM, BN, BK, WM, WN>;
+  __shared__ __attribute__((aligned(16))) float lds_a0[C_::kLdsA];
+  __shared__ __attribute__((aligned(16))) float lds_a1[C_::kLdsA];
+  __shared__ __attribute__((aligned(16))) float lds_b0[C_::kLdsB];
+  __shared__ __attribute__((aligned(16))) float lds_b1[C_::kLdsB];
+  dma_tile<BM, BN, BK, WM, WN, false>(lds_a0, lds_a1, lds_b0, lds_b1, p, tiles_m, tiles_n, kchunk,
+                                      part, ep, nullptr);
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int kMinWaves>
@@ -272,37 +313,101 @@ hipError_t launch_dma(const Problem& p, int slices, int kchunk, float* partials,
   return launch_combine(p, slices, partials, s, e);
 }
 
+#if GEMM_F32_SWEEP
+// The same tile with per-workgroup timestamps (whole K, one product).
+template <int BM, int BN, int BK, int WM, int WN, int kMinWaves>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+    __attribute__((amdgpu_waves_per_eu(kMinWaves)))
+    mfma_dma_stamp_kernel(Problem p, int tiles_m, int tiles_n, Epilogue ep,
+                          unsigned long long* stamps) {
+  using C_ = Cfg<BM, BN, BK, WM, WN>;
+  __shared__ __attribute__((aligned(16))) float lds_a0[C_::kLdsA];
+  __shared__ __attribute__((aligned(16))) float lds_a1[C_::kLdsA];
+  __shared__ __attribute__((aligned(16))) float lds_b0[C_::kLdsB];
+  __shared__ __attribute__((aligned(16))) float lds_b1[C_::kLdsB];
+  dma_tile<BM, BN, BK, WM, WN, true>(lds_a0, lds_a1, lds_b0, lds_b1, p, tiles_m, tiles_n, p.K,
+                                     nullptr, ep, stamps);
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int kMinWaves>
+hipError_t launch_dma_stamp(const Problem& p, const Epilogue& e, unsigned long long* stamps,
+                            int64_t words, hipStream_t s) {
+  using C_ = Cfg<BM, BN, BK, WM, WN>;
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int64_t tiles = (int64_t)tiles_m * tiles_n;
+  if (tiles > 0x7fffffff || p.batch != 1 || !stamps || words < 6 * tiles)
+    return hipErrorInvalidConfiguration;
+  if (p.K % BK != 0 || p.lda % 4 != 0 || p.ldb % 4 != 0 || p.N % 4 != 0 ||
+      (reinterpret_cast<uintptr_t>(p.A) & 15) != 0 || (reinterpret_cast<uintptr_t>(p.B) & 15) != 0)
+    return hipErrorInvalidValue;
+  Problem pp = p;
+  int tm = tiles_m, tn = tiles_n;
+  Epilogue ee = e;
+  unsigned long long* st = stamps;
+  void* args[] = {&pp, &tm, &tn, &ee, &st};
+  return hipLaunchKernel(
+      reinterpret_cast<const void*>(&mfma_dma_stamp_kernel<BM, BN, BK, WM, WN, kMinWaves>),
+      dim3((unsigned)tiles), dim3(C_::kThreads), args, 0, s);
+}
+#endif
+
+// The tiles: the default build holds the ones the tuning table can pick; a
+// build with GEMM_F32_SWEEP also holds the ones tuning sweeps compared them
+// with.
+#define GEMMF32_DMA_TILES(X) \
+  X(256, 256, 32, 64, 128, 1) \
+  X(128, 256, 16, 64, 128, 2) \
+  X(128, 192, 32, 32, 96, 2)  \
+  X(192, 128, 32, 96, 32, 2)  \
+  X(128, 128, 32, 64, 32, 2)  \
+  X(128, 128, 16, 64, 64, 3)  \
+  X(64, 64, 32, 32, 32, 4)
+#define GEMMF32_DMA_SWEEP_TILES(X) \
+  X(256, 128, 16, 128, 64, 2)      \
+  X(256, 128, 32, 128, 64, 1)      \
+  X(128, 128, 32, 64, 64, 2)       \
+  X(128, 128, 64, 64, 64, 1)       \
+  X(128, 64, 32, 64, 32, 3)        \
+  X(128, 64, 64, 64, 32, 2)        \
+  X(64, 64, 64, 32, 32, 2)         \
+  X(256, 256, 16, 128, 64, 1)      \
+  X(256, 256, 16, 64, 128, 1)      \
+  X(256, 256, 32, 128, 64, 1)
+
 #define GEMMF32_MFMA_DMA(BM, BN, BK, WM, WN, MW)                                          \
   {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN "_d6_vec", BM, BN, BK, WM, WN, true, true, \
-   true, &launch_dma<BM, BN, BK, WM, WN, MW>}
+   true, &launch_dma<BM, BN, BK, WM, WN, MW>},
 
-// The default build holds the tiles the tuning table can pick; a build with
-// GEMM_F32_SWEEP also holds the ones tuning sweeps compared them with.
 const MfmaVariant kDmaVariants[] = {
-    GEMMF32_MFMA_DMA(256, 256, 32, 64, 128, 1),
-    GEMMF32_MFMA_DMA(128, 256, 16, 64, 128, 2),
-    GEMMF32_MFMA_DMA(128, 192, 32, 32, 96, 2),
-    GEMMF32_MFMA_DMA(192, 128, 32, 96, 32, 2),
-    GEMMF32_MFMA_DMA(128, 128, 32, 64, 32, 2),
-    GEMMF32_MFMA_DMA(128, 128, 16, 64, 64, 3),
-    GEMMF32_MFMA_DMA(64, 64, 32, 32, 32, 4),
+    GEMMF32_DMA_TILES(GEMMF32_MFMA_DMA)
 #if GEMM_F32_SWEEP
-    GEMMF32_MFMA_DMA(256, 128, 16, 128, 64, 2),
-    GEMMF32_MFMA_DMA(256, 128, 32, 128, 64, 1),
-    GEMMF32_MFMA_DMA(128, 128, 32, 64, 64, 2),
-    GEMMF32_MFMA_DMA(128, 128, 64, 64, 64, 1),
-    GEMMF32_MFMA_DMA(128, 64, 32, 64, 32, 3),
-    GEMMF32_MFMA_DMA(128, 64, 64, 64, 32, 2),
-    GEMMF32_MFMA_DMA(64, 64, 64, 32, 32, 2),
-    GEMMF32_MFMA_DMA(256, 256, 16, 128, 64, 1),
-    GEMMF32_MFMA_DMA(256, 256, 16, 64, 128, 1),
-    GEMMF32_MFMA_DMA(256, 256, 32, 128, 64, 1),
+    GEMMF32_DMA_SWEEP_TILES(GEMMF32_MFMA_DMA)
 #endif
 };
+
+#if GEMM_F32_SWEEP
+using StampLaunch = hipError_t (*)(const Problem&, const Epilogue&, unsigned long long*, int64_t,
+                                   hipStream_t);
+#define GEMMF32_DMA_STAMP(BM, BN, BK, WM, WN, MW) &launch_dma_stamp<BM, BN, BK, WM, WN, MW>,
+// in the order of kDmaVariants
+const StampLaunch kDmaStamped[] = {GEMMF32_DMA_TILES(GEMMF32_DMA_STAMP)
+                                       GEMMF32_DMA_SWEEP_TILES(GEMMF32_DMA_STAMP)};
+static_assert(sizeof(kDmaStamped) / sizeof(kDmaStamped[0]) ==
+                  sizeof(kDmaVariants) / sizeof(kDmaVariants[0]),
+              "one instrumented launch per tile");
+#endif
 
 }  // namespace
 
 int mfma_dma_variant_count() { return (int)(sizeof(kDmaVariants) / sizeof(kDmaVariants[0])); }
+#if GEMM_F32_SWEEP
+hipError_t launch_dma_stamped(int i, const Problem& p, const Epilogue& e,
+                              unsigned long long* stamps, int64_t words, hipStream_t s) {
+  if (i < 0 || i >= mfma_dma_variant_count()) return hipErrorInvalidValue;
+  return kDmaStamped[i](p, e, stamps, words, s);
+}
+#endif
 const MfmaVariant& mfma_dma_variant(int i) { return kDmaVariants[i]; }
 
 }  // namespace gemmf32

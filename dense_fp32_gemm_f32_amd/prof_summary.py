@@ -45,7 +45,7 @@ def kernel_sources(kernel: str | None = None) -> list[str]:
         elif "_kw" in kernel:
             files += ["kernels_mfma_dma_ks.hip", "lds_dma.h"]
         elif "_d6_" in kernel:
-            files += ["kernels_mfma_dma.hip", "lds_dma.h"]
+            files += ["kernels_mfma_dma.hip", "lds_dma.h", "stamps.h"]
         else:
             files += ["kernels_mfma.hip"]
         files += ["mfma_common.h"]

@@ -33,6 +33,41 @@ def test_library_exports_every_declared_symbol():
     assert sorted(binding.EXPORTS) == declared_functions()
 
 
+SWEEP_HEADER = ROOT / "include" / "gemm_f32_sweep.h"
+
+
+def sweep_only_functions():
+    text = re.sub(r"/\*.*?\*/", "", SWEEP_HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_f32\w*)\s*\(", text)))
+
+
+def test_sweep_only_calls_stay_out_of_the_product_library():
+    lib = binding.load()
+    assert sweep_only_functions() == ["gemm_f32_stamped"]
+    for name in sweep_only_functions():
+        assert not hasattr(lib, name), f"{name} is for the sweep build only"
+
+
+def test_sweep_library_exports_both_headers():
+    from dense_fp32_gemm_f32_amd import build_lib
+    if not build_lib.SWEEP_LIB.exists():
+        pytest.skip("the sweep library is not built")
+    lib = ctypes.CDLL(str(build_lib.SWEEP_LIB))
+    for name in declared_functions() + sweep_only_functions():
+        assert hasattr(lib, name), f"{name} not exported by the sweep library"
+    # an entry that is not a direct-to-LDS tile is refused before any device call
+    lib.gemm_f32_stamped.argtypes = [ctypes.c_int] + [ctypes.c_int64] * 3 + [
+        ctypes.c_void_p, ctypes.c_int64] * 3 + [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.gemm_f32_kernel_count.restype = ctypes.c_int
+    lib.gemm_f32_kernel_name.argtypes = [ctypes.c_int]
+    lib.gemm_f32_kernel_name.restype = ctypes.c_char_p
+    names = [lib.gemm_f32_kernel_name(i).decode() for i in range(lib.gemm_f32_kernel_count())]
+    other = names.index("ref_naive")
+    assert lib.gemm_f32_stamped(other, 64, 64, 64, P16, 64, Q16, 64, R16, 64, P16, 96, None) == 8
+    assert lib.gemm_f32_stamped(len(names), 64, 64, 64, P16, 64, Q16, 64, R16, 64, P16, 96,
+                                None) == 8
+
+
 def test_version():
     assert binding.gemm_f32_version() == 5
 
