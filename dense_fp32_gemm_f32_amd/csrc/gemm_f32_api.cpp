@@ -20,6 +20,7 @@
 #include <vector>
 
 #include "gemm_f32_internal.h"
+#include "read_probe.h"
 #include "stamps.h"
 #include "tuning_gfx950.h"
 #if GEMM_F32_SWEEP
@@ -904,6 +905,27 @@ int gemm_f32_stamped(int index, int64_t M, int64_t N, int64_t K, const float* A,
   if (rc != GEMM_F32_OK) return rc;
   if (gemmf32::launch_dma_stamped(tile, r.p, op.epilogue(), stamps, stamp_words,
                                   static_cast<hipStream_t>(stream)) != hipSuccess) {
+    (void)hipGetLastError();
+    return GEMM_F32_ERR_LAUNCH;
+  }
+  return GEMM_F32_OK;
+}
+
+int gemm_f32_read_probe(const float* x, int64_t n, int groups, float* out, void* stream) {
+  if (groups < 1 || groups > 65535 || n <= 0 || n > (INT64_C(1) << 40) ||
+      n % ((int64_t)256 * groups) != 0)
+    return GEMM_F32_ERR_INVALID_DIM;
+  if (!x || !out) return GEMM_F32_ERR_NULL_PTR;
+  if (((uintptr_t)x & 15u) != 0 || !aligned4(out)) return GEMM_F32_ERR_POINTER;
+  const uintptr_t x0 = (uintptr_t)x, x1 = x0 + (uintptr_t)(n * 4), o = (uintptr_t)out;
+  if (o + (uintptr_t)groups * 32 > x0 && o < x1) return GEMM_F32_ERR_ALIAS;
+  int dev = -1;
+  int rc = check_device(&dev);
+  if (rc != GEMM_F32_OK) return rc;
+  if ((rc = check_pointer(x, dev)) != GEMM_F32_OK || (rc = check_pointer(out, dev)) != GEMM_F32_OK)
+    return rc;
+  if (gemmf32::launch_read_probe(x, n, groups, out, static_cast<hipStream_t>(stream)) !=
+      hipSuccess) {
     (void)hipGetLastError();
     return GEMM_F32_ERR_LAUNCH;
   }

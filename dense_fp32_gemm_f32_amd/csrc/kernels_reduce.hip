@@ -9,7 +9,7 @@
 //  pass 1: G groups (G and the chunk length depend on n only), group g owns
 //          the contiguous chunk [g c, min(n, (g + 1) c)) (c a multiple of 4).
 //          Thread t keeps four running sums, one per float4 component, over
-//          the float4s t, t + 256, ... of the chunk (16 loads in flight,
+//          the float4s t, t + 256, ... of the chunk (8 loads in flight,
 //          non-temporal); then (s0 + s1) + (s2 + s3), a butterfly across the
 //          wave (xor 32, 16, ..., 1: fp addition commutes, so every lane ends
 //          with the same value), and the four waves in LDS in wave order.
@@ -40,7 +40,7 @@ namespace {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;             // 4 waves
-constexpr int kUnroll = 16;               // float4 loads in flight per thread (16 KiB per wave)
+constexpr int kInFlight = 8;              // float4 loads in flight per thread (8 KiB per wave)
 constexpr int kMaxGroups = 256;           // one per CU of MI355X
 constexpr int64_t kMinPerGroup = 16384;   // elements; smaller arrays use fewer groups
 constexpr int kMaxPolls = 1 << 20;        // group 0's bound on polling one slot
@@ -75,20 +75,30 @@ __global__ void __launch_bounds__(kThreads)
   const int64_t n4 = (end - begin) >> 2;   // whole float4s of the chunk
   const float* xc = x + begin;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  int64_t i = threadIdx.x;
-  for (; i + (kUnroll - 1) * kThreads < n4; i += kUnroll * kThreads) {
-    floatx4 v[kUnroll];
+  // float4 j of thread t is t + 256 j of the chunk, added in order j = 0,
+  // 1, ...; the load of float4 j + kInFlight is issued right after float4 j
+  // is added, so the loads stay in flight without bursts (past the end of
+  // the chunk they re-read its last float4, which is not added)
+  const int64_t tid = threadIdx.x;
+  const int64_t cnt = n4 > tid ? (n4 - tid + kThreads - 1) / kThreads : 0;
+  if (cnt > 0) {
+    auto load_j = [&](int64_t j) {
+      const int64_t e = tid + j * kThreads;
+      return load4<VEC>(xc, 4 * (e < n4 ? e : n4 - 1));
+    };
+    floatx4 v[kInFlight];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = load4<VEC>(xc, 4 * (i + u * kThreads));
+    for (int u = 0; u < kInFlight; ++u) v[u] = load_j(u);
+    for (int64_t j0 = 0; j0 < cnt; j0 += kInFlight) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+      for (int u = 0; u < kInFlight; ++u) {
+        if (j0 + u < cnt) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] += v[u][c];
-  }
-  for (; i < n4; i += kThreads) {
-    const floatx4 v = load4<VEC>(xc, 4 * i);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] += v[c];
+          for (int c = 0; c < 4; ++c) acc[c] += v[u][c];
+        }
+        v[u] = load_j(j0 + kInFlight + u);
+      }
+    }
   }
   // the last (end - begin) % 4 elements (only the last group has any)
   const int64_t rem = (end - begin) - 4 * n4;
@@ -110,7 +120,8 @@ __global__ void __launch_bounds__(kThreads)
     // The other groups never wait, so their partials arrive within the time
     // of the stream; the bound on polling (about 1-2 s at one atomic round
     // trip per poll) only guarantees that the dispatch ends, with NaN as the
-    // sum, should a partial never arrive.
+    // sum, should a partial not arrive.  A partial that arrives after that
+    // stays in its slot until the workspaces are released.
     unsigned long long w = 0;
     for (int poll = 0; poll < kMaxPolls; ++poll) {
       w = __hip_atomic_exchange(slots + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

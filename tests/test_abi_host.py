@@ -43,7 +43,7 @@ def sweep_only_functions():
 
 def test_sweep_only_calls_stay_out_of_the_product_library():
     lib = binding.load()
-    assert sweep_only_functions() == ["gemm_f32_stamped"]
+    assert sweep_only_functions() == ["gemm_f32_read_probe", "gemm_f32_stamped"]
     for name in sweep_only_functions():
         assert not hasattr(lib, name), f"{name} is for the sweep build only"
 
@@ -66,6 +66,18 @@ def test_sweep_library_exports_both_headers():
     assert lib.gemm_f32_stamped(other, 64, 64, 64, P16, 64, Q16, 64, R16, 64, P16, 96, None) == 8
     assert lib.gemm_f32_stamped(len(names), 64, 64, 64, P16, 64, Q16, 64, R16, 64, P16, 96,
                                 None) == 8
+    # the read probe's argument errors, before any device call
+    lib.gemm_f32_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    probe = lib.gemm_f32_read_probe
+    assert probe(P16, 1 << 20, 0, Q16, None) == 1          # no workgroup
+    assert probe(P16, 1 << 20, 65536, Q16, None) == 1      # too many
+    assert probe(P16, 0, 1, Q16, None) == 1                # empty
+    assert probe(P16, (1 << 20) + 64, 4, Q16, None) == 1   # not whole 1 KiB pieces per group
+    assert probe(None, 1 << 20, 4, Q16, None) == 3
+    assert probe(P16, 1 << 20, 4, None, None) == 3
+    assert probe(P16 + 4, 1 << 20, 4, Q16, None) == 9      # x not 16-byte aligned
+    assert probe(P16, 1 << 20, 4, P16 + 64, None) == 4     # out inside x
 
 
 def test_version():

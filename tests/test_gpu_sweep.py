@@ -1,8 +1,12 @@
-"""GPU checks of the sweep build's instrumented tile kernels
-(``gemm_f32_stamped``, ``include/gemm_f32_sweep.h``): the instrumented copy
-computes bitwise what the plain kernel computes (and matches the oracle
-exactly on integer inputs), and every workgroup's stamps are ordered in
-time.  Skipped when the sweep library has not been built."""
+"""GPU checks of the sweep build's measurement calls (``include/gemm_f32_sweep.h``):
+
+- ``gemm_f32_stamped``: the instrumented tile computes bitwise what the plain
+  kernel computes (and matches the oracle exactly on integer inputs), and
+  every workgroup's stamps are ordered in time;
+- ``gemm_f32_read_probe``: it reads exactly the elements it is meant to (the
+  per-wave sums it writes, on integer data, against a host computation).
+
+Skipped when the sweep library has not been built."""
 import ctypes
 
 import numpy as np
@@ -28,6 +32,8 @@ def sweep():
     lib.gemm_f32_stamped.restype = ci
     lib.gemm_f32_run_kernel.argtypes = [ci, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
     lib.gemm_f32_run_kernel.restype = ci
+    lib.gemm_f32_read_probe.argtypes = [vp, i64, ci, vp, vp]
+    lib.gemm_f32_read_probe.restype = ci
     lib.gemm_f32_kernel_count.restype = ci
     lib.gemm_f32_kernel_name.argtypes = [ci]
     lib.gemm_f32_kernel_name.restype = ctypes.c_char_p
@@ -92,3 +98,23 @@ def test_stamped_argument_errors(sweep):
     assert lib.gemm_f32_stamped(d6, M, N, 100, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N,
                                 stamps.data_ptr(), 96, s) == 8
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("groups,pieces", [(4, 37), (256, 16), (3, 8), (1, 1)])
+def test_read_probe_reads_its_pattern(sweep, groups, pieces):
+    """Lane 0 of wave w in workgroup g adds floats 0..3 of 1 KiB pieces w,
+    w + 8, ... of chunk g; small integers make every sum exact."""
+    lib, _ = sweep
+    chunk = 256 * pieces
+    n = groups * chunk
+    x = torch.from_numpy(np.random.default_rng(8200 + groups).integers(-8, 9, n).astype(np.float32))
+    out = torch.full((8 * groups,), float("nan"), device="cuda")
+    print(f"read probe {groups} groups x {pieces} pieces", flush=True)
+    assert lib.gemm_f32_read_probe(x.cuda().data_ptr(), n, groups, out.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    xv = x.numpy().astype(np.float64).reshape(groups, pieces, 256)[:, :, :4].sum(axis=2)
+    want = np.zeros((groups, 8))
+    for w in range(8):
+        want[:, w] = xv[:, w::8].sum(axis=1)
+    assert np.array_equal(out.cpu().numpy().reshape(groups, 8), want.astype(np.float32))
