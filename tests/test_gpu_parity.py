@@ -140,6 +140,9 @@ def test_every_kernel_variant(gpu_lib, kname):
         # taken (two K-tiles), odd pitches
         bk = int(kname.split("_")[1].split("x")[2])
         cases += [(130, 70, 3 * bk, 3 * bk + 1, 73), (67, 200, 2 * bk, 2 * bk + 3, 201)]
+        # one row, one column: every other row / column of the tile reads the
+        # clamped last one
+        cases += [(1, 3, 2 * bk + 5, 2 * bk + 6, 4), (70, 1, 5 * bk + 3, 5 * bk + 4, 2)]
     for (M, N, K, lda, ldb), integer in [(c, i) for c in cases for i in (True, False)]:
         dist = "int2" if integer else "u11"
         A, B = inputs.make_ab(M, N, K, dist, dist, 3001 + integer, lda=lda, ldb=ldb)
