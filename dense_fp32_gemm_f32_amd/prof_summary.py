@@ -247,9 +247,10 @@ def main(argv=None):
         calls, avg, mn, mx = dur[n]
         tot_avg += avg
         lines.append(f"| `{n[:110]}` | {calls} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | {mx / 1e3:.2f} |")
+    rate = f"{args.flops / (tot_avg * 1e-9) / 1e12:.2f} TFLOP/s, " if args.flops > 0 else ""
     lines += ["", f"Sum of average durations of the matched kernels: {tot_avg / 1e3:.2f} us "
-              f"-> {args.flops / (tot_avg * 1e-9) / 1e12:.2f} TFLOP/s, "
-              f"{args.algo_bytes / (tot_avg * 1e-9) / 1e9:.1f} GB/s of algorithmic traffic", ""]
+              f"-> {rate}{args.algo_bytes / (tot_avg * 1e-9) / 1e9:.1f} GB/s of algorithmic "
+              "traffic", ""]
     if args.log:
         probe = [l.strip() for l in Path(args.log).read_text().splitlines()
                  if l.startswith("clock probe:")]
